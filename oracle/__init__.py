@@ -1,0 +1,250 @@
+"""ctypes front end of the fp64 CPU oracle (``h3_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product path (the HIP library
+and its binding) never loads it.
+
+The oracle evaluates, in fp64 from the same bf16 input bits the GPU reads,
+per-head RMSNorm of q and k, interleaved-pair RoPE (3D t/h/w sections for
+video tokens, one section over all dims for audio tokens) and block-diagonal
+non-causal softmax attention; see the C file's header for the definitions and
+the pages they follow.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "h3_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD, "liboracle.so")
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared",
+                               "-Wall", "-Wno-unused-function", src, "-o", tmp,
+                               "-lm", "-lpthread"])
+        os.replace(tmp, out)
+    return out
+
+
+class _Seq(C.Structure):
+    _fields_ = [("T", C.c_int32), ("Hg", C.c_int32), ("Wg", C.c_int32), ("n_audio", C.c_int32)]
+
+
+class _Problem(C.Structure):
+    _fields_ = [("H", C.c_int32), ("d", C.c_int32), ("S", C.c_int32), ("rope", C.c_int32),
+                ("split", C.c_int32 * 3), ("pad", C.c_int32),
+                ("theta", C.c_double), ("eps", C.c_double), ("scale", C.c_double),
+                ("cu", C.POINTER(C.c_int32)), ("seqs", C.POINTER(_Seq)),
+                ("q", C.POINTER(C.c_uint16)), ("k", C.POINTER(C.c_uint16)),
+                ("v", C.POINTER(C.c_uint16)),
+                ("q_stride", C.c_int64), ("k_stride", C.c_int64), ("v_stride", C.c_int64),
+                ("norm_w", C.POINTER(C.c_float))]
+
+
+_lib = None
+
+
+def lib(path: Optional[str] = None):
+    """Load (building if absent) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(C.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _bind(C.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _bind(L):
+    P = C.POINTER
+    L.orc_bf16_to_f64.restype = C.c_double
+    L.orc_bf16_to_f64.argtypes = [C.c_uint16]
+    L.orc_token_pos.argtypes = [P(_Problem), C.c_int64, P(C.c_int32), P(C.c_int32), P(C.c_int32)]
+    L.orc_rope_angles.argtypes = [P(_Problem), C.c_int32, P(C.c_int32), P(C.c_double)]
+    L.orc_rmsnorm.argtypes = [P(C.c_uint16), P(C.c_float), C.c_int, C.c_double, P(C.c_double)]
+    L.orc_rope_rotate.argtypes = [P(C.c_double), P(C.c_double), C.c_int, P(C.c_double)]
+    L.orc_prologue_rows.argtypes = [P(_Problem), C.c_int, P(C.c_int64), C.c_int64,
+                                    P(C.c_double), C.c_int]
+    L.orc_attention_core.argtypes = [P(C.c_double), C.c_int64, P(C.c_double), P(C.c_double),
+                                     C.c_int64, C.c_int, C.c_double, P(C.c_double)]
+    L.orc_attention_rows.argtypes = [P(_Problem), P(C.c_int64), C.c_int64, P(C.c_double), C.c_int]
+    L.orc_default_threads.restype = C.c_int
+    L.orc_q8_kmean.argtypes = [P(_Problem), P(C.c_double), C.c_int]
+    L.orc_q8_block_quant.argtypes = [P(_Problem), C.c_int, C.c_int32, C.c_int32, C.c_int32,
+                                     P(C.c_double), P(C.c_double), P(C.c_double), P(C.c_int8)]
+    L.orc_q8_v_quant.argtypes = [P(_Problem), C.c_int32, C.c_int32, P(C.c_double),
+                                 P(C.c_double), P(C.c_uint8)]
+    L.orc_e4m3_encode.restype = C.c_uint8
+    L.orc_e4m3_encode.argtypes = [C.c_double]
+    L.orc_e4m3_decode.restype = C.c_double
+    L.orc_e4m3_decode.argtypes = [C.c_uint8]
+    return L
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(C.POINTER(t))
+
+
+class Problem:
+    """One oracle problem; keeps the numpy buffers it points into alive.
+
+    ``seqs`` is a list of (T, Hg, Wg, n_audio); q, k, v are uint16 bf16 bits
+    [N, H, d] (any token stride is taken from the array's first stride);
+    norm_w is float32 [2, H, d].
+    """
+
+    def __init__(self, H: int, d: int, seqs: Sequence, split, q, k, v, norm_w,
+                 theta: float = 10000.0, eps: float = 1e-6, scale: Optional[float] = None,
+                 rope: bool = True, library=None):
+        self.L = library or lib()
+        self.H, self.d = int(H), int(d)
+        seqs = [tuple(int(x) for x in (s if not hasattr(s, "T") else (s.T, s.Hg, s.Wg, s.n_audio)))
+                for s in seqs]
+        self.seqs_py = seqs
+        n = [s[0] * s[1] * s[2] + s[3] for s in seqs]
+        self.cu = np.zeros(len(seqs) + 1, dtype=np.int32)
+        self.cu[1:] = np.cumsum(n)
+        self.N = int(self.cu[-1])
+        self._seqs = (_Seq * max(1, len(seqs)))(*[_Seq(*s) for s in seqs])
+        self.q, self.k, self.v = (self._prep(x) for x in (q, k, v))
+        self.norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+        assert self.norm_w.shape == (2, self.H, self.d)
+        self.scale = float(scale) if scale is not None else 1.0 / np.sqrt(self.d)
+        pr = _Problem()
+        pr.H, pr.d, pr.S, pr.rope = self.H, self.d, len(seqs), 1 if rope else 0
+        pr.split[:] = list(split)
+        pr.theta, pr.eps, pr.scale = float(theta), float(eps), self.scale
+        pr.cu = _ptr(self.cu, C.c_int32)
+        pr.seqs = self._seqs
+        pr.q, pr.k, pr.v = (_ptr(x, C.c_uint16) for x in (self.q, self.k, self.v))
+        pr.q_stride, pr.k_stride, pr.v_stride = (x.strides[0] // 2 for x in (self.q, self.k, self.v))
+        pr.norm_w = _ptr(self.norm_w, C.c_float)
+        self.pr = pr
+
+    def _prep(self, x):
+        x = np.asarray(x)
+        assert x.dtype == np.uint16 and x.ndim == 3 and x.shape[1:] == (self.H, self.d)
+        if x.strides[1] != self.d * 2 or x.strides[2] != 2:
+            x = np.ascontiguousarray(x)
+        return x
+
+    @classmethod
+    def from_workload(cls, w, inputs, **kw):
+        return cls(w.H, w.d, w.seqs, w.split, inputs["q"], inputs["k"], inputs["v"],
+                   inputs["norm_w"], theta=w.theta, eps=w.eps, **kw)
+
+    # -- queries -----------------------------------------------------------
+    def attention_rows(self, rows, nthreads: int = 0) -> np.ndarray:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.zeros((len(rows), self.d), dtype=np.float64)
+        st = self.L.orc_attention_rows(C.byref(self.pr), _ptr(rows, C.c_int64), len(rows),
+                                       _ptr(out, C.c_double), int(nthreads))
+        if st != 0:
+            raise ValueError("oracle: row outside every sequence")
+        return out
+
+    def prologue_rows(self, which: int, rows, nthreads: int = 0) -> np.ndarray:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.zeros((len(rows), self.d), dtype=np.float64)
+        st = self.L.orc_prologue_rows(C.byref(self.pr), int(which), _ptr(rows, C.c_int64),
+                                      len(rows), _ptr(out, C.c_double), int(nthreads))
+        if st != 0:
+            raise ValueError("oracle: row outside every sequence")
+        return out
+
+    def token_pos(self, token: int):
+        s, a = C.c_int32(), C.c_int32()
+        pos = (C.c_int32 * 3)()
+        self.L.orc_token_pos(C.byref(self.pr), int(token), C.byref(s), C.byref(a), pos)
+        return s.value, bool(a.value), tuple(pos)
+
+    def rope_angles(self, is_audio: bool, pos) -> np.ndarray:
+        p = (C.c_int32 * 3)(*[int(x) for x in (list(pos) + [0, 0, 0])[:3]])
+        out = np.zeros(self.d // 2, dtype=np.float64)
+        self.L.orc_rope_angles(C.byref(self.pr), 1 if is_audio else 0, p, _ptr(out, C.c_double))
+        return out
+
+    # -- quantised-path stages ---------------------------------------------
+    def q8_kmean(self, nthreads: int = 0) -> np.ndarray:
+        out = np.zeros((len(self.seqs_py), self.H, self.d), dtype=np.float64)
+        self.L.orc_q8_kmean(C.byref(self.pr), _ptr(out, C.c_double), int(nthreads))
+        return out
+
+    def q8_block_quant(self, which: int, seq: int, head: int, block: int, kmean=None):
+        rows_max = 64
+        ratio = np.zeros((rows_max, self.d), dtype=np.float64)
+        codes = np.zeros((rows_max, self.d), dtype=np.int8)
+        scale = C.c_double()
+        km = np.ascontiguousarray(kmean if kmean is not None else
+                                  np.zeros((len(self.seqs_py), self.H, self.d)), dtype=np.float64)
+        rows = self.L.orc_q8_block_quant(C.byref(self.pr), int(which), int(seq), int(head),
+                                         int(block), _ptr(km, C.c_double), C.byref(scale),
+                                         _ptr(ratio, C.c_double), _ptr(codes, C.c_int8))
+        if rows < 0:
+            raise ValueError("oracle: bad quantisation block")
+        return scale.value, ratio[:rows], codes[:rows]
+
+    def q8_v_quant(self, seq: int, head: int):
+        n = int(self.cu[seq + 1] - self.cu[seq])
+        scale = np.zeros(self.d, dtype=np.float64)
+        ratio = np.zeros((max(n, 1), self.d), dtype=np.float64)
+        codes = np.zeros((max(n, 1), self.d), dtype=np.uint8)
+        self.L.orc_q8_v_quant(C.byref(self.pr), int(seq), int(head), _ptr(scale, C.c_double),
+                              _ptr(ratio, C.c_double), _ptr(codes, C.c_uint8))
+        return scale, ratio[:n], codes[:n]
+
+
+def attention_core(qhat, khat, v, scale: float, library=None) -> np.ndarray:
+    """Softmax attention of fp64 rows qhat [nq, d] over keys khat, v [nk, d]."""
+    L = library or lib()
+    qhat, khat, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (qhat, khat, v))
+    nq, d = qhat.shape
+    out = np.zeros((nq, d), dtype=np.float64)
+    L.orc_attention_core(_ptr(qhat, C.c_double), nq, _ptr(khat, C.c_double),
+                         _ptr(v, C.c_double), khat.shape[0], d, float(scale),
+                         _ptr(out, C.c_double))
+    return out
+
+
+def rmsnorm(x_bf16, w, eps: float, library=None) -> np.ndarray:
+    L = library or lib()
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    out = np.zeros(x.shape[-1], dtype=np.float64)
+    L.orc_rmsnorm(_ptr(x, C.c_uint16), _ptr(w, C.c_float), x.shape[-1], float(eps),
+                  _ptr(out, C.c_double))
+    return out
+
+
+def rope_rotate(x, phi, library=None) -> np.ndarray:
+    L = library or lib()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    phi = np.ascontiguousarray(phi, dtype=np.float64)
+    out = np.zeros_like(x)
+    L.orc_rope_rotate(_ptr(x, C.c_double), _ptr(phi, C.c_double), x.shape[-1],
+                      _ptr(out, C.c_double))
+    return out
+
+
+def e4m3_encode(x: float, library=None) -> int:
+    return int((library or lib()).orc_e4m3_encode(float(x)))
+
+
+def e4m3_decode(c: int, library=None) -> float:
+    return float((library or lib()).orc_e4m3_decode(int(c)))
+
+
+def default_threads(library=None) -> int:
+    return int((library or lib()).orc_default_threads())
