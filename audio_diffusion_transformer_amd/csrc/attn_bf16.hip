@@ -1,0 +1,237 @@
+// Flash-style non-causal attention over packed sequences, bf16 MFMA on gfx950.
+//
+// This is the attention share of a MiniMax-H3 block (about 58% of block time
+// on the page "Buyer Questions: Current Evidence Status", question 4), and the
+// "H3-specific attention backend" the page "H3 Runtime Current State" lists
+// under "Owned Performance Kernels".  It consumes the prologue's head-major
+// qhat / khat and per-tile transposed V, and computes, for each query row,
+// the softmax over the keys of its own sequence with an online (running-max)
+// softmax, never materialising the N x N score matrix.
+//
+// Work decomposition.  One workgroup = 4 waves = 128 query rows of one
+// (sequence, head); each wave owns 32 query rows.  Workgroups are ordered
+// longest sequence first, then head, then query block, so consecutive
+// workgroups (which the dispatcher spreads over the 8 XCDs) stream the same
+// head's K/V and share it through each XCD's L2.
+//
+// Matrix-core layout.  Both products use v_mfma_f32_32x32x16_bf16 and are
+// arranged so every lane keeps one query row throughout:
+//   S^T = K . Q^T   A = K tile rows from LDS (M = key), B = Q^T held in
+//                   registers (N = query); the 32x32 accumulator gives lane l
+//                   query l%32 and 16 of the 32 keys.
+//   O^T = V^T . P^T A = V^T rows from LDS (M = channel), B = P^T straight from
+//                   the score registers (N = query); lane l accumulates 16
+//                   channels per 32-channel block of query l%32.
+// So the softmax row max and row sum are in-lane reductions plus one
+// exchange with lane l^32, and the running-max rescale of O is a per-lane
+// scalar.  The 8 keys one lane feeds to a P.V step are keys
+// {16c + 8(e/4) + 4(l/32) + e%4}; the prologue stores V^T with bits 2 and 3 of
+// the in-tile key index swapped so those 8 keys are one contiguous 16-byte LDS
+// read.
+//
+// Pipelining.  K and V^T tiles of 64 keys are double-buffered in LDS; the
+// global loads of tile j+1 are issued before tile j is computed and written to
+// the other buffer after it, with one barrier per tile.  LDS rows are XOR
+// swizzled at 16-byte granularity so the 16-byte fragment reads of 8
+// consecutive lanes hit distinct banks.
+//
+// Online softmax in base 2: p = 2^(s*c - m*c), c = scale*log2(e).  The running
+// max m is only raised when a tile's max exceeds it by more than 8 (in log2
+// units), so O and l are rescaled rarely; p then stays below 2^8, well inside
+// bf16 and fp32 range.  P is rounded to bf16 for the P.V product and the row
+// sum l adds exactly those rounded values.
+#include "h3_internal.h"
+
+namespace h3 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLazyRescale = 8.0f;
+
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
+{
+    constexpr int KSTEPS = D / 16;          // k-steps of the S^T product
+    constexpr int DB = D / 32;              // 32-channel output blocks
+    constexpr int KCH = D / 8;              // 16-byte chunks per K row
+    constexpr int PER = kTile * D / 8 / 256; // 16-byte chunks per lane per tile (each of K, V)
+    __shared__ __attribute__((aligned(16))) uint16_t lk[2][kTile * D];
+    __shared__ __attribute__((aligned(16))) uint16_t lv[2][D * kTile];
+
+    // ---- work item: (sequence, head, 128-row query block)
+    const int b = blockIdx.x;
+    int si = 0;
+    while (b >= a.item_pre[si + 1]) ++si;
+    const int rem = b - a.item_pre[si];
+    const int nqb = a.seq_nqb[si];
+    const int head = rem / nqb, qb = rem % nqb;
+    const int n = a.seq_n[si];
+    const int off = a.seq_off[si];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int m = lane & 31, hh = lane >> 5;
+    const int q0 = qb * kBlockM + wave * 32;
+
+    // ---- Q^T fragments: lane holds query q0+m, channels 16s + 8hh .. +7
+    bf16x8 qf[KSTEPS];
+    {
+        const uint16_t *qp = a.qhat + ((int64_t)head * a.Npad + off + q0 + m) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+    }
+
+    const uint16_t *kbase = a.khat + ((int64_t)head * a.Npad + off) * D;
+    const uint16_t *vbase = a.vt + ((int64_t)head * (a.Npad / kTile) + off / kTile) * (D * kTile);
+    const int nt = (n + kTile - 1) / kTile;
+
+    u32x4 stk[PER], stv[PER];
+    auto gload = [&](int j) {
+        const u32x4 *ks = reinterpret_cast<const u32x4 *>(kbase + (int64_t)j * kTile * D);
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>(vbase + (int64_t)j * D * kTile);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            stk[i] = ks[tid + 256 * i];
+            stv[i] = vs[tid + 256 * i];
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int g = tid + 256 * i;
+            const int kr = g / KCH, kc = g % KCH;
+            *reinterpret_cast<u32x4 *>(&lk[buf][kr * D + 8 * (kc ^ (kr & (KCH - 1)))]) = stk[i];
+            const int vr = g >> 3, vc = g & 7;
+            *reinterpret_cast<u32x4 *>(&lv[buf][vr * kTile + 8 * (vc ^ (vr & 7))]) = stv[i];
+        }
+    };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] = (f32x16){};
+    float m_used = -INFINITY, l = 0.f;
+    const float c = a.scale_log2;
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int j = 0; j < nt; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < nt) gload(j + 1);
+
+        // ---- S^T = K . Q^T for 64 keys (two 32-key blocks)
+        f32x16 s0 = (f32x16){}, s1 = (f32x16){};
+        const uint16_t *kl = lk[buf];
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+            const int ch = (2 * st + hh) ^ (m & (KCH - 1));
+            const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(kl + m * D + 8 * ch);
+            const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(kl + (32 + m) * D + 8 * ch);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[st], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[st], s1, 0, 0, 0);
+        }
+
+        // ---- mask keys past the end of the sequence (last tile only)
+        const int valid = n - j * kTile;
+        if (valid < kTile) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (key >= valid) s0[r] = -INFINITY;
+                if (32 + key >= valid) s1[r] = -INFINITY;
+            }
+        }
+
+        // ---- online softmax (row = this lane's query)
+        float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool need = (mx - m_used) * c > kLazyRescale;
+        if (__any(need)) {
+            const float mn = need ? mx : m_used;
+            const float alpha = __builtin_amdgcn_exp2f((m_used - mn) * c);
+            m_used = mn;
+            l *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        }
+        const float mc = m_used * c;
+        uint32_t p0[8], p1[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            p0[r / 2] = pack2(__builtin_amdgcn_exp2f(fmaf(s0[r], c, -mc)),
+                              __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c, -mc)));
+            p1[r / 2] = pack2(__builtin_amdgcn_exp2f(fmaf(s1[r], c, -mc)),
+                              __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c, -mc)));
+        }
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p0[i]), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p1[i]), ones, l, false);
+        }
+
+        // ---- O^T += V^T . P^T
+        const uint16_t *vl = lv[buf];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const uint32_t *pp = kb ? p1 : p0;
+                const u32x4 pw = {pp[4 * cc], pp[4 * cc + 1], pp[4 * cc + 2], pp[4 * cc + 3]};
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+                const int ch = (4 * kb + 2 * cc + hh) ^ (m & 7);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vl + (32 * db + m) * kTile + 8 * ch);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (j + 1 < nt) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: o = O / l, bf16, rows of this sequence only
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = 1.0f / lt;
+    const int qrow = q0 + m;
+    if (qrow < n) {
+        uint16_t *op = a.out + ((int64_t)a.seq_cu[si] + qrow) * a.o_stride + (int64_t)head * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 w = {pack2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv),
+                                 pack2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(op + 32 * db + 8 * i + 4 * hh) = w;
+            }
+        }
+    }
+}
+
+hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_t st)
+{
+    if (nitems <= 0) return hipSuccess;
+    if (d == 128)
+        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)nitems), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)nitems), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace h3

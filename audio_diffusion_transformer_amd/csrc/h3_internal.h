@@ -1,0 +1,133 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+// Not part of the public ABI (include/h3attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3 {
+
+constexpr int kMaxSeqs = 64;     // == H3ATTN_MAX_SEQS
+constexpr int kSeqPad = 256;     // every sequence starts at a multiple of this in the workspace
+constexpr int kTile = 64;        // key tile (and quantisation block) in tokens
+
+// Workspace layout of one call.  Head-major copies of the prologue outputs:
+//   qhat, khat : bf16 [H][Npad][d]
+//   vt         : bf16 [H][Npad/64][d][64]  (V transposed per 64-key tile; the
+//                keys inside each 32-key half are stored in the order the
+//                P.V matrix-core operand consumes them, see attn_bf16.hip)
+// Quantised path:
+//   q8, k8     : int8 [H][Npad][d]
+//   v8t        : fp8  [H][Npad/64][d][64]  (transposed; key order of the FP8 P.V operand)
+//   qscale, kscale : fp32 [H][Npad/64]
+//   ksum, vmax : fp32 [H][Npad/64][d]  per-tile partial sums / maxima
+//   kmean, vscale : fp32 [S][H][d]
+struct Plan {
+    int32_t S, H, d;
+    int64_t N, Npad;
+    int32_t cu[kMaxSeqs + 1];    // packed token starts
+    int32_t off[kMaxSeqs + 1];   // padded starts (multiples of kSeqPad)
+    size_t qhat, khat, vt;       // byte offsets into the workspace
+    size_t q8, k8, v8t, qscale, kscale, ksum, vmax, kmean, vscale;
+    size_t bytes_bf16, bytes_q8;
+};
+
+// Which sequence a padded 64-token tile belongs to: tiles of sequence s are
+// [off[s]/64, off[s]/64 + ceil(n_s/64)); the remaining tiles up to off[s+1]/64
+// are padding.
+struct SeqTable {
+    int32_t S;
+    int32_t cu[kMaxSeqs + 1];
+    int32_t off[kMaxSeqs + 1];
+};
+
+struct PrologueArgs {
+    const uint16_t *q, *k, *v;
+    int64_t q_stride, k_stride, v_stride;
+    const float *norm_w;
+    const float *rope;
+    // bf16 outputs.  qhat/khat element (h, padded token t, c) at
+    // h*out_hstride + t*out_tstride + c.  When `natural` is set, t is the packed
+    // token and padding rows are skipped (diagnostic export).
+    uint16_t *qhat, *khat, *vt;
+    int64_t out_hstride, out_tstride;
+    int32_t natural;
+    int32_t H;
+    int64_t Npad;
+    float eps;
+    int32_t ntiles;              // Npad / 64
+    SeqTable seq;
+};
+
+struct AttnArgs {
+    const uint16_t *qhat, *khat, *vt;
+    uint16_t *out;
+    int64_t o_stride;
+    int64_t Npad;
+    int32_t H;
+    float scale_log2;            // softmax scale * log2(e)
+    int32_t nseq;                // sequences with work, longest first
+    int32_t seq_n[kMaxSeqs];
+    int32_t seq_cu[kMaxSeqs];
+    int32_t seq_off[kMaxSeqs];
+    int32_t seq_nqb[kMaxSeqs];
+    int32_t item_pre[kMaxSeqs + 1];   // prefix sums of H * nqb
+};
+
+struct Q8Args {
+    const uint16_t *q, *k, *v;
+    int64_t q_stride, k_stride, v_stride;
+    const float *norm_w, *rope;
+    int8_t *q8, *k8;
+    uint8_t *v8t;
+    float *qscale, *kscale, *ksum, *vmax, *kmean, *vscale;
+    int32_t H;
+    int64_t Npad;
+    float eps;
+    int32_t ntiles;
+    SeqTable seq;
+};
+
+struct Q8AttnArgs {
+    const int8_t *q8, *k8;
+    const uint8_t *v8t;
+    const float *qscale, *kscale, *vscale;
+    uint16_t *out;
+    int64_t o_stride;
+    int64_t Npad;
+    int32_t H;
+    float scale_log2;
+    int32_t nseq;
+    int32_t seq_n[kMaxSeqs];
+    int32_t seq_cu[kMaxSeqs];
+    int32_t seq_off[kMaxSeqs];
+    int32_t seq_idx[kMaxSeqs];   // original sequence index (for vscale)
+    int32_t seq_nqb[kMaxSeqs];
+    int32_t item_pre[kMaxSeqs + 1];
+};
+
+struct Q8ExportArgs {
+    const int8_t *q8, *k8;
+    const uint8_t *v8t;
+    const float *qscale, *kscale;
+    int8_t *q8_out, *k8_out;
+    uint8_t *v8_out;
+    float *qscale_out, *kscale_out;
+    int32_t H, d;
+    int64_t Npad;
+    int32_t ntiles;
+    int32_t nblocks;             // sum of ceil(n_s / 64)
+    SeqTable seq;
+};
+
+// Launchers: return the hipError_t of the launch.
+hipError_t launch_prologue(const PrologueArgs &a, int d, hipStream_t st);
+hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_t st);
+hipError_t launch_q8_prep(const Q8Args &a, int d, hipStream_t st);
+hipError_t launch_attn_q8(const Q8AttnArgs &a, int d, int64_t nitems, hipStream_t st);
+hipError_t launch_q8_export(const Q8ExportArgs &a, hipStream_t st);
+
+// Queries per workgroup of the attention kernels (work-item granularity).
+constexpr int kBlockM = 128;
+
+}  // namespace h3

@@ -1,0 +1,382 @@
+// Host side of the C ABI declared in include/h3attn.h: argument checks,
+// workspace plan, work ordering and kernel launches.  Every check runs on the
+// host before any HIP call, so invalid arguments are reported without a GPU.
+#include "h3attn.h"
+#include "h3_internal.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+
+using namespace h3;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+h3attn_status fail(h3attn_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+h3attn_status ok()
+{
+    g_last_error.clear();
+    return H3ATTN_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Shape, stride and cu_seqlens checks; fills the workspace plan.
+h3attn_status make_plan(const h3attn_params *p, const int32_t *cu, Plan *pl)
+{
+    if (!p) return fail(H3ATTN_ERR_INVALID_ARG, "params is NULL");
+    if (!cu) return fail(H3ATTN_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+    if (p->num_heads < 1) return fail(H3ATTN_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", p->num_heads);
+    if (p->num_heads > 4096) return fail(H3ATTN_ERR_UNSUPPORTED, "num_heads %d > 4096", p->num_heads);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(H3ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+    if (p->num_seqs < 1 || p->num_seqs > H3ATTN_MAX_SEQS)
+        return fail(H3ATTN_ERR_INVALID_ARG, "num_seqs must be in [1, %d] (got %d)", H3ATTN_MAX_SEQS, p->num_seqs);
+    if (p->flags != 0) return fail(H3ATTN_ERR_INVALID_ARG, "flags must be 0");
+    const int64_t hd = (int64_t)p->num_heads * p->head_dim;
+    const int64_t strides[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
+    const char *names[4] = {"q_stride", "k_stride", "v_stride", "o_stride"};
+    for (int i = 0; i < 4; ++i) {
+        if (strides[i] < hd)
+            return fail(H3ATTN_ERR_INVALID_ARG, "%s %lld < num_heads*head_dim %lld", names[i],
+                        (long long)strides[i], (long long)hd);
+        if (strides[i] % 8)
+            return fail(H3ATTN_ERR_INVALID_ARG, "%s %lld is not a multiple of 8", names[i], (long long)strides[i]);
+    }
+    if (!(p->eps > 0.f) || !std::isfinite(p->eps))
+        return fail(H3ATTN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!std::isfinite(p->softmax_scale)) return fail(H3ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (cu[0] != 0) return fail(H3ATTN_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+    for (int s = 0; s < p->num_seqs; ++s)
+        if (cu[s + 1] < cu[s])
+            return fail(H3ATTN_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", s, cu[s], cu[s + 1]);
+    std::memset(pl, 0, sizeof *pl);
+    pl->S = p->num_seqs;
+    pl->H = p->num_heads;
+    pl->d = p->head_dim;
+    pl->N = cu[p->num_seqs];
+    int64_t off = 0;
+    for (int s = 0; s <= p->num_seqs; ++s) {
+        pl->cu[s] = cu[s];
+        pl->off[s] = (int32_t)off;
+        if (s < p->num_seqs) off += round_up(cu[s + 1] - cu[s], kSeqPad);
+        if (off > INT32_MAX - kSeqPad) return fail(H3ATTN_ERR_UNSUPPORTED, "too many tokens");
+    }
+    pl->Npad = off;
+    const int64_t H = pl->H, d = pl->d, Np = pl->Npad, T = Np / kTile, S = pl->S;
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = at;
+        at = (size_t)round_up((int64_t)(at + bytes), 256);
+        return o;
+    };
+    pl->qhat = take(H * Np * d * 2);
+    pl->khat = take(H * Np * d * 2);
+    pl->vt = take(H * Np * d * 2);
+    pl->bytes_bf16 = std::max<size_t>(at, 256);   // never 0: 0 reports an error
+    at = 0;
+    pl->q8 = take(H * Np * d);
+    pl->k8 = take(H * Np * d);
+    pl->v8t = take(H * Np * d);
+    pl->qscale = take(H * T * 4);
+    pl->kscale = take(H * T * 4);
+    pl->ksum = take(H * T * d * 4);
+    pl->vmax = take(H * T * d * 4);
+    pl->kmean = take(S * H * d * 4);
+    pl->vscale = take(S * H * d * 4);
+    pl->bytes_q8 = std::max<size_t>(at, 256);
+    return H3ATTN_OK;
+}
+
+h3attn_status check_device()
+{
+    static std::atomic<int> checked[64];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(H3ATTN_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64 && checked[dev].load() == 1) return H3ATTN_OK;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(H3ATTN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(H3ATTN_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+    if (dev >= 0 && dev < 64) checked[dev].store(1);
+    return H3ATTN_OK;
+}
+
+h3attn_status check_ptrs(const void *q, const void *k, const void *v, const float *norm_w,
+                         const float *rope, const void *out)
+{
+    const void *ps[6] = {q, k, v, norm_w, rope, out};
+    const char *names[6] = {"q", "k", "v", "norm_w", "rope_tables", "out"};
+    for (int i = 0; i < 6; ++i) {
+        if (!ps[i]) return fail(H3ATTN_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(ps[i], 16)) return fail(H3ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    return H3ATTN_OK;
+}
+
+SeqTable seq_table(const Plan &pl)
+{
+    SeqTable t;
+    std::memset(&t, 0, sizeof t);
+    t.S = pl.S;
+    for (int s = 0; s <= pl.S; ++s) {
+        t.cu[s] = pl.cu[s];
+        t.off[s] = pl.off[s];
+    }
+    return t;
+}
+
+PrologueArgs prologue_args(const h3attn_params *p, const Plan &pl, const void *q, const void *k,
+                           const void *v, const float *norm_w, const float *rope)
+{
+    PrologueArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.q_stride = p->q_stride;
+    a.k_stride = p->k_stride;
+    a.v_stride = p->v_stride;
+    a.norm_w = norm_w;
+    a.rope = rope;
+    a.H = pl.H;
+    a.Npad = pl.Npad;
+    a.eps = p->eps;
+    a.ntiles = (int32_t)(pl.Npad / kTile);
+    a.seq = seq_table(pl);
+    return a;
+}
+
+float scale_log2(const h3attn_params *p)
+{
+    const double s = p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim);
+    return (float)(s * 1.4426950408889634);
+}
+
+// Sequences with work, longest first (stable), and the work-item prefix.
+template <class Args>
+int64_t order_work(const Plan &pl, Args &a, int32_t *seq_idx)
+{
+    int order[kMaxSeqs];
+    std::iota(order, order + pl.S, 0);
+    std::stable_sort(order, order + pl.S, [&](int x, int y) {
+        return pl.cu[x + 1] - pl.cu[x] > pl.cu[y + 1] - pl.cu[y];
+    });
+    int64_t items = 0;
+    int k = 0;
+    a.item_pre[0] = 0;
+    for (int i = 0; i < pl.S; ++i) {
+        const int s = order[i];
+        const int n = pl.cu[s + 1] - pl.cu[s];
+        if (n == 0) continue;
+        a.seq_n[k] = n;
+        a.seq_cu[k] = pl.cu[s];
+        a.seq_off[k] = pl.off[s];
+        a.seq_nqb[k] = (n + kBlockM - 1) / kBlockM;
+        if (seq_idx) seq_idx[k] = s;
+        items += (int64_t)pl.H * a.seq_nqb[k];
+        a.item_pre[k + 1] = (int32_t)items;
+        ++k;
+    }
+    a.nseq = k;
+    for (int i = k + 1; i <= kMaxSeqs; ++i) a.item_pre[i] = (int32_t)items;
+    return items;
+}
+
+h3attn_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(H3ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_version(void) { return H3ATTN_VERSION; }
+
+const char *h3attn_status_string(h3attn_status s)
+{
+    switch (s) {
+    case H3ATTN_OK: return "H3ATTN_OK";
+    case H3ATTN_ERR_INVALID_ARG: return "H3ATTN_ERR_INVALID_ARG";
+    case H3ATTN_ERR_UNSUPPORTED: return "H3ATTN_ERR_UNSUPPORTED";
+    case H3ATTN_ERR_WORKSPACE: return "H3ATTN_ERR_WORKSPACE";
+    case H3ATTN_ERR_DEVICE: return "H3ATTN_ERR_DEVICE";
+    case H3ATTN_ERR_HIP: return "H3ATTN_ERR_HIP";
+    }
+    return "H3ATTN_UNKNOWN_STATUS";
+}
+
+const char *h3attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t h3attn_workspace_size(const h3attn_params *p, const int32_t *cu_seqlens_host, int quantized)
+{
+    Plan pl;
+    if (make_plan(p, cu_seqlens_host, &pl) != H3ATTN_OK) return 0;
+    if (quantized && pl.d != 128) {
+        fail(H3ATTN_ERR_UNSUPPORTED, "the quantised path needs head_dim 128");
+        return 0;
+    }
+    ok();
+    return quantized ? pl.bytes_q8 : pl.bytes_bf16;
+}
+
+h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                                void *out, void *workspace, size_t workspace_bytes, void *stream, int stages)
+{
+    Plan pl;
+    h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
+    if (st != H3ATTN_OK) return st;
+    if (stages < 1 || stages > 3) return fail(H3ATTN_ERR_INVALID_ARG, "stages must be 1, 2 or 3 (got %d)", stages);
+    if ((st = check_ptrs(q, k, v, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
+    if (!workspace) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(H3ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < pl.bytes_bf16)
+        return fail(H3ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes_bf16);
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    if (pl.N == 0) return ok();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+
+    PrologueArgs pa = prologue_args(p, pl, q, k, v, norm_w, rope_tables);
+    pa.qhat = reinterpret_cast<uint16_t *>(ws + pl.qhat);
+    pa.khat = reinterpret_cast<uint16_t *>(ws + pl.khat);
+    pa.vt = reinterpret_cast<uint16_t *>(ws + pl.vt);
+    pa.out_hstride = pl.Npad * pl.d;
+    pa.out_tstride = pl.d;
+    pa.natural = 0;
+    if (stages & 1)
+        if ((st = hip_status(launch_prologue(pa, pl.d, hs), "prologue launch")) != H3ATTN_OK) return st;
+    if (!(stages & 2)) return ok();
+
+    AttnArgs aa;
+    std::memset(&aa, 0, sizeof aa);
+    aa.qhat = pa.qhat;
+    aa.khat = pa.khat;
+    aa.vt = pa.vt;
+    aa.out = static_cast<uint16_t *>(out);
+    aa.o_stride = p->o_stride;
+    aa.Npad = pl.Npad;
+    aa.H = pl.H;
+    aa.scale_log2 = scale_log2(p);
+    const int64_t items = order_work(pl, aa, nullptr);
+    return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "attention launch");
+}
+
+h3attn_status h3attn_fwd(const h3attn_params *p, const void *q, const void *k, const void *v,
+                         const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                         void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return h3attn_fwd_stages(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, out, workspace,
+                             workspace_bytes, stream, 3);
+}
+
+h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void *k, const float *norm_w,
+                              const float *rope_tables, const int32_t *cu_seqlens_host, void *q_hat,
+                              void *k_hat, void *stream)
+{
+    Plan pl;
+    h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
+    if (st != H3ATTN_OK) return st;
+    if ((st = check_ptrs(q, k, q, norm_w, rope_tables, q_hat)) != H3ATTN_OK) return st;
+    if (!k_hat) return fail(H3ATTN_ERR_INVALID_ARG, "k_hat is NULL");
+    if (!aligned(k_hat, 16)) return fail(H3ATTN_ERR_INVALID_ARG, "k_hat is not 16-byte aligned");
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    if (pl.N == 0) return ok();
+    PrologueArgs pa = prologue_args(p, pl, q, k, q, norm_w, rope_tables);
+    pa.qhat = static_cast<uint16_t *>(q_hat);
+    pa.khat = static_cast<uint16_t *>(k_hat);
+    pa.vt = nullptr;
+    pa.out_hstride = pl.d;
+    pa.out_tstride = (int64_t)pl.H * pl.d;
+    pa.natural = 1;
+    return hip_status(launch_prologue(pa, pl.d, static_cast<hipStream_t>(stream)), "prologue launch");
+}
+
+h3attn_status h3attn_fwd_q8(const h3attn_params *p, const void *q, const void *k, const void *v,
+                            const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                            void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)p; (void)q; (void)k; (void)v; (void)norm_w; (void)rope_tables; (void)cu_seqlens_host;
+    (void)out; (void)workspace; (void)workspace_bytes; (void)stream;
+    return fail(H3ATTN_ERR_UNSUPPORTED, "quantised path not built yet");
+}
+
+h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                 const float *norm_w, const float *rope_tables,
+                                 const int32_t *cu_seqlens_host, void *workspace, size_t workspace_bytes,
+                                 int8_t *q8, int8_t *k8, float *q_scale, float *k_scale, float *k_mean,
+                                 uint8_t *v8, float *v_scale, void *stream)
+{
+    (void)p; (void)q; (void)k; (void)v; (void)norm_w; (void)rope_tables; (void)cu_seqlens_host;
+    (void)workspace; (void)workspace_bytes; (void)q8; (void)k8; (void)q_scale; (void)k_scale;
+    (void)k_mean; (void)v8; (void)v_scale; (void)stream;
+    return fail(H3ATTN_ERR_UNSUPPORTED, "quantised path not built yet");
+}
+
+h3attn_status h3attn_rope_fill_video(int32_t T, int32_t Hg, int32_t Wg, int32_t dt, int32_t dh, int32_t dw,
+                                     double theta, float *out)
+{
+    if (T < 0 || Hg < 1 || Wg < 1) return fail(H3ATTN_ERR_INVALID_ARG, "grid must be T >= 0, Hg, Wg >= 1");
+    if (dt < 2 || dh < 2 || dw < 2 || (dt | dh | dw) & 1)
+        return fail(H3ATTN_ERR_INVALID_ARG, "section sizes must be even and >= 2");
+    if (!(theta > 1.0) || !std::isfinite(theta)) return fail(H3ATTN_ERR_INVALID_ARG, "theta must be > 1");
+    if (!out && (int64_t)T * Hg * Wg > 0) return fail(H3ATTN_ERR_INVALID_ARG, "out is NULL");
+    const int half = (dt + dh + dw) / 2;
+    const int32_t secs[3] = {dt, dh, dw};
+    for (int64_t nidx = 0; nidx < (int64_t)T * Hg * Wg; ++nidx) {
+        const int64_t pos[3] = {nidx / ((int64_t)Hg * Wg), (nidx / Wg) % Hg, nidx % Wg};
+        float *row = out + nidx * half * 2;
+        int pair = 0;
+        for (int ax = 0; ax < 3; ++ax) {
+            for (int j = 0; j < secs[ax] / 2; ++j, ++pair) {
+                const double phi = (double)pos[ax] * std::pow(theta, -2.0 * j / secs[ax]);
+                row[2 * pair] = (float)std::cos(phi);
+                row[2 * pair + 1] = (float)std::sin(phi);
+            }
+        }
+    }
+    return ok();
+}
+
+h3attn_status h3attn_rope_fill_audio(int32_t n, int32_t pos0, int32_t dim, double theta, float *out)
+{
+    if (n < 0 || pos0 < 0) return fail(H3ATTN_ERR_INVALID_ARG, "n and pos0 must be >= 0");
+    if (dim < 2 || (dim & 1)) return fail(H3ATTN_ERR_INVALID_ARG, "dim must be even and >= 2");
+    if (!(theta > 1.0) || !std::isfinite(theta)) return fail(H3ATTN_ERR_INVALID_ARG, "theta must be > 1");
+    if (!out && n > 0) return fail(H3ATTN_ERR_INVALID_ARG, "out is NULL");
+    for (int64_t i = 0; i < n; ++i) {
+        float *row = out + i * dim;
+        for (int j = 0; j < dim / 2; ++j) {
+            const double phi = (double)(pos0 + i) * std::pow(theta, -2.0 * j / dim);
+            row[2 * j] = (float)std::cos(phi);
+            row[2 * j + 1] = (float)std::sin(phi);
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// Fused Q/K RMSNorm + RoPE + layout prologue for gfx950.
+//
+// The page "H3 Runtime Current State" lists "Fused Q/K RMSNorm, RoPE, and
+// layout work" under "Owned Performance Kernels"; "Buyer Questions: Current
+// Evidence Status" (question 4) measures norm/RoPE as about 4% of a block and
+// the strided-NHD QKV copy as about 3.6%.  This kernel does all of it in one
+// HBM pass: it reads q, k and v once through their token strides, normalises
+// and rotates q and k in fp32, and writes the head-major bf16 copies the
+// attention kernel streams (qhat, khat: [H][Npad][d]; vt: V transposed per
+// 64-key tile).  Padding rows of every sequence are written as zeros, so the
+// attention kernel never reads uninitialised memory.
+//
+// Work split: one workgroup (256 lanes) handles one 64-token tile of one head.
+// d/8 lanes share a (token, head) row, 16 bytes (8 channels) per lane, so
+// every global access is a coalesced 16-byte vector access and the RMSNorm
+// reduction is a d/8-lane butterfly.  RoPE pairs (2j, 2j+1) sit inside one
+// lane.  Workgroups are numbered so that all heads of one token tile run on
+// the same XCD (dispatch is round-robin over the 8 XCDs): the RoPE table rows
+// of the tile are then fetched into that XCD's L2 once.
+#include "h3_internal.h"
+
+namespace h3 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Position of token r (0..63) inside its tile of the transposed V copy: bits
+// 2 and 3 swapped, the order in which the attention kernel's P.V operand
+// consumes keys (see attn_bf16.hip).
+__device__ __forceinline__ int vt_pos(int r)
+{
+    return (r & ~0xC) | ((r >> 1) & 4) | ((r << 1) & 8);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
+{
+    constexpr int LPR = D / 8;          // lanes per (token, head) row
+    constexpr int RPP = 256 / LPR;      // rows per pass
+    __shared__ __attribute__((aligned(16))) uint16_t vl[D][64 + 8];
+
+    const int H = a.H;
+    const int b = blockIdx.x;
+    const int gt = 8 * ((b >> 3) / H) + (b & 7);    // padded tile index
+    const int h = (b >> 3) % H;
+    if (gt >= a.ntiles) return;
+    int s = 0;
+    while (s + 1 < a.seq.S && gt >= a.seq.off[s + 1] / kTile) ++s;
+    const int j = gt - a.seq.off[s] / kTile;
+    const int n_s = a.seq.cu[s + 1] - a.seq.cu[s];
+    const int valid = min(max(n_s - kTile * j, 0), kTile);
+    if (a.natural && valid == 0) return;
+
+    const int t = threadIdx.x;
+    const int c = t % LPR;
+    const int rr = t / LPR;
+    const float inv_d = 1.0f / (float)D;
+
+#pragma unroll
+    for (int pass = 0; pass < kTile / RPP; ++pass) {
+        const int r = pass * RPP + rr;
+        const bool ok = r < valid;
+        const int64_t tok = (int64_t)a.seq.cu[s] + kTile * j + r;
+        f32x4 cs0 = {1.f, 0.f, 1.f, 0.f}, cs1 = {1.f, 0.f, 1.f, 0.f};
+        if (ok) {
+            const f32x4 *rp = reinterpret_cast<const f32x4 *>(a.rope + tok * D + 8 * c);
+            cs0 = rp[0];
+            cs1 = rp[1];
+        }
+        const int64_t orow = a.natural ? tok : (int64_t)a.seq.off[s] + kTile * j + r;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const uint16_t *src = which ? a.k + tok * a.k_stride : a.q + tok * a.q_stride;
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (ok) raw = *reinterpret_cast<const u32x4 *>(src + h * D + 8 * c);
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = bf_lo(raw[i]);
+                x[2 * i + 1] = bf_hi(raw[i]);
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+#pragma unroll
+            for (int msk = LPR / 2; msk >= 1; msk >>= 1) ss += __shfl_xor(ss, msk, LPR);
+            const float rs = rsqrtf(fmaf(ss, inv_d, a.eps));
+            const f32x4 *wp = reinterpret_cast<const f32x4 *>(a.norm_w + (which * H + h) * D + 8 * c);
+            const f32x4 w0 = wp[0], w1 = wp[1];
+            const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+            const float cs[8] = {cs0[0], cs0[1], cs0[2], cs0[3], cs1[0], cs1[1], cs1[2], cs1[3]};
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float y0 = x[2 * i] * rs * wv[2 * i];
+                const float y1 = x[2 * i + 1] * rs * wv[2 * i + 1];
+                const float co = cs[2 * i], si = cs[2 * i + 1];
+                o[i] = pack_bf16(y0 * co - y1 * si, y0 * si + y1 * co);
+            }
+            if (!ok) o = (u32x4){0u, 0u, 0u, 0u};
+            if (ok || !a.natural) {
+                uint16_t *dst = (which ? a.khat : a.qhat) + h * a.out_hstride + orow * a.out_tstride + 8 * c;
+                *reinterpret_cast<u32x4 *>(dst) = o;
+            }
+        }
+        if (!a.natural) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (ok) raw = *reinterpret_cast<const u32x4 *>(a.v + tok * a.v_stride + h * D + 8 * c);
+            const int p = vt_pos(r);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vl[8 * c + 2 * i][p] = (uint16_t)(raw[i] & 0xffffu);
+                vl[8 * c + 2 * i + 1][p] = (uint16_t)(raw[i] >> 16);
+            }
+        }
+    }
+    if (a.natural) return;
+    __syncthreads();
+    uint16_t *vt = a.vt + ((int64_t)h * a.ntiles + gt) * (D * kTile);
+#pragma unroll
+    for (int g = t; g < D * 8; g += 256) {
+        const int row = g >> 3, cc = g & 7;
+        *reinterpret_cast<u32x4 *>(vt + row * kTile + 8 * cc) =
+            *reinterpret_cast<const u32x4 *>(&vl[row][8 * cc]);
+    }
+}
+
+hipError_t launch_prologue(const PrologueArgs &a, int d, hipStream_t st)
+{
+    const int64_t groups = (a.ntiles + 7) / 8;
+    const dim3 grid((unsigned)(groups * 8 * a.H));
+    if (d == 128)
+        hipLaunchKernelGGL(prologue_kernel<128>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(prologue_kernel<64>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace h3

@@ -1,0 +1,274 @@
+"""Thin ctypes binding of libh3attn.so (include/h3attn.h), same names as the C ABI.
+
+Argument marshalling only: tensors supply device pointers and the current
+HIP stream; every step of the computation runs in the library's kernels.  The
+library must have been built (``python -m audio_diffusion_transformer_amd.build``);
+loading fails loudly otherwise -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libh3attn.so")
+
+H3ATTN_OK = 0
+H3ATTN_ERR_INVALID_ARG = 1
+H3ATTN_ERR_UNSUPPORTED = 2
+H3ATTN_ERR_WORKSPACE = 3
+H3ATTN_ERR_DEVICE = 4
+H3ATTN_ERR_HIP = 5
+H3ATTN_MAX_SEQS = 64
+
+EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
+            "h3attn_prologue",
+            "h3attn_q8_prologue", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
+            "h3attn_status_string", "h3attn_last_error", "h3attn_version")
+
+
+class H3AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (status_string(status), msg))
+        self.status = status
+
+
+class h3attn_params(C.Structure):
+    _fields_ = [("num_heads", C.c_int32), ("head_dim", C.c_int32), ("num_seqs", C.c_int32),
+                ("flags", C.c_int32), ("q_stride", C.c_int64), ("k_stride", C.c_int64),
+                ("v_stride", C.c_int64), ("o_stride", C.c_int64), ("eps", C.c_float),
+                ("softmax_scale", C.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libh3attn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libh3attn.so is not built (%s); run "
+                               "`python -m audio_diffusion_transformer_amd.build`" % LIB_PATH)
+        L = C.CDLL(LIB_PATH)
+        P, vp = C.POINTER, C.c_void_p
+        L.h3attn_workspace_size.restype = C.c_size_t
+        L.h3attn_workspace_size.argtypes = [P(h3attn_params), P(C.c_int32), C.c_int]
+        fwd_args = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp, vp, C.c_size_t, vp]
+        for name in ("h3attn_fwd", "h3attn_fwd_q8"):
+            getattr(L, name).restype = C.c_int
+            getattr(L, name).argtypes = fwd_args
+        L.h3attn_fwd_stages.restype = C.c_int
+        L.h3attn_fwd_stages.argtypes = fwd_args + [C.c_int]
+        L.h3attn_prologue.restype = C.c_int
+        L.h3attn_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, P(C.c_int32), vp, vp, vp]
+        L.h3attn_q8_prologue.restype = C.c_int
+        L.h3attn_q8_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp,
+                                         C.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.h3attn_rope_fill_video.restype = C.c_int
+        L.h3attn_rope_fill_video.argtypes = [C.c_int32] * 6 + [C.c_double, P(C.c_float)]
+        L.h3attn_rope_fill_audio.restype = C.c_int
+        L.h3attn_rope_fill_audio.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_double, P(C.c_float)]
+        L.h3attn_status_string.restype = C.c_char_p
+        L.h3attn_status_string.argtypes = [C.c_int]
+        L.h3attn_last_error.restype = C.c_char_p
+        L.h3attn_version.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().h3attn_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().h3attn_last_error().decode()
+
+
+def version() -> int:
+    return int(lib().h3attn_version())
+
+
+def _check(status: int):
+    if status != H3ATTN_OK:
+        raise H3AttnError(status, last_error())
+
+
+def make_params(num_heads: int, head_dim: int, num_seqs: int, q_stride: int, k_stride: int,
+                v_stride: int, o_stride: int, eps: float = 1e-6, softmax_scale: float = 0.0,
+                flags: int = 0) -> h3attn_params:
+    return h3attn_params(num_heads, head_dim, num_seqs, flags, q_stride, k_stride, v_stride,
+                         o_stride, eps, softmax_scale)
+
+
+def _cu_array(cu_seqlens) -> np.ndarray:
+    if hasattr(cu_seqlens, "detach"):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    return np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+
+
+def _cu_ptr(cu: np.ndarray):
+    return cu.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def h3attn_workspace_size(params: h3attn_params, cu_seqlens, quantized: bool = False) -> int:
+    cu = _cu_array(cu_seqlens)
+    n = int(lib().h3attn_workspace_size(C.byref(params), _cu_ptr(cu), 1 if quantized else 0))
+    if n == 0:
+        raise H3AttnError(H3ATTN_ERR_INVALID_ARG, last_error())
+    return n
+
+
+# ---------------------------------------------------------------- raw calls
+
+def fwd_raw(params, q, k, v, norm_w, rope_tables, cu_seqlens, out, workspace, workspace_bytes,
+            stream, quantized: bool = False, stages: int = 3) -> int:
+    """Direct call with integer device pointers; returns the status code.
+    ``stages`` (1 prologue, 2 attention, 3 both) selects h3attn_fwd_stages /
+    h3attn_fwd_q8_stages when it is not 3."""
+    cu = _cu_array(cu_seqlens)
+    args = (C.byref(params), q, k, v, norm_w, rope_tables, _cu_ptr(cu), out, workspace,
+            workspace_bytes, stream)
+    if stages != 3:
+        f = lib().h3attn_fwd_q8_stages if quantized else lib().h3attn_fwd_stages
+        return int(f(*args, int(stages)))
+    f = lib().h3attn_fwd_q8 if quantized else lib().h3attn_fwd
+    return int(f(*args))
+
+
+# ------------------------------------------------------------ torch helpers
+
+def _dev_ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def params_for(q, k, v, out, num_seqs: int, eps: float = 1e-6, softmax_scale: float = 0.0):
+    """Params from [N, H, d] bf16 tensors (any token stride, unit channel stride)."""
+    N, H, d = q.shape
+    for t in (q, k, v, out):
+        if t.dim() != 3 or t.shape[1:] != (H, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError("q/k/v/out must be [N, H, d] with contiguous heads and channels")
+    return make_params(H, d, num_seqs, q.stride(0), k.stride(0), v.stride(0), out.stride(0),
+                       eps, softmax_scale)
+
+
+def workspace_for(q, cu_seqlens, quantized: bool = False, eps: float = 1e-6):
+    import torch
+    N, H, d = q.shape
+    cu = _cu_array(cu_seqlens)
+    p = make_params(H, d, len(cu) - 1, H * d, H * d, H * d, H * d, eps)
+    n = h3attn_workspace_size(p, cu, quantized)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=None,
+               eps: float = 1e-6, softmax_scale: float = 0.0, stream=None, quantized: bool = False,
+               stages: int = 3):
+    """out[N, H, d] (bf16) = fused RMSNorm + RoPE + attention of bf16 q, k, v [N, H, d].
+
+    norm_w: fp32 [2, H, d] on the device; rope_tables: fp32 [N, d/2, 2] on the
+    device; cu_seqlens: int32 [S+1] (host array or CPU tensor)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    cu = _cu_array(cu_seqlens)
+    params = params_for(q, k, v, out, len(cu) - 1, eps, softmax_scale)
+    if workspace is None:
+        workspace = torch.empty(h3attn_workspace_size(params, cu, quantized), dtype=torch.uint8,
+                                device=q.device)
+    _check(fwd_raw(params, _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w),
+                   _dev_ptr(rope_tables), cu, _dev_ptr(out), _dev_ptr(workspace),
+                   workspace.numel() * workspace.element_size(), _stream_ptr(stream), quantized,
+                   stages))
+    return out
+
+
+def h3attn_fwd_q8(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=None,
+                  eps: float = 1e-6, softmax_scale: float = 0.0, stream=None):
+    return h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out, workspace, eps,
+                      softmax_scale, stream, quantized=True)
+
+
+def h3attn_prologue(q, k, norm_w, rope_tables, cu_seqlens, q_hat=None, k_hat=None,
+                    eps: float = 1e-6, stream=None):
+    import torch
+    q_hat = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if q_hat is None else q_hat
+    k_hat = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if k_hat is None else k_hat
+    cu = _cu_array(cu_seqlens)
+    params = params_for(q, k, q, q_hat, len(cu) - 1, eps)
+    _check(lib().h3attn_prologue(C.byref(params), _dev_ptr(q), _dev_ptr(k), _dev_ptr(norm_w),
+                                 _dev_ptr(rope_tables), _cu_ptr(cu), _dev_ptr(q_hat),
+                                 _dev_ptr(k_hat), _stream_ptr(stream)))
+    return q_hat, k_hat
+
+
+def h3attn_q8_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,
+                       eps: float = 1e-6, stream=None):
+    """Quantised prologue exported in natural layouts (see include/h3attn.h)."""
+    import torch
+    N, H, d = q.shape
+    cu = _cu_array(cu_seqlens)
+    S = len(cu) - 1
+    nblocks = int(sum((int(cu[s + 1] - cu[s]) + 63) // 64 for s in range(S)))
+    params = params_for(q, k, v, q, S, eps)
+    if workspace is None:
+        workspace = torch.empty(h3attn_workspace_size(params, cu, True), dtype=torch.uint8,
+                                device=q.device)
+    dev = q.device
+    res = {
+        "q8": torch.empty((N, H, d), dtype=torch.int8, device=dev),
+        "k8": torch.empty((N, H, d), dtype=torch.int8, device=dev),
+        "q_scale": torch.empty((H, nblocks), dtype=torch.float32, device=dev),
+        "k_scale": torch.empty((H, nblocks), dtype=torch.float32, device=dev),
+        "k_mean": torch.empty((S, H, d), dtype=torch.float32, device=dev),
+        "v8": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
+        "v_scale": torch.empty((S, H, d), dtype=torch.float32, device=dev),
+    }
+    _check(lib().h3attn_q8_prologue(
+        C.byref(params), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w),
+        _dev_ptr(rope_tables), _cu_ptr(cu), _dev_ptr(workspace),
+        workspace.numel() * workspace.element_size(),
+        *[_dev_ptr(res[n]) for n in ("q8", "k8", "q_scale", "k_scale", "k_mean", "v8", "v_scale")],
+        _stream_ptr(stream)))
+    return res
+
+
+# ------------------------------------------------------------- RoPE tables
+
+def h3attn_rope_fill_video(T: int, Hg: int, Wg: int, dt: int, dh: int, dw: int,
+                           theta: float = 10000.0) -> np.ndarray:
+    out = np.zeros((T * Hg * Wg, (dt + dh + dw) // 2, 2), dtype=np.float32)
+    _check(lib().h3attn_rope_fill_video(T, Hg, Wg, dt, dh, dw, float(theta),
+                                        out.ctypes.data_as(C.POINTER(C.c_float))))
+    return out
+
+
+def h3attn_rope_fill_audio(n: int, pos0: int, dim: int, theta: float = 10000.0) -> np.ndarray:
+    out = np.zeros((n, dim // 2, 2), dtype=np.float32)
+    _check(lib().h3attn_rope_fill_audio(n, pos0, dim, float(theta),
+                                        out.ctypes.data_as(C.POINTER(C.c_float))))
+    return out
+
+
+def rope_table(seqs: Sequence, split, d: int, theta: float = 10000.0) -> np.ndarray:
+    """Packed RoPE table [N, d/2, 2] for sequences given as (T, Hg, Wg, n_audio):
+    each sequence's video grid rows followed by its audio rows (positions from 0)."""
+    parts = []
+    for s in seqs:
+        T, Hg, Wg, na = (s.T, s.Hg, s.Wg, s.n_audio) if hasattr(s, "T") else tuple(s)
+        if T * Hg * Wg > 0:
+            parts.append(h3attn_rope_fill_video(T, Hg, Wg, *split, theta=theta))
+        if na > 0:
+            parts.append(h3attn_rope_fill_audio(na, 0, d, theta=theta))
+    if not parts:
+        return np.zeros((0, d // 2, 2), dtype=np.float32)
+    return np.ascontiguousarray(np.concatenate(parts, axis=0))

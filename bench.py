@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused RMSNorm + RoPE + attention hot path on one MI355X.
+
+One step = one h3attn_fwd pass (the prologue kernel, then the attention
+kernel) over the joint video+audio workload: one packed sequence of a
+t31 x h48 x w84 video grid (124,992 tokens) plus 250 audio tokens, H = 24,
+d = 128, bf16 inputs already resident in HBM.  The step is issued as its two
+stages (h3attn_fwd_stages 1 then 2, exactly what h3attn_fwd does) with HIP
+events between them on the launch stream, so each kernel's average duration
+is measured live over the timed region.
+
+Prints one JSON line: whole-step attention TFLOP/s (4 * sum n_i^2 * d * H per
+step), the attention kernel's roofline against the bf16 dense MFMA peak, and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_DENSE_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense, no sparsity)
+MI355X_FP8_DENSE_TFLOPS = 5033.2
+MI355X_HBM_GBPS = 8000.0
+METRIC = "attention TFLOP/s and % of bf16 MFMA peak at N=125k packed tokens, H=24, d=128"
+
+
+def kernel_source_sha(name: str) -> str:
+    path = os.path.join(ROOT, "audio_diffusion_transformer_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel_file: str, summary: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != kernel_source_sha(kernel_file):
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, inputs, seconds: float, threads: int):
+    """Time the fp64 CPU oracle on sampled query rows of one head (full key set)."""
+    import oracle
+    p = oracle.Problem.from_workload(w, inputs)
+    n = w.seqs[0].n
+    rng = np.random.default_rng(w.seed + 99)
+    head = int(rng.integers(w.H))
+    flops_per_row = 4.0 * n * w.d
+
+    def run(nrows):
+        toks = np.sort(rng.choice(n, size=nrows, replace=False)).astype(np.int64)
+        rows = toks * w.H + head
+        t0 = time.perf_counter()
+        p.attention_rows(rows, nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe = 2 * threads
+    t_probe = run(probe)
+    nrows = int(max(probe, min(n, probe * seconds / max(t_probe, 1e-3))))
+    t = run(nrows)
+    return {
+        "value": round(nrows * flops_per_row / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d query rows of head %d (of %d x %d rows), each over all %d keys; fp64; "
+                  "the keys' RMSNorm+RoPE included; %.1f s" % (nrows, head, w.N, w.H, n, t),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="joint")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from audio_diffusion_transformer_amd import h3attn as h
+    from audio_diffusion_transformer_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = synth.generate(w)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"].view(np.int16)).to(dev).view(torch.bfloat16)
+    k = torch.from_numpy(inp["k"].view(np.int16)).to(dev).view(torch.bfloat16)
+    v = torch.from_numpy(inp["v"].view(np.int16)).to(dev).view(torch.bfloat16)
+    norm_w = torch.from_numpy(inp["norm_w"]).to(dev)
+    rope = torch.from_numpy(h.rope_table(w.seqs, w.split, w.d, w.theta)).to(dev)
+    cu = inp["cu_seqlens"]
+    out = torch.empty_like(q)
+    params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
+    ws_bytes = h.h3attn_workspace_size(params, cu, w.quantized)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
+    torch.cuda.synchronize()
+    print("[bench] inputs ready for %s (N=%d) in %.1f s" % (w.name, w.N, time.time() - t0),
+          file=sys.stderr, flush=True)
+
+    def stage(sid):
+        st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp,
+                       w.quantized, sid)
+        if st != 0:
+            raise RuntimeError("%s: %s" % (h.status_string(st), h.last_error()))
+
+    for _ in range(args.warmup):
+        stage(1)
+        stage(2)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        stage(1)
+        ev[i][1].record(stream)
+        stage(2)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    pro_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    att_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_step = total_ms / K
+    att_avg = float(np.mean(att_ms))
+    pro_avg = float(np.mean(pro_ms))
+    print("[bench] %d steps: %.3f ms/step (attention %.3f, prologue %.3f), wall %.3f s" % (
+        K, ms_step, att_avg, pro_avg, wall), file=sys.stderr, flush=True)
+
+    flops = w.flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    peak = MI355X_FP8_DENSE_TFLOPS if w.quantized else MI355X_BF16_DENSE_TFLOPS
+    achieved = flops / (att_avg * 1e-3) / 1e12
+    kernel_file = "q8.hip" if w.quantized else "attn_bf16.hip"
+    summary = ("attn_q8_%s_pmc.md" if w.quantized else "attn_bf16_%s_pmc.md") % w.name
+    traffic = measured_traffic(kernel_file, summary)
+    N, H, d = w.N, w.H, w.d
+    pro_bytes = 3 * N * H * d * 2 + 3 * N * H * d * 2 + N * (d // 2) * 8   # read q,k,v,table; write 3 copies
+    res = {
+        "metric": METRIC if w.name == "joint" else METRIC.replace("N=125k", "N=%d" % N),
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8/fp8" if w.quantized else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "tokens": N, "heads": H,
+                   "head_dim": d, "seq_lens": [s.n for s in w.seqs], "parallelism": "none"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "attn_q8_kernel" if w.quantized else "attn_bf16_kernel<128>",
+                     "avg_ms": round(att_avg, 4)},
+        "kernels": {"prologue_avg_ms": round(pro_avg, 4),
+                    "prologue_GBps": round(pro_bytes / (pro_avg * 1e-3) / 1e9, 1),
+                    "prologue_hbm_frac": round(pro_bytes / (pro_avg * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4),
+                    "attention_avg_ms": round(att_avg, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        print("[bench] timing the CPU oracle on %d threads" % threads, file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, threads)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

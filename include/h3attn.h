@@ -1,0 +1,188 @@
+/*
+ * h3attn.h -- C ABI of the MI355X (gfx950) fused Q/K RMSNorm + RoPE +
+ * non-causal multi-head attention library.
+ *
+ * The operation is the self-attention of a joint video+audio diffusion
+ * transformer block (MiniMax-H3) over its packed token sequence, with the Q/K
+ * RMSNorm and RoPE that the page "H3 Runtime Current State" lists, under
+ * "Owned Performance Kernels", as fused "Q/K RMSNorm, RoPE, and layout work"
+ * still owed beside an H3-specific attention backend.  The page "Buyer
+ * Questions: Current Evidence Status", question 4 ("Current answer"), puts
+ * attention at about 58% and norm/RoPE at about 4% of a block and credits the
+ * removal of the strided-NHD QKV copy with about 3.6%: here q, k and v are
+ * read through token strides, so views into a fused QKV buffer need no copy.
+ *
+ * For every sequence s (packed tokens [cu[s], cu[s+1])), head h and token i:
+ *   qhat_i = RoPE_i( q_i / sqrt(mean_c q_ic^2 + eps) * w_q[h] )   (same for k with w_k[h])
+ *   o_i    = sum_j softmax_j( scale * qhat_i . khat_j ) v_j       (j in the same sequence)
+ * RoPE rotates interleaved pairs (2j, 2j+1) of each section by the per-token
+ * angles in `rope_tables` (see h3attn_rope_fill_video / _audio).  Non-causal;
+ * sequences do not see each other.
+ *
+ * Conventions shared by every entry point
+ *  - Ownership: every pointer is caller-owned.  The library never allocates,
+ *    frees or keeps a pointer after the call returns.
+ *  - Asynchrony: device work is enqueued on `stream` (a hipStream_t; NULL is
+ *    the null stream) and the call returns without synchronising.  Buffers must
+ *    stay alive until the stream reaches that point.  No call allocates or
+ *    copies host memory to the device, so the calls may be captured in a HIP
+ *    graph (cu_seqlens is read on the host and baked into kernel arguments).
+ *  - Errors: every function returns a status; on anything but H3ATTN_OK
+ *    nothing was enqueued (except H3ATTN_ERR_HIP after a failed launch) and
+ *    h3attn_last_error() gives a message (thread-local).  Argument checks run
+ *    on the host before any HIP call.  No C++ exception crosses the ABI.
+ *  - Device: the current HIP device must be a gfx950 (MI355X); otherwise
+ *    H3ATTN_ERR_DEVICE.
+ *  - Aliasing: q, k and v may alias one another (e.g. views of a fused
+ *    [N, 3, H, d] buffer).  out and the workspace must not overlap any input.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3ATTN_VERSION 1
+#define H3ATTN_MAX_SEQS 64      /* sequences per call */
+
+typedef enum h3attn_status {
+    H3ATTN_OK = 0,
+    H3ATTN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, stride or cu_seqlens */
+    H3ATTN_ERR_UNSUPPORTED = 2,   /* shape the kernels do not implement */
+    H3ATTN_ERR_WORKSPACE = 3,     /* workspace too small or misaligned */
+    H3ATTN_ERR_DEVICE = 4,        /* no HIP device, or not a gfx950 */
+    H3ATTN_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+} h3attn_status;
+
+/* Shape and numerics of one call.  H = num_heads, d = head_dim. */
+typedef struct h3attn_params {
+    int32_t num_heads;     /* H >= 1 */
+    int32_t head_dim;      /* d: 64 or 128 */
+    int32_t num_seqs;      /* S in [1, H3ATTN_MAX_SEQS] */
+    int32_t flags;         /* reserved, must be 0 */
+    int64_t q_stride;      /* elements between consecutive tokens of q: >= H*d, multiple of 8 */
+    int64_t k_stride;      /* same for k */
+    int64_t v_stride;      /* same for v */
+    int64_t o_stride;      /* same for out */
+    float eps;             /* RMSNorm epsilon (> 0, e.g. 1e-6) */
+    float softmax_scale;   /* scale on q.k; <= 0 selects 1/sqrt(d) */
+} h3attn_params;
+
+/*
+ * Bytes of device workspace h3attn_fwd (quantized = 0) or h3attn_fwd_q8
+ * (quantized = 1) needs for this shape.  cu_seqlens_host: HOST int32 [S+1],
+ * cu[0] = 0, non-decreasing; N = cu[S] is the packed token count.  Returns 0
+ * and sets the last error when the arguments are invalid.
+ */
+size_t h3attn_workspace_size(const h3attn_params *p, const int32_t *cu_seqlens_host,
+                             int quantized);
+
+/*
+ * Fused RMSNorm + RoPE + attention in bf16 with fp32 accumulation.
+ *   q, k, v     device bf16, token t head h channel c at x[t*stride + h*d + c]
+ *   norm_w      device fp32 [2][H][d]: RMSNorm weights of q, then of k
+ *   rope_tables device fp32 [N][d/2][2]: (cos, sin) of the angle of pair j of token t
+ *   cu_seqlens_host HOST int32 [S+1] (see h3attn_workspace_size)
+ *   out         device bf16, token stride o_stride, same channel order as q
+ *   workspace   device, 256-byte aligned, >= h3attn_workspace_size(p, cu, 0) bytes;
+ *               its contents on entry do not matter and on exit are unspecified
+ *   stream      hipStream_t
+ * Sequences of length 0 are allowed and produce nothing.
+ */
+h3attn_status h3attn_fwd(const h3attn_params *p, const void *q, const void *k, const void *v,
+                         const float *norm_w, const float *rope_tables,
+                         const int32_t *cu_seqlens_host, void *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * The two stages of h3attn_fwd as separate launches, for callers that time or
+ * schedule them apart: stages = 1 runs the RMSNorm + RoPE + layout prologue
+ * (q, k, v -> workspace), stages = 2 the attention (workspace -> out), 3 both.
+ * Same arguments and requirements as h3attn_fwd; a stage-2 call must follow a
+ * stage-1 call with the same inputs and workspace on the same stream.
+ * h3attn_fwd(...) is exactly h3attn_fwd_stages(..., 3).
+ */
+h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const void *k,
+                                const void *v, const float *norm_w, const float *rope_tables,
+                                const int32_t *cu_seqlens_host, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream, int stages);
+
+/*
+ * Block-quantised variant with the same arguments and result layout
+ * (workspace >= h3attn_workspace_size(p, cu, 1)).  After the same RMSNorm +
+ * RoPE: the per-sequence mean of khat over tokens is subtracted (which leaves
+ * softmax unchanged); qhat and khat are quantised to symmetric INT8 with one
+ * scale per 64-token block (aligned to the sequence start) per head; v to FP8
+ * e4m3 with one scale per (sequence, head, channel); scores use INT8 MFMA
+ * with i32 accumulation, probabilities are quantised to FP8 e4m3 with a fixed
+ * per-row scale and P.V uses FP8 MFMA with fp32 accumulation.  Lossy: the
+ * result approximates h3attn_fwd.  The quantised-path design of SageAttention2,
+ * the default quality backend on the page "H3 Runtime Current State", is the
+ * prior art.
+ */
+h3attn_status h3attn_fwd_q8(const h3attn_params *p, const void *q, const void *k,
+                            const void *v, const float *norm_w, const float *rope_tables,
+                            const int32_t *cu_seqlens_host, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * Diagnostic: the fused RMSNorm + RoPE prologue alone, written as bf16 qhat and
+ * khat in the natural layout (token stride H*d), using the same kernel code as
+ * h3attn_fwd.  q_hat and k_hat: device bf16 [N][H][d].
+ */
+h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void *k,
+                              const float *norm_w, const float *rope_tables,
+                              const int32_t *cu_seqlens_host, void *q_hat, void *k_hat,
+                              void *stream);
+
+/*
+ * Diagnostic: the quantised prologue of h3attn_fwd_q8, exported in natural
+ * layouts.  Runs the same kernels as h3attn_fwd_q8 into `workspace`, then
+ * copies out:
+ *   q8, k8    device int8 [N][H][d]   INT8 codes of qhat and of khat - mean
+ *   q_scale,
+ *   k_scale   device fp32 [H][B]      B = sum over sequences of ceil(n_s / 64);
+ *                                     block b of sequence s is entry
+ *                                     (sum_{s'<s} ceil(n_s'/64)) + b
+ *   k_mean    device fp32 [S][H][d]   per-sequence mean of khat
+ *   v8        device uint8 [N][H][d]  FP8 e4m3 codes of v
+ *   v_scale   device fp32 [S][H][d]   per-(sequence, head, channel) scale of v
+ */
+h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const void *k,
+                                 const void *v, const float *norm_w, const float *rope_tables,
+                                 const int32_t *cu_seqlens_host, void *workspace,
+                                 size_t workspace_bytes, int8_t *q8, int8_t *k8,
+                                 float *q_scale, float *k_scale, float *k_mean, uint8_t *v8,
+                                 float *v_scale, void *stream);
+
+/*
+ * Host helpers that fill RoPE tables (fp32 (cos, sin) pairs) on the host.
+ * Video: a T x Hg x Wg latent grid in t-major raster order (token n has
+ * t = n / (Hg*Wg), y = (n / Wg) % Hg, x = n % Wg, all 0-based); dims [0, dt)
+ * rotate with t, [dt, dt+dh) with y, [dt+dh, dt+dh+dw) with x; a section of D
+ * dims turns its pair j by pos * theta^(-2j/D).  out: [T*Hg*Wg][(dt+dh+dw)/2][2].
+ * Audio: n tokens at positions pos0 .. pos0+n-1, one section over all `dim`
+ * dims.  out: [n][dim/2][2].  Section sizes must be even and positive
+ * (dt, dh, dw >= 2).  The pages give no formula for the rotation; this is the
+ * original interleaved-pair RoPE applied per axis.
+ */
+h3attn_status h3attn_rope_fill_video(int32_t T, int32_t Hg, int32_t Wg, int32_t dt, int32_t dh,
+                                     int32_t dw, double theta, float *out);
+h3attn_status h3attn_rope_fill_audio(int32_t n, int32_t pos0, int32_t dim, double theta,
+                                     float *out);
+
+/* Static name of a status code. */
+const char *h3attn_status_string(h3attn_status s);
+/* Detail of the calling thread's last non-OK status ("" if none). */
+const char *h3attn_last_error(void);
+/* H3ATTN_VERSION of the built library. */
+int h3attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H3ATTN_H */

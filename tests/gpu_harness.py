@@ -1,0 +1,93 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, run the HIP
+path through the C ABI, and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import os
+import sys
+from typing import Dict
+
+import numpy as np
+
+import oracle
+from audio_diffusion_transformer_amd import h3attn as h
+from audio_diffusion_transformer_amd import synth
+
+
+def announce(msg: str):
+    """Name the case on the real stderr before a GPU step (survives a lost box)."""
+    sys.__stderr__.write("[gpu-step] %s\n" % msg)
+    sys.__stderr__.flush()
+
+
+def oracle_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def to_device(inputs: Dict[str, np.ndarray], w: synth.Workload, device="cuda:0"):
+    import torch
+    t = {}
+    for key in ("q", "k", "v"):
+        t[key] = torch.from_numpy(inputs[key].view(np.int16)).to(device).view(torch.bfloat16)
+    t["norm_w"] = torch.from_numpy(inputs["norm_w"]).to(device)
+    t["rope"] = torch.from_numpy(h.rope_table(w.seqs, w.split, w.d, w.theta)).to(device)
+    t["cu"] = inputs["cu_seqlens"]
+    return t
+
+
+def run(w: synth.Workload, t, quantized=False, out=None, workspace=None, stream=None, label=""):
+    import torch
+    announce("%s workload=%s seed=%d N=%d H=%d d=%d entry=%s" % (
+        label, w.name, w.seed, w.N, w.H, w.d, "h3attn_fwd_q8" if quantized else "h3attn_fwd"))
+    o = h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], out=out,
+                     workspace=workspace, eps=w.eps, stream=stream, quantized=quantized)
+    torch.cuda.synchronize()
+    return o
+
+
+def bits(o) -> np.ndarray:
+    import torch
+    return o.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def decode(b: np.ndarray) -> np.ndarray:
+    return synth.f32_from_bf16_bits(b).astype(np.float64)
+
+
+def metrics(got: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
+    d = got - ref
+    return {
+        "max_abs": float(np.abs(d).max()),
+        "mean_abs": float(np.abs(d).mean()),
+        "rmse": float(np.sqrt((d * d).mean())),
+        "rel_l2": float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)),
+        "cosine": float((got * ref).sum() / max(np.linalg.norm(got) * np.linalg.norm(ref), 1e-300)),
+        "ref_mean_abs": float(np.abs(ref).mean()),
+    }
+
+
+# bf16 path gates: the max/mean absolute bounds of the target, plus relative
+# guards (rel-L2, cosine) that an all-zero or norm-skipping output would fail.
+BF16_GATE = dict(max_abs=2e-2, mean_abs=2e-3, rel_l2=1e-2, cosine=0.9999)
+# quantised path: mean-abs bound of the target plus relative guards.
+Q8_GATE = dict(mean_abs=2e-2, rel_l2=0.1, cosine=0.995)
+
+
+def check(m: Dict[str, float], gate: Dict[str, float], label: str):
+    bad = []
+    for k, lim in gate.items():
+        if k == "cosine":
+            if not m[k] >= lim:
+                bad.append("%s %.6g < %g" % (k, m[k], lim))
+        elif not m[k] <= lim:
+            bad.append("%s %.6g > %g" % (k, m[k], lim))
+    announce("%s metrics %s" % (label, {k: round(v, 8) for k, v in m.items()}))
+    assert not bad, "%s: %s" % (label, "; ".join(bad))
+
+
+def oracle_rows(w: synth.Workload, inputs, rows: np.ndarray) -> np.ndarray:
+    p = oracle.Problem.from_workload(w, inputs)
+    return p.attention_rows(rows, nthreads=oracle_threads())
+
+
+def gpu_rows(out_bits: np.ndarray, rows: np.ndarray, H: int) -> np.ndarray:
+    return decode(out_bits[rows // H, rows % H])

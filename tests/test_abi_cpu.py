@@ -1,0 +1,201 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load and export every function include/h3attn.h declares;
+every argument error must be reported, with a message, before any HIP call;
+the host RoPE table helpers must agree with the oracle's independently
+computed fp64 angles.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from audio_diffusion_transformer_amd import h3attn as h
+from audio_diffusion_transformer_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3attn.h")
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3attn_\w+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = h.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), "libh3attn.so does not export %s" % n
+    assert set(names) <= set(h.EXPORTED) | {"h3attn_fwd_q8_stages"}
+    assert h.version() == 1
+
+
+def test_status_strings():
+    for code, name in [(0, "H3ATTN_OK"), (1, "H3ATTN_ERR_INVALID_ARG"), (2, "H3ATTN_ERR_UNSUPPORTED"),
+                       (3, "H3ATTN_ERR_WORKSPACE"), (4, "H3ATTN_ERR_DEVICE"), (5, "H3ATTN_ERR_HIP")]:
+        assert h.status_string(code) == name
+
+
+FAKE = 1 << 20          # aligned fake device address; never dereferenced on a failing path
+
+
+def _params(**kw):
+    base = dict(num_heads=24, head_dim=128, num_seqs=1, q_stride=3072, k_stride=3072,
+                v_stride=3072, o_stride=3072, eps=1e-6, softmax_scale=0.0, flags=0)
+    base.update(kw)
+    return h.make_params(**base)
+
+
+def _call(params=None, cu=(0, 1000), ws_bytes=1 << 40, ptrs=None, quantized=False, stages=3):
+    params = params if params is not None else _params()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, norm_w=FAKE, rope=FAKE, out=FAKE, ws=FAKE * 256)
+    p.update(ptrs or {})
+    return h.fwd_raw(params, p["q"], p["k"], p["v"], p["norm_w"], p["rope"], np.array(cu, np.int32),
+                     p["out"], p["ws"], ws_bytes, None, quantized, stages)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(num_heads=0), "num_heads"),
+    (dict(head_dim=96), "head_dim"),
+    (dict(num_seqs=0), "num_seqs"),
+    (dict(num_seqs=65), "num_seqs"),
+    (dict(flags=1), "flags"),
+    (dict(q_stride=3064), "q_stride"),
+    (dict(k_stride=3073), "k_stride"),
+    (dict(v_stride=100), "v_stride"),
+    (dict(o_stride=3076), "o_stride"),
+    (dict(eps=0.0), "eps"),
+    (dict(eps=float("nan")), "eps"),
+    (dict(softmax_scale=float("inf")), "softmax_scale"),
+])
+def test_invalid_params_rejected_before_any_hip_call(kw, msg):
+    st = _call(_params(**kw))
+    assert st in (h.H3ATTN_ERR_INVALID_ARG, h.H3ATTN_ERR_UNSUPPORTED)
+    assert msg in h.last_error()
+
+
+@pytest.mark.parametrize("cu,msg", [((1, 10), "cu_seqlens[0]"), ((0, 10, 5), "decreases")])
+def test_invalid_cu_seqlens(cu, msg):
+    st = _call(_params(num_seqs=len(cu) - 1), cu=cu)
+    assert st == h.H3ATTN_ERR_INVALID_ARG and msg in h.last_error()
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "norm_w", "rope", "out"])
+def test_null_and_misaligned_pointers(name):
+    assert _call(ptrs={name: 0}) == h.H3ATTN_ERR_INVALID_ARG
+    assert "NULL" in h.last_error()
+    assert _call(ptrs={name: FAKE + 8}) == h.H3ATTN_ERR_INVALID_ARG
+    assert "aligned" in h.last_error()
+
+
+def test_workspace_errors():
+    need = h.h3attn_workspace_size(_params(), [0, 1000])
+    assert _call(ws_bytes=need - 1) == h.H3ATTN_ERR_WORKSPACE and "needs" in h.last_error()
+    assert _call(ptrs={"ws": 0}) == h.H3ATTN_ERR_WORKSPACE
+    assert _call(ptrs={"ws": FAKE * 256 + 128}) == h.H3ATTN_ERR_WORKSPACE
+    assert _call(stages=0) == h.H3ATTN_ERR_INVALID_ARG and "stages" in h.last_error()
+    assert _call(stages=4) == h.H3ATTN_ERR_INVALID_ARG
+
+
+def test_workspace_size_layout():
+    # three head-major bf16 copies; every sequence padded to 256 tokens
+    p = _params()
+    cu = [0, 18144, 63394, 70594]
+    got = h.h3attn_workspace_size(_params(num_seqs=3), cu)
+    npad = sum(-(-(cu[i + 1] - cu[i]) // 256) * 256 for i in range(3))
+    assert got == 3 * 24 * npad * 128 * 2
+    assert h.h3attn_workspace_size(p, [0, 0]) == 256     # empty input is valid; 0 means error
+    with pytest.raises(h.H3AttnError):
+        h.h3attn_workspace_size(_params(head_dim=80), [0, 10])
+    with pytest.raises(h.H3AttnError):
+        h.h3attn_workspace_size(_params(head_dim=64, num_heads=2, q_stride=128, k_stride=128,
+                                        v_stride=128, o_stride=128), [0, 10], quantized=True)
+
+
+@pytest.mark.skipif(_gpu_present(), reason="checks the no-device error path; a GPU is present")
+def test_valid_call_without_gpu_reports_device_error():
+    assert _call() == h.H3ATTN_ERR_DEVICE
+    assert "device" in h.last_error().lower()
+
+
+def test_error_message_is_thread_local():
+    import threading
+    _call(_params(num_heads=0))
+    msgs = []
+
+    def other():
+        msgs.append(h.last_error())
+        _call(_params(head_dim=3))
+        msgs.append(h.last_error())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert msgs[0] == "" and "head_dim" in msgs[1]
+    assert "num_heads" in h.last_error()
+
+
+# ----------------------------------------------------------- RoPE tables
+
+def _oracle_angles(seqs, split, d):
+    N = sum(s[0] * s[1] * s[2] + s[3] for s in seqs)
+    z = np.zeros((N, 1, d), np.uint16)
+    p = oracle.Problem(1, d, seqs, split, z, z, z, np.ones((2, 1, d), np.float32))
+    out = np.zeros((N, d // 2))
+    for t in range(N):
+        _, aud, pos = p.token_pos(t)
+        out[t] = p.rope_angles(aud, pos)
+    return out
+
+
+@pytest.mark.parametrize("seqs,split,d", [
+    ([(4, 8, 8, 0)], (16, 24, 24), 64),
+    ([(3, 7, 9, 250), (2, 5, 5, 0), (0, 1, 1, 4)], (32, 48, 48), 128),
+])
+def test_rope_tables_match_oracle_angles(seqs, split, d):
+    tab = h.rope_table(seqs, split, d)
+    phi = _oracle_angles(seqs, split, d)
+    assert tab.shape == (phi.shape[0], d // 2, 2) and tab.dtype == np.float32
+    np.testing.assert_allclose(tab[..., 0], np.cos(phi), atol=1e-7, rtol=0)
+    np.testing.assert_allclose(tab[..., 1], np.sin(phi), atol=1e-7, rtol=0)
+
+
+def test_rope_fill_argument_errors():
+    out = (ctypes.c_float * 64)()
+    L = h.lib()
+    assert L.h3attn_rope_fill_video(1, 1, 1, 3, 2, 2, 1e4, out) == h.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_rope_fill_video(1, 0, 1, 2, 2, 2, 1e4, out) == h.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_rope_fill_video(1, 1, 1, 2, 2, 2, 0.5, out) == h.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_rope_fill_audio(2, -1, 8, 1e4, out) == h.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_rope_fill_audio(2, 0, 7, 1e4, out) == h.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_rope_fill_audio(2, 0, 8, 1e4, None) == h.H3ATTN_ERR_INVALID_ARG
+
+
+def test_synth_is_seeded_and_bf16_rounding_is_nearest_even():
+    w = synth.WORKLOADS["tiny"]
+    a, b = synth.generate(w), synth.generate(w)
+    for key in ("q", "k", "v", "norm_w"):
+        np.testing.assert_array_equal(a[key], b[key])
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.5], np.float32)   # ties -> even
+    np.testing.assert_array_equal(synth.f32_from_bf16_bits(synth.bf16_bits_from_f32(x)),
+                                  [1.0, 1.0 + 2 ** -6, -1.5])
+    rows = synth.sample_rows(synth.WORKLOADS["ragged"], 4096)
+    assert len(rows) == 4096 and len(np.unique(rows)) == 4096
+    H = 24
+    toks = set((rows // H).tolist())
+    for t in (0, 18143, 18144, 18144 + 45000, 63393, 63394, 70593):
+        assert t in toks

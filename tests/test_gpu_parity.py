@@ -1,0 +1,157 @@
+"""GPU parity of the bf16 path (h3attn_fwd / h3attn_prologue) against the fp64 oracle.
+
+Small cases compare every (token, head) row; the full-size workloads compare
+4096 seeded sampled rows (always including the first and last token of every
+sequence and the first and last audio token).  Everything goes through the C
+ABI via the ctypes binding.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from audio_diffusion_transformer_amd import h3attn as h
+from audio_diffusion_transformer_amd import synth
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+Seq = synth.Seq
+
+# Small cases: several key tiles, ragged tails, empty and audio-only sequences,
+# exact tile multiples, d = 64 and d = 128.
+SMALL = {
+    "tiny": synth.WORKLOADS["tiny"],
+    "ragged_tail_337": synth.Workload("ragged_tail_337", H=3, d=128, seqs=(Seq(3, 10, 11, 7),),
+                                      split=(32, 48, 48), seed=11),
+    "multi_seq_empty_audio_only": synth.Workload(
+        "multi_seq_empty_audio_only", H=2, d=128,
+        seqs=(Seq(2, 8, 9), Seq(0, 1, 1), Seq(1, 4, 5, 70), Seq(0, 1, 1, 33), Seq(1, 1, 1)),
+        split=(32, 48, 48), k_offset_std=0.5, seed=12),
+    "exact_tiles_d64": synth.Workload("exact_tiles_d64", H=4, d=64,
+                                      seqs=(Seq(2, 8, 8), Seq(4, 4, 8, 128)), split=(16, 24, 24),
+                                      seed=13),
+    "long_1500_d64": synth.Workload("long_1500_d64", H=2, d=64, seqs=(Seq(5, 15, 20),),
+                                    split=(16, 24, 24), seed=14),
+    "sharp_700": synth.Workload("sharp_700", H=4, d=128, seqs=(Seq(4, 10, 15, 100),),
+                                split=(32, 48, 48), seed=15, sharp=True),
+}
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_attention_all_rows(torch_dev, name):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, label=name))
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    ref = G.oracle_rows(w, inp, rows)
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.BF16_GATE, name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "multi_seq_empty_audio_only", "sharp_700"])
+def test_prologue_stage_all_rows(torch_dev, name):
+    """bf16 qhat/khat of every (token, head) within one bf16 rounding of the fp64 oracle."""
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    G.announce("prologue %s" % name)
+    qh, kh = h.h3attn_prologue(t["q"], t["k"], t["norm_w"], t["rope"], t["cu"], eps=w.eps)
+    torch_dev.cuda.synchronize()
+    p = oracle.Problem.from_workload(w, inp)
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    for which, got in ((0, qh), (1, kh)):
+        g = G.decode(G.bits(got).reshape(-1, w.d))
+        ref = p.prologue_rows(which, rows, nthreads=G.oracle_threads())
+        err = np.abs(g - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-6
+        assert np.all(err <= bound), "%s %s: worst excess %g" % (
+            name, "qk"[which], float((err - bound).max()))
+
+
+@pytest.mark.parametrize("name", ["video", "joint", "ragged"])
+def test_attention_full_size_sampled_rows(torch_dev, name):
+    w = synth.WORKLOADS[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, label=name))
+    del t
+    rows = synth.sample_rows(w, 4096)
+    ref = G.oracle_rows(w, inp, rows)
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.BF16_GATE, name)
+
+
+def test_sharp_full_video_shape_sampled(torch_dev):
+    """Peaky softmax (score std ~4) at the 58,320-token video shape: outputs are
+    O(0.3-1), so absolute tolerances are meaningful here."""
+    w = synth.WORKLOADS["video"].replace(name="video_sharp", sharp=True, seed=1102)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, label="video_sharp"))
+    rows = synth.sample_rows(w, 2048)
+    ref = G.oracle_rows(w, inp, rows)
+    m = G.metrics(G.gpu_rows(out, rows, w.H), ref)
+    assert m["ref_mean_abs"] > 0.05
+    G.check(m, G.BF16_GATE, "video_sharp")
+
+
+def test_repeat_calls_bit_identical(torch_dev):
+    w = SMALL["ragged_tail_337"].replace(seqs=(Seq(7, 20, 30, 250), Seq(2, 3, 3)))
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    a = G.bits(G.run(w, t, label="determinism-1"))
+    b = G.bits(G.run(w, t, label="determinism-2"))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_fused_qkv_views_and_strided_output(torch_dev):
+    """q, k, v as views of one [N, 3, H, d] buffer and out with a padded token
+    stride give the same bits as contiguous tensors; padding is untouched."""
+    torch = torch_dev
+    w = SMALL["multi_seq_empty_audio_only"]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    ref = G.bits(G.run(w, t, label="contiguous"))
+    qkv = torch.stack([t["q"], t["k"], t["v"]], dim=1).contiguous()        # [N, 3, H, d]
+    big = torch.full((w.N, w.H * w.d + 64), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    out = big[:, : w.H * w.d].view(w.N, w.H, w.d)
+    t2 = dict(t, q=qkv[:, 0], k=qkv[:, 1], v=qkv[:, 2])
+    G.run(w, t2, out=out, label="strided")
+    np.testing.assert_array_equal(G.bits(out.contiguous()), ref)
+    assert bool((big[:, w.H * w.d:] == 7.0).all())
+
+
+def test_stages_equal_single_call_and_side_stream(torch_dev):
+    torch = torch_dev
+    w = SMALL["ragged_tail_337"]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    ref = G.bits(G.run(w, t, label="fused-call"))
+    s = torch.cuda.Stream()
+    ws = h.workspace_for(t["q"], t["cu"])
+    out = torch.empty_like(t["q"])
+    G.announce("stages 1 then 2 on a side stream")
+    with torch.cuda.stream(s):
+        for stage in (1, 2):
+            h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], out=out,
+                         workspace=ws, eps=w.eps, stream=s, stages=stage)
+    s.synchronize()
+    np.testing.assert_array_equal(G.bits(out), ref)
+
+
+def test_empty_input_is_a_no_op(torch_dev):
+    torch = torch_dev
+    buf = torch.zeros((1, 2, 64), dtype=torch.bfloat16, device="cuda:0")
+    nw = torch.ones((2, 2, 64), dtype=torch.float32, device="cuda:0")
+    rope = torch.zeros((1, 32, 2), dtype=torch.float32, device="cuda:0")
+    out = torch.full((1, 2, 64), 3.0, dtype=torch.bfloat16, device="cuda:0")
+    G.announce("empty input")
+    h.h3attn_fwd(buf[:0], buf[:0], buf[:0], nw, rope, np.array([0, 0, 0], np.int32), out=out[:0])
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
