@@ -251,6 +251,7 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
     if (st != H3ATTN_OK) return st;
     if (stages < 1 || stages > 3) return fail(H3ATTN_ERR_INVALID_ARG, "stages must be 1, 2 or 3 (got %d)", stages);
+    if (pl.N == 0) return ok();   // nothing is read or written; pointers may be NULL
     if ((st = check_ptrs(q, k, v, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
     if (!workspace) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
     if (!aligned(workspace, 256)) return fail(H3ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
@@ -301,6 +302,7 @@ h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void 
     Plan pl;
     h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
     if (st != H3ATTN_OK) return st;
+    if (pl.N == 0) return ok();
     if ((st = check_ptrs(q, k, q, norm_w, rope_tables, q_hat)) != H3ATTN_OK) return st;
     if (!k_hat) return fail(H3ATTN_ERR_INVALID_ARG, "k_hat is NULL");
     if (!aligned(k_hat, 16)) return fail(H3ATTN_ERR_INVALID_ARG, "k_hat is not 16-byte aligned");

@@ -91,7 +91,8 @@ size_t h3attn_workspace_size(const h3attn_params *p, const int32_t *cu_seqlens_h
  *   workspace   device, 256-byte aligned, >= h3attn_workspace_size(p, cu, 0) bytes;
  *               its contents on entry do not matter and on exit are unspecified
  *   stream      hipStream_t
- * Sequences of length 0 are allowed and produce nothing.
+ * Sequences of length 0 are allowed and produce nothing; when N = 0 nothing is
+ * read, written or launched and the pointers may be NULL.
  */
 h3attn_status h3attn_fwd(const h3attn_params *p, const void *q, const void *k, const void *v,
                          const float *norm_w, const float *rope_tables,

@@ -68,6 +68,12 @@ def metrics(got: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
 # bf16 path gates: the max/mean absolute bounds of the target, plus relative
 # guards (rel-L2, cosine) that an all-zero or norm-skipping output would fail.
 BF16_GATE = dict(max_abs=2e-2, mean_abs=2e-3, rel_l2=1e-2, cosine=0.9999)
+# Sharp diagnostic inputs (RMSNorm weights ~2, per-token scales): qhat . khat /
+# sqrt(d) reaches ~45 and storing qhat/khat in bf16 (unit roundoff u = 2^-9)
+# perturbs scores by about u * |qhat| |khat| / sqrt(d) ~ 0.02 typical, i.e. ~2%
+# relative on the dominant softmax weights of outputs of size ~0.4.  The gate
+# is three times that budget; BF16_GATE applies to every standard workload.
+SHARP_GATE = dict(max_abs=6e-2, mean_abs=6e-3, rel_l2=1.5e-2, cosine=0.9999)
 # quantised path: mean-abs bound of the target plus relative guards.
 Q8_GATE = dict(mean_abs=2e-2, rel_l2=0.1, cosine=0.995)
 

@@ -52,7 +52,8 @@ def test_attention_all_rows(torch_dev, name):
     out = G.bits(G.run(w, t, label=name))
     rows = np.arange(w.N * w.H, dtype=np.int64)
     ref = G.oracle_rows(w, inp, rows)
-    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.BF16_GATE, name)
+    gate = G.SHARP_GATE if w.sharp else G.BF16_GATE
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), gate, name)
 
 
 @pytest.mark.parametrize("name", ["tiny", "multi_seq_empty_audio_only", "sharp_700"])
@@ -98,7 +99,7 @@ def test_sharp_full_video_shape_sampled(torch_dev):
     ref = G.oracle_rows(w, inp, rows)
     m = G.metrics(G.gpu_rows(out, rows, w.H), ref)
     assert m["ref_mean_abs"] > 0.05
-    G.check(m, G.BF16_GATE, "video_sharp")
+    G.check(m, G.SHARP_GATE, "video_sharp")
 
 
 def test_repeat_calls_bit_identical(torch_dev):
