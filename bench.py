@@ -69,9 +69,13 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
         p.attention_rows(rows, nthreads=threads)
         return time.perf_counter() - t0
 
+    # fixed cost (the keys' prologue) + per-row cost, from two probes
     probe = 2 * threads
-    t_probe = run(probe)
-    nrows = int(max(probe, min(n, probe * seconds / max(t_probe, 1e-3))))
+    t1 = run(probe)
+    t2 = run(2 * probe)
+    per_row = max((t2 - t1) / probe, 1e-6)
+    fixed = max(t1 - per_row * probe, 0.0)
+    nrows = int(max(probe, min(n, (seconds - fixed) / per_row)))
     t = run(nrows)
     return {
         "value": round(nrows * flops_per_row / t / 1e12, 6),
@@ -91,6 +95,9 @@ def main():
     ap.add_argument("--workload", default="joint")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB "
+                         "(reference kernel for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -121,6 +128,16 @@ def main():
     torch.cuda.synchronize()
     print("[bench] inputs ready for %s (N=%d) in %.1f s" % (w.name, w.N, time.time() - t0),
           file=sys.stderr, flush=True)
+
+    if args.calib_copy_mb > 0:
+        nb = args.calib_copy_mb << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: %d bytes read, %d bytes written" % (nb, nb),
+              file=sys.stderr, flush=True)
+        del src, dst
 
     def stage(sid):
         st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp,
