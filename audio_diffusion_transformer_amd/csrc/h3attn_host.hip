@@ -318,13 +318,84 @@ h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void 
     return hip_status(launch_prologue(pa, pl.d, static_cast<hipStream_t>(stream)), "prologue launch");
 }
 
+static h3attn_status q8_common(const h3attn_params *p, const void *q, const void *k, const void *v,
+                               const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                               const void *out, void *workspace, size_t workspace_bytes, Plan &pl, Q8Args &qa)
+{
+    h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
+    if (st != H3ATTN_OK) return st;
+    if (pl.d != 128) return fail(H3ATTN_ERR_UNSUPPORTED, "the quantised path needs head_dim 128 (got %d)", pl.d);
+    if (pl.N == 0) return H3ATTN_OK;
+    if ((st = check_ptrs(q, k, v, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
+    if (!workspace) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(H3ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < pl.bytes_q8)
+        return fail(H3ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes_q8);
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    char *ws = static_cast<char *>(workspace);
+    std::memset(&qa, 0, sizeof qa);
+    qa.q = static_cast<const uint16_t *>(q);
+    qa.k = static_cast<const uint16_t *>(k);
+    qa.v = static_cast<const uint16_t *>(v);
+    qa.q_stride = p->q_stride;
+    qa.k_stride = p->k_stride;
+    qa.v_stride = p->v_stride;
+    qa.norm_w = norm_w;
+    qa.rope = rope_tables;
+    qa.q8 = reinterpret_cast<int8_t *>(ws + pl.q8);
+    qa.k8 = reinterpret_cast<int8_t *>(ws + pl.k8);
+    qa.v8t = reinterpret_cast<uint8_t *>(ws + pl.v8t);
+    qa.qscale = reinterpret_cast<float *>(ws + pl.qscale);
+    qa.kscale = reinterpret_cast<float *>(ws + pl.kscale);
+    qa.ksum = reinterpret_cast<float *>(ws + pl.ksum);
+    qa.vmax = reinterpret_cast<float *>(ws + pl.vmax);
+    qa.kmean = reinterpret_cast<float *>(ws + pl.kmean);
+    qa.vscale = reinterpret_cast<float *>(ws + pl.vscale);
+    qa.H = pl.H;
+    qa.Npad = pl.Npad;
+    qa.eps = p->eps;
+    qa.ntiles = (int32_t)(pl.Npad / kTile);
+    qa.seq = seq_table(pl);
+    return H3ATTN_OK;
+}
+
+h3attn_status h3attn_fwd_q8_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                   const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                                   void *out, void *workspace, size_t workspace_bytes, void *stream, int stages)
+{
+    if (stages < 1 || stages > 3) return fail(H3ATTN_ERR_INVALID_ARG, "stages must be 1, 2 or 3 (got %d)", stages);
+    Plan pl;
+    Q8Args qa;
+    h3attn_status st = q8_common(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, out, workspace,
+                                 workspace_bytes, pl, qa);
+    if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (stages & 1)
+        if ((st = hip_status(launch_q8_prep(qa, pl.d, hs), "quantised prologue launch")) != H3ATTN_OK) return st;
+    if (!(stages & 2)) return ok();
+    Q8AttnArgs aa;
+    std::memset(&aa, 0, sizeof aa);
+    aa.q8 = qa.q8;
+    aa.k8 = qa.k8;
+    aa.v8t = qa.v8t;
+    aa.qscale = qa.qscale;
+    aa.kscale = qa.kscale;
+    aa.vscale = qa.vscale;
+    aa.out = static_cast<uint16_t *>(out);
+    aa.o_stride = p->o_stride;
+    aa.Npad = pl.Npad;
+    aa.H = pl.H;
+    aa.scale_log2 = scale_log2(p);
+    const int64_t items = order_work(pl, aa, aa.seq_idx);
+    return hip_status(launch_attn_q8(aa, pl.d, items, hs), "quantised attention launch");
+}
+
 h3attn_status h3attn_fwd_q8(const h3attn_params *p, const void *q, const void *k, const void *v,
                             const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
                             void *out, void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)p; (void)q; (void)k; (void)v; (void)norm_w; (void)rope_tables; (void)cu_seqlens_host;
-    (void)out; (void)workspace; (void)workspace_bytes; (void)stream;
-    return fail(H3ATTN_ERR_UNSUPPORTED, "quantised path not built yet");
+    return h3attn_fwd_q8_stages(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, out, workspace,
+                                workspace_bytes, stream, 3);
 }
 
 h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -333,10 +404,40 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
                                  int8_t *q8, int8_t *k8, float *q_scale, float *k_scale, float *k_mean,
                                  uint8_t *v8, float *v_scale, void *stream)
 {
-    (void)p; (void)q; (void)k; (void)v; (void)norm_w; (void)rope_tables; (void)cu_seqlens_host;
-    (void)workspace; (void)workspace_bytes; (void)q8; (void)k8; (void)q_scale; (void)k_scale;
-    (void)k_mean; (void)v8; (void)v_scale; (void)stream;
-    return fail(H3ATTN_ERR_UNSUPPORTED, "quantised path not built yet");
+    Plan pl;
+    Q8Args qa;
+    h3attn_status st = q8_common(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, q8, workspace,
+                                 workspace_bytes, pl, qa);
+    if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
+    const void *outs[6] = {k8, q_scale, k_scale, k_mean, v8, v_scale};
+    const char *names[6] = {"k8", "q_scale", "k_scale", "k_mean", "v8", "v_scale"};
+    for (int i = 0; i < 6; ++i)
+        if (!outs[i]) return fail(H3ATTN_ERR_INVALID_ARG, "%s is NULL", names[i]);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = hip_status(launch_q8_prep(qa, pl.d, hs), "quantised prologue launch")) != H3ATTN_OK) return st;
+    Q8ExportArgs ea;
+    std::memset(&ea, 0, sizeof ea);
+    ea.q8 = qa.q8;
+    ea.k8 = qa.k8;
+    ea.v8t = qa.v8t;
+    ea.qscale = qa.qscale;
+    ea.kscale = qa.kscale;
+    ea.q8_out = q8;
+    ea.k8_out = k8;
+    ea.v8_out = v8;
+    ea.qscale_out = q_scale;
+    ea.kscale_out = k_scale;
+    ea.H = pl.H;
+    ea.d = pl.d;
+    ea.Npad = pl.Npad;
+    ea.ntiles = qa.ntiles;
+    for (int s = 0; s < pl.S; ++s) ea.nblocks += (pl.cu[s + 1] - pl.cu[s] + kTile - 1) / kTile;
+    ea.seq = qa.seq;
+    if ((st = hip_status(launch_q8_export(ea, hs), "quantised export launch")) != H3ATTN_OK) return st;
+    const size_t sb = (size_t)pl.S * pl.H * pl.d * sizeof(float);
+    if ((st = hip_status(hipMemcpyAsync(k_mean, qa.kmean, sb, hipMemcpyDeviceToDevice, hs), "k_mean copy")) != H3ATTN_OK)
+        return st;
+    return hip_status(hipMemcpyAsync(v_scale, qa.vscale, sb, hipMemcpyDeviceToDevice, hs), "v_scale copy");
 }
 
 h3attn_status h3attn_rope_fill_video(int32_t T, int32_t Hg, int32_t Wg, int32_t dt, int32_t dh, int32_t dw,

@@ -18,16 +18,12 @@
 // the same XCD (dispatch is round-robin over the 8 XCDs): the RoPE table rows
 // of the tile are then fetched into that XCD's L2 once.
 #include "h3_internal.h"
+#include "norm_rope.h"
 
 namespace h3 {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
@@ -56,68 +52,46 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
     const int gt = 8 * ((b >> 3) / H) + (b & 7);    // padded tile index
     const int h = (b >> 3) % H;
     if (gt >= a.ntiles) return;
-    int s = 0;
-    while (s + 1 < a.seq.S && gt >= a.seq.off[s + 1] / kTile) ++s;
-    const int j = gt - a.seq.off[s] / kTile;
-    const int n_s = a.seq.cu[s + 1] - a.seq.cu[s];
-    const int valid = min(max(n_s - kTile * j, 0), kTile);
+    int s, j, valid;
+    tile_seq(a.seq.cu, a.seq.off, a.seq.S, gt, s, j, valid);
     if (a.natural && valid == 0) return;
 
     const int t = threadIdx.x;
     const int c = t % LPR;
     const int rr = t / LPR;
     const float inv_d = 1.0f / (float)D;
+    float wq[8], wk[8];
+    load_w8(a.norm_w, h, D, c, wq);
+    load_w8(a.norm_w, H + h, D, c, wk);
 
 #pragma unroll
     for (int pass = 0; pass < kTile / RPP; ++pass) {
         const int r = pass * RPP + rr;
         const bool ok = r < valid;
         const int64_t tok = (int64_t)a.seq.cu[s] + kTile * j + r;
-        f32x4 cs0 = {1.f, 0.f, 1.f, 0.f}, cs1 = {1.f, 0.f, 1.f, 0.f};
-        if (ok) {
-            const f32x4 *rp = reinterpret_cast<const f32x4 *>(a.rope + tok * D + 8 * c);
-            cs0 = rp[0];
-            cs1 = rp[1];
-        }
+        float cs[8] = {1.f, 0.f, 1.f, 0.f, 1.f, 0.f, 1.f, 0.f};
+        if (ok) load_cs8(a.rope, tok, D, c, cs);
         const int64_t orow = a.natural ? tok : (int64_t)a.seq.off[s] + kTile * j + r;
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             const uint16_t *src = which ? a.k + tok * a.k_stride : a.q + tok * a.q_stride;
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (ok) raw = *reinterpret_cast<const u32x4 *>(src + h * D + 8 * c);
-            float x[8];
+            u32x4_t raw = {0u, 0u, 0u, 0u};
+            if (ok) raw = *reinterpret_cast<const u32x4_t *>(src + h * D + 8 * c);
+            float x[8], y[8];
+            unpack8(raw, x);
+            norm_rope8<LPR>(x, which ? wk : wq, cs, inv_d, a.eps, y);
+            u32x4_t o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = bf_lo(raw[i]);
-                x[2 * i + 1] = bf_hi(raw[i]);
-            }
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
-#pragma unroll
-            for (int msk = LPR / 2; msk >= 1; msk >>= 1) ss += __shfl_xor(ss, msk, LPR);
-            const float rs = rsqrtf(fmaf(ss, inv_d, a.eps));
-            const f32x4 *wp = reinterpret_cast<const f32x4 *>(a.norm_w + (which * H + h) * D + 8 * c);
-            const f32x4 w0 = wp[0], w1 = wp[1];
-            const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-            const float cs[8] = {cs0[0], cs0[1], cs0[2], cs0[3], cs1[0], cs1[1], cs1[2], cs1[3]};
-            u32x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float y0 = x[2 * i] * rs * wv[2 * i];
-                const float y1 = x[2 * i + 1] * rs * wv[2 * i + 1];
-                const float co = cs[2 * i], si = cs[2 * i + 1];
-                o[i] = pack_bf16(y0 * co - y1 * si, y0 * si + y1 * co);
-            }
-            if (!ok) o = (u32x4){0u, 0u, 0u, 0u};
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf16(y[2 * i], y[2 * i + 1]);
+            if (!ok) o = (u32x4_t){0u, 0u, 0u, 0u};
             if (ok || !a.natural) {
                 uint16_t *dst = (which ? a.khat : a.qhat) + h * a.out_hstride + orow * a.out_tstride + 8 * c;
-                *reinterpret_cast<u32x4 *>(dst) = o;
+                *reinterpret_cast<u32x4_t *>(dst) = o;
             }
         }
         if (!a.natural) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (ok) raw = *reinterpret_cast<const u32x4 *>(a.v + tok * a.v_stride + h * D + 8 * c);
+            u32x4_t raw = {0u, 0u, 0u, 0u};
+            if (ok) raw = *reinterpret_cast<const u32x4_t *>(a.v + tok * a.v_stride + h * D + 8 * c);
             const int p = vt_pos(r);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -132,8 +106,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
 #pragma unroll
     for (int g = t; g < D * 8; g += 256) {
         const int row = g >> 3, cc = g & 7;
-        *reinterpret_cast<u32x4 *>(vt + row * kTile + 8 * cc) =
-            *reinterpret_cast<const u32x4 *>(&vl[row][8 * cc]);
+        *reinterpret_cast<u32x4_t *>(vt + row * kTile + 8 * cc) =
+            *reinterpret_cast<const u32x4_t *>(&vl[row][8 * cc]);
     }
 }
 

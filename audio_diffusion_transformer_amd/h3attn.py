@@ -25,7 +25,7 @@ H3ATTN_ERR_HIP = 5
 H3ATTN_MAX_SEQS = 64
 
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
-            "h3attn_prologue",
+            "h3attn_fwd_q8_stages", "h3attn_prologue",
             "h3attn_q8_prologue", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
@@ -61,8 +61,9 @@ def lib():
         for name in ("h3attn_fwd", "h3attn_fwd_q8"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = fwd_args
-        L.h3attn_fwd_stages.restype = C.c_int
-        L.h3attn_fwd_stages.argtypes = fwd_args + [C.c_int]
+        for name in ("h3attn_fwd_stages", "h3attn_fwd_q8_stages"):
+            getattr(L, name).restype = C.c_int
+            getattr(L, name).argtypes = fwd_args + [C.c_int]
         L.h3attn_prologue.restype = C.c_int
         L.h3attn_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, P(C.c_int32), vp, vp, vp]
         L.h3attn_q8_prologue.restype = C.c_int

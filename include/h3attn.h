@@ -130,6 +130,13 @@ h3attn_status h3attn_fwd_q8(const h3attn_params *p, const void *q, const void *k
                             const int32_t *cu_seqlens_host, void *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* The two stages of h3attn_fwd_q8 (1: quantised prologue, 2: attention, 3: both);
+ * same contract as h3attn_fwd_stages. */
+h3attn_status h3attn_fwd_q8_stages(const h3attn_params *p, const void *q, const void *k,
+                                   const void *v, const float *norm_w, const float *rope_tables,
+                                   const int32_t *cu_seqlens_host, void *out, void *workspace,
+                                   size_t workspace_bytes, void *stream, int stages);
+
 /*
  * Diagnostic: the fused RMSNorm + RoPE prologue alone, written as bf16 qhat and
  * khat in the natural layout (token stride H*d), using the same kernel code as

@@ -40,7 +40,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), "libh3attn.so does not export %s" % n
-    assert set(names) <= set(h.EXPORTED) | {"h3attn_fwd_q8_stages"}
+    assert set(names) == set(h.EXPORTED)
     assert h.version() == 1
 
 
@@ -199,3 +199,14 @@ def test_synth_is_seeded_and_bf16_rounding_is_nearest_even():
     toks = set((rows // H).tolist())
     for t in (0, 18143, 18144, 18144 + 45000, 63393, 63394, 70593):
         assert t in toks
+
+
+def test_quantised_path_argument_errors():
+    small = _params(num_heads=2, head_dim=64, q_stride=128, k_stride=128, v_stride=128, o_stride=128)
+    assert _call(small, quantized=True) == h.H3ATTN_ERR_UNSUPPORTED
+    assert "head_dim 128" in h.last_error()
+    need = h.h3attn_workspace_size(_params(), [0, 1000], quantized=True)
+    assert need < h.h3attn_workspace_size(_params(), [0, 1000])
+    assert _call(ws_bytes=need - 1, quantized=True) == h.H3ATTN_ERR_WORKSPACE
+    assert _call(quantized=True, stages=5) == h.H3ATTN_ERR_INVALID_ARG
+    assert _call(ptrs={"v": 0}, quantized=True) == h.H3ATTN_ERR_INVALID_ARG
