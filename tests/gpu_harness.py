@@ -74,8 +74,10 @@ BF16_GATE = dict(max_abs=2e-2, mean_abs=2e-3, rel_l2=1e-2, cosine=0.9999)
 # relative on the dominant softmax weights of outputs of size ~0.4.  The gate
 # is three times that budget; BF16_GATE applies to every standard workload.
 SHARP_GATE = dict(max_abs=6e-2, mean_abs=6e-3, rel_l2=1.5e-2, cosine=0.9999)
-# quantised path: mean-abs bound of the target plus relative guards.
-Q8_GATE = dict(mean_abs=2e-2, rel_l2=0.1, cosine=0.995)
+# Quantised path: mean-abs bound of the target plus relative guards set at the
+# measured error (rel-L2 0.034-0.039, cosine >= 0.9992 on every case) plus margin;
+# an all-zero output (rel-L2 1) or a dropped V scale would fail them.
+Q8_GATE = dict(mean_abs=2e-2, rel_l2=0.06, cosine=0.998)
 
 
 def check(m: Dict[str, float], gate: Dict[str, float], label: str):
