@@ -29,11 +29,14 @@
 // the in-tile key index swapped so those 8 keys are one contiguous 16-byte LDS
 // read.
 //
-// Pipelining.  K and V^T tiles of 64 keys are double-buffered in LDS; the
-// global loads of tile j+1 are issued before tile j is computed and written to
-// the other buffer after it, with one barrier per tile.  LDS rows are XOR
-// swizzled at 16-byte granularity so the 16-byte fragment reads of 8
-// consecutive lanes hit distinct banks.
+// Pipelining.  K and V^T tiles of 64 keys are double-buffered in LDS and
+// filled straight from global memory by global_load_lds_dwordx4 (no staging
+// registers).  K runs one tile ahead of V: iteration j issues the scores of
+// tile j+1 (matrix cores) next to the softmax of tile j (vector ALUs), which
+// do not depend on each other, then the P.V product of tile j; the loads of K
+// tile j+2 and V tile j+1 are in flight meanwhile, and one barrier per tile
+// hands the buffers over.  LDS rows are XOR swizzled at 16-byte granularity so
+// the 16-byte fragment reads of each group of 16 lanes hit distinct banks.
 //
 // Online softmax in base 2: p = 2^(s*c - m*c), c = scale*log2(e).  The running
 // max m is only raised when a tile's max exceeds it by more than 8 (in log2
@@ -52,6 +55,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyRescale = 8.0f;
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt left at their maximum.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
@@ -59,13 +64,63 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// 16-byte chunk swizzle of an LDS row: rows of 256 bytes (16 chunks) XOR the
+// chunk index with row % 16, rows of 128 bytes (8 chunks) with (row / 2) % 8,
+// so that 16 consecutive rows read at one logical chunk cover all 64 banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row)
+{
+    return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// Direct-to-LDS tile fill: a tile of ROWS x CPR 16-byte chunks lies
+// contiguously in global memory; every wave instruction writes 1 KB of LDS,
+// lane L the 16 bytes at offset 16 L, so lane L fetches the global chunk the
+// swizzle places there.  The per-lane global offsets do not depend on the tile
+// and are computed once.
+template <int ROWS, int CPR>
+struct TileFill {
+    static constexpr int KB = ROWS * CPR / 64;   // 1 KB pieces in the tile
+    static constexpr int PER_WAVE = KB / 4;
+    static constexpr int RPK = 64 / CPR;         // rows per piece
+    uint32_t goff[PER_WAVE];                     // byte offsets in the global tile
+    __device__ __forceinline__ void init(int wave, int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int row = (wave * PER_WAVE + i) * RPK + lane / CPR;
+            goff[i] = (uint32_t)(row * CPR + ((lane % CPR) ^ swz<CPR>(row))) * 16u;
+        }
+    }
+    __device__ __forceinline__ void load(const uint16_t *g, uint16_t *lds, int wave) const
+    {
+        const char *gb = reinterpret_cast<const char *>(g);
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i)
+            __builtin_amdgcn_global_load_lds(gb + goff[i],
+                                             (__attribute__((address_space(3))) void *)(lds + (wave * PER_WAVE + i) * 512),
+                                             16, 0, 0);
+    }
+};
+
+// max / sum of a lane's value and the value of lane l ^ 32 (same query row).
+__device__ __forceinline__ float row_max2(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_sum2(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 {
     constexpr int KSTEPS = D / 16;          // k-steps of the S^T product
     constexpr int DB = D / 32;              // 32-channel output blocks
-    constexpr int KCH = D / 8;              // 16-byte chunks per K row
-    constexpr int PER = kTile * D / 8 / 256; // 16-byte chunks per lane per tile (each of K, V)
+    constexpr int KCPR = D / 8;             // 16-byte chunks per K row
     __shared__ __attribute__((aligned(16))) uint16_t lk[2][kTile * D];
     __shared__ __attribute__((aligned(16))) uint16_t lv[2][D * kTile];
 
@@ -95,25 +150,25 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     const uint16_t *kbase = a.khat + ((int64_t)head * a.Npad + off) * D;
     const uint16_t *vbase = a.vt + ((int64_t)head * (a.Npad / kTile) + off / kTile) * (D * kTile);
     const int nt = (n + kTile - 1) / kTile;
+    TileFill<kTile, KCPR> kfill;
+    TileFill<D, 8> vfill;
+    kfill.init(wave, lane);
+    vfill.init(wave, lane);
+    auto load_k = [&](int j, int buf) { kfill.load(kbase + (int64_t)j * kTile * D, lk[buf], wave); };
+    auto load_v = [&](int j, int buf) { vfill.load(vbase + (int64_t)j * D * kTile, lv[buf], wave); };
 
-    u32x4 stk[PER], stv[PER];
-    auto gload = [&](int j) {
-        const u32x4 *ks = reinterpret_cast<const u32x4 *>(kbase + (int64_t)j * kTile * D);
-        const u32x4 *vs = reinterpret_cast<const u32x4 *>(vbase + (int64_t)j * D * kTile);
+    // S^T of one 64-key tile from the K buffer `buf`.
+    auto scores = [&](int buf, f32x16 &s0, f32x16 &s1) {
+        const uint16_t *kl = lk[buf];
+        s0 = (f32x16){};
+        s1 = (f32x16){};
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            stk[i] = ks[tid + 256 * i];
-            stv[i] = vs[tid + 256 * i];
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int g = tid + 256 * i;
-            const int kr = g / KCH, kc = g % KCH;
-            *reinterpret_cast<u32x4 *>(&lk[buf][kr * D + 8 * (kc ^ (kr & (KCH - 1)))]) = stk[i];
-            const int vr = g >> 3, vc = g & 7;
-            *reinterpret_cast<u32x4 *>(&lv[buf][vr * kTile + 8 * (vc ^ (vr & 7))]) = stv[i];
+        for (int st = 0; st < KSTEPS; ++st) {
+            const int ch = (2 * st + hh) ^ swz<KCPR>(m);
+            const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(kl + m * D + 8 * ch);
+            const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(kl + (32 + m) * D + 8 * ch);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[st], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[st], s1, 0, 0, 0);
         }
     };
 
@@ -122,28 +177,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     for (int i = 0; i < DB; ++i) o[i] = (f32x16){};
     float m_used = -INFINITY, l = 0.f;
     const float c = a.scale_log2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int j = 0; j < nt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nt) gload(j + 1);
-
-        // ---- S^T = K . Q^T for 64 keys (two 32-key blocks)
-        f32x16 s0 = (f32x16){}, s1 = (f32x16){};
-        const uint16_t *kl = lk[buf];
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-            const int ch = (2 * st + hh) ^ (m & (KCH - 1));
-            const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(kl + m * D + 8 * ch);
-            const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(kl + (32 + m) * D + 8 * ch);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[st], s1, 0, 0, 0);
-        }
-
-        // ---- mask keys past the end of the sequence (last tile only)
+    // softmax of tile j (scores s0, s1) and O^T += V^T P^T from V buffer `buf`
+    auto softmax_pv = [&](int j, int buf, f32x16 &s0, f32x16 &s1) {
         const int valid = n - j * kTile;
         if (valid < kTile) {
 #pragma unroll
@@ -153,12 +190,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
                 if (32 + key >= valid) s1[r] = -INFINITY;
             }
         }
-
-        // ---- online softmax (row = this lane's query)
         float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = row_max2(mx);
         const bool need = (mx - m_used) * c > kLazyRescale;
         if (__any(need)) {
             const float mn = need ? mx : m_used;
@@ -177,14 +212,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
             p1[r / 2] = pack2(__builtin_amdgcn_exp2f(fmaf(s1[r], c, -mc)),
                               __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c, -mc)));
         }
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p0[i]), ones, l, false);
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p1[i]), ones, l, false);
         }
-
-        // ---- O^T += V^T . P^T
         const uint16_t *vl = lv[buf];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -193,22 +225,46 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
                 const uint32_t *pp = kb ? p1 : p0;
                 const u32x4 pw = {pp[4 * cc], pp[4 * cc + 1], pp[4 * cc + 2], pp[4 * cc + 3]};
                 const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-                const int ch = (4 * kb + 2 * cc + hh) ^ (m & 7);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vl + (32 * db + m) * kTile + 8 * ch);
+                    const int row = 32 * db + m;
+                    const int ch = (4 * kb + 2 * cc + hh) ^ swz<8>(row);
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vl + row * kTile + 8 * ch);
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
                 }
             }
         }
+    };
 
-        if (j + 1 < nt) lstore(buf ^ 1);
+    // ---- prologue: K0, V0 (and K1) resident, scores of tile 0
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(0, 0);
+    load_v(0, 0);
+    if (nt > 1) load_k(1, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    f32x16 sa0, sa1, sb0, sb1;
+    scores(0, sa0, sa1);
+    __syncthreads();
+
+    // iteration j: loads K[j+2] -> lk[j&1], V[j+1] -> lv[(j+1)&1]; scores of
+    // tile j+1 from lk[(j+1)&1]; softmax + P.V of tile j from lv[j&1].
+    auto step = [&](int j, f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1) {
+        if (j + 2 < nt) load_k(j + 2, j & 1);
+        if (j + 1 < nt) load_v(j + 1, (j + 1) & 1);
+        if (j + 1 < nt) scores((j + 1) & 1, n0, n1);
+        softmax_pv(j, j & 1, c0, c1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
+    };
+    for (int j = 0; j < nt; ++j) {
+        step(j, sa0, sa1, sb0, sb1);
+        sa0 = sb0;
+        sa1 = sb1;
     }
 
     // ---- epilogue: o = O / l, bf16, rows of this sequence only
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / row_sum2(l);
     const int qrow = q0 + m;
     if (qrow < n) {
         uint16_t *op = a.out + ((int64_t)a.seq_cu[si] + qrow) * a.o_stride + (int64_t)head * D;
