@@ -121,8 +121,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     constexpr int KSTEPS = D / 16;          // k-steps of the S^T product
     constexpr int DB = D / 32;              // 32-channel output blocks
     constexpr int KCPR = D / 8;             // 16-byte chunks per K row
-    __shared__ __attribute__((aligned(16))) uint16_t lk[2][kTile * D];
-    __shared__ __attribute__((aligned(16))) uint16_t lv[2][D * kTile];
+    // Separate arrays per buffer: the compiler can then prove that a
+    // direct-to-LDS fill of one buffer does not alias fragment reads of the
+    // other, and need not wait for the fill before reading.
+    __shared__ __attribute__((aligned(16))) uint16_t lk0[kTile * D], lk1[kTile * D];
+    __shared__ __attribute__((aligned(16))) uint16_t lv0[D * kTile], lv1[D * kTile];
 
     // ---- work item: (sequence, head, 128-row query block)
     const int b = blockIdx.x;
@@ -154,12 +157,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     TileFill<D, 8> vfill;
     kfill.init(wave, lane);
     vfill.init(wave, lane);
-    auto load_k = [&](int j, int buf) { kfill.load(kbase + (int64_t)j * kTile * D, lk[buf], wave); };
-    auto load_v = [&](int j, int buf) { vfill.load(vbase + (int64_t)j * D * kTile, lv[buf], wave); };
+    auto kbuf = [&](int buf) { return buf ? lk1 : lk0; };
+    auto vbuf = [&](int buf) { return buf ? lv1 : lv0; };
+    auto load_k = [&](int j, uint16_t *dst) { kfill.load(kbase + (int64_t)j * kTile * D, dst, wave); };
+    auto load_v = [&](int j, uint16_t *dst) { vfill.load(vbase + (int64_t)j * D * kTile, dst, wave); };
 
     // S^T of one 64-key tile from the K buffer `buf`.
-    auto scores = [&](int buf, f32x16 &s0, f32x16 &s1) {
-        const uint16_t *kl = lk[buf];
+    auto scores = [&](const uint16_t *kl, f32x16 &s0, f32x16 &s1) {
         s0 = (f32x16){};
         s1 = (f32x16){};
 #pragma unroll
@@ -179,10 +183,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     const float c = a.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // softmax of tile j (scores s0, s1) and O^T += V^T P^T from V buffer `buf`
-    auto softmax_pv = [&](int j, int buf, f32x16 &s0, f32x16 &s1) {
+    // Row max of tile j's scores (masking keys past the sequence end on the
+    // last tile) and the lazy running-max update of O and l.
+    auto row_max_update = [&](int j, f32x16 &s0, f32x16 &s1, bool mask) {
         const int valid = n - j * kTile;
-        if (valid < kTile) {
+        if (mask && valid < kTile) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -203,6 +208,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 #pragma unroll
             for (int i = 0; i < DB; ++i) o[i] *= alpha;
         }
+    };
+    // p = 2^(s c - m c) in bf16, l += p, O^T += V^T P^T from V buffer `buf`.
+    auto exp_pv = [&](const uint16_t *vl, const f32x16 &s0, const f32x16 &s1) {
         const float mc = m_used * c;
         uint32_t p0[8], p1[8];
 #pragma unroll
@@ -217,7 +225,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p0[i]), ones, l, false);
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p1[i]), ones, l, false);
         }
-        const uint16_t *vl = lv[buf];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -236,32 +243,105 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
         }
     };
 
+    // Hand-scheduled steady-state body: 2*KSTEPS score MFMAs of tile j+1 then
+    // 4*DB P.V MFMAs of tile j, one per chunk; chunk i also issues the LDS
+    // fragment read of MFMA i+PD, and each score chunk carries the softmax of
+    // two elements of tile j (fma, exp2, bf16 pack, row-sum dot2).  Scheduling
+    // barriers keep the chunks in this order, so every fragment read has PD
+    // MFMAs to land and the exps run beside the matrix cores.
+    constexpr int PD = 3;
+    constexpr int NQK = 2 * KSTEPS, NM = 2 * KSTEPS + 4 * DB;
+    auto frag = [&](int i, const uint16_t *kl, const uint16_t *vl) -> bf16x8 {
+        if (i < NQK) {
+            const int st = i >> 1, blk = i & 1;
+            const int ch = (2 * st + hh) ^ swz<KCPR>(m);
+            return *reinterpret_cast<const bf16x8 *>(kl + (32 * blk + m) * D + 8 * ch);
+        }
+        const int k = i - NQK, kb = k / (2 * DB), cc = (k / DB) & 1, db = k % DB;
+        const int row = 32 * db + m;
+        const int ch = (4 * kb + 2 * cc + hh) ^ swz<8>(row);
+        return *reinterpret_cast<const bf16x8 *>(vl + row * kTile + 8 * ch);
+    };
+    auto body = [&](const uint16_t *kl, const uint16_t *vl, const f32x16 &c0, const f32x16 &c1,
+                    f32x16 &n0, f32x16 &n1) {
+        const float mc = m_used * c;
+        bf16x8 fa[NM];
+        uint32_t pw[16];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) fa[i] = frag(i, kl, vl);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            if (i + PD < NM) fa[i + PD] = frag(i + PD, kl, vl);
+            if (i < NQK) {
+                const int st = i >> 1, blk = i & 1;
+                if (blk == 0)
+                    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n0 : (f32x16){}, 0, 0, 0);
+                else
+                    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n1 : (f32x16){}, 0, 0, 0);
+                constexpr int PIECES = 16 / NQK;        // element pairs of tile j per score chunk
+#pragma unroll
+                for (int q = 0; q < PIECES; ++q) {
+                    const int pi = i * PIECES + q;
+                    const int e = 2 * pi, sb = e >> 4, r = e & 15;
+                    const f32x16 &sc = sb ? c1 : c0;
+                    const uint32_t w = pack2(__builtin_amdgcn_exp2f(fmaf(sc[r], c, -mc)),
+                                             __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c, -mc)));
+                    pw[pi] = w;
+                    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l, false);
+                }
+            } else {
+                const int k = i - NQK, kb = k / (2 * DB), cc = (k / DB) & 1, db = k % DB;
+                const u32x4 q4 = {pw[8 * kb + 4 * cc], pw[8 * kb + 4 * cc + 1], pw[8 * kb + 4 * cc + 2],
+                                  pw[8 * kb + 4 * cc + 3]};
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], __builtin_bit_cast(bf16x8, q4), o[db], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     // ---- prologue: K0, V0 (and K1) resident, scores of tile 0
     __builtin_amdgcn_sched_barrier(0);
-    load_k(0, 0);
-    load_v(0, 0);
-    if (nt > 1) load_k(1, 1);
+    load_k(0, lk0);
+    load_v(0, lv0);
+    if (nt > 1) load_k(1, lk1);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     f32x16 sa0, sa1, sb0, sb1;
-    scores(0, sa0, sa1);
+    scores(lk0, sa0, sa1);
     __syncthreads();
 
-    // iteration j: loads K[j+2] -> lk[j&1], V[j+1] -> lv[(j+1)&1]; scores of
-    // tile j+1 from lk[(j+1)&1]; softmax + P.V of tile j from lv[j&1].
-    auto step = [&](int j, f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1) {
-        if (j + 2 < nt) load_k(j + 2, j & 1);
-        if (j + 1 < nt) load_v(j + 1, (j + 1) & 1);
-        if (j + 1 < nt) scores((j + 1) & 1, n0, n1);
-        softmax_pv(j, j & 1, c0, c1);
+    // Iteration j: fills K[j+2] -> lk[j&1] and V[j+1] -> lv[(j+1)&1]; scores
+    // of tile j+1 from lk[(j+1)&1] beside the softmax of tile j; P.V of tile j
+    // from lv[j&1]; then wait for the fills and one barrier.  The steady state
+    // runs two iterations per trip with the buffers named at compile time.
+    int j = 0;
+    for (; j + 3 < nt; j += 2) {
+        load_k(j + 2, lk0);
+        load_v(j + 1, lv1);
+        row_max_update(j, sa0, sa1, false);
+        body(lk1, lv0, sa0, sa1, sb0, sb1);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-    };
-    for (int j = 0; j < nt; ++j) {
-        step(j, sa0, sa1, sb0, sb1);
+        load_k(j + 3, lk1);
+        load_v(j + 2, lv0);
+        row_max_update(j + 1, sb0, sb1, false);
+        body(lk0, lv1, sb0, sb1, sa0, sa1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+    }
+    for (; j + 1 < nt; ++j) {
+        if (j + 2 < nt) load_k(j + 2, kbuf(j & 1));
+        load_v(j + 1, vbuf((j + 1) & 1));
+        row_max_update(j, sa0, sa1, false);
+        scores(kbuf((j + 1) & 1), sb0, sb1);
+        exp_pv(vbuf(j & 1), sa0, sa1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
         sa0 = sb0;
         sa1 = sb1;
     }
+    row_max_update(j, sa0, sa1, true);
+    exp_pv(vbuf(j & 1), sa0, sa1);
 
     // ---- epilogue: o = O / l, bf16, rows of this sequence only
     const float inv = 1.0f / row_sum2(l);
