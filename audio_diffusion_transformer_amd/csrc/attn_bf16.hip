@@ -38,11 +38,14 @@
 // hands the buffers over.  LDS rows are XOR swizzled at 16-byte granularity so
 // the 16-byte fragment reads of each group of 16 lanes hit distinct banks.
 //
-// Online softmax in base 2: p = 2^(s*c - m*c), c = scale*log2(e).  The running
-// max m is only raised when a tile's max exceeds it by more than 8 (in log2
-// units), so O and l are rescaled rarely; p then stays below 2^8, well inside
-// bf16 and fp32 range.  P is rounded to bf16 for the P.V product and the row
-// sum l adds exactly those rounded values.
+// Online softmax in base 2.  The prologue stores qhat * scale * log2(e), and
+// each score MFMA chain starts from -m instead of 0, where m is the running
+// row maximum (log2 units): the matrix cores deliver x = s*scale*log2(e) - m
+// directly and p = 2^x needs no further VALU work.  m is raised only when a
+// tile's maximum exceeds it by more than 8, so O and l are rescaled (and that
+// tile's x shifted) rarely; p stays below 2^8, well inside bf16 and fp32
+// range.  P is rounded to bf16 for the P.V product and the row sum l adds
+// exactly those rounded values.
 #include "h3_internal.h"
 
 namespace h3 {
@@ -115,6 +118,20 @@ __device__ __forceinline__ float row_sum2(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Row maximum of the 32 scores a lane holds (16 of each 32-key block).
+__device__ __forceinline__ float lane_max32(const f32x16 &s0, const f32x16 &s1)
+{
+    float a = max3f(s0[0], s0[1], s0[2]), b = max3f(s1[0], s1[1], s1[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+        a = max3f(a, s0[r], s0[r + 1]);
+        b = max3f(b, s1[r], s1[r + 1]);
+    }
+    return max3f(a, b, fmaxf(s0[15], s1[15]));
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 {
@@ -138,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     const int off = a.seq_off[si];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, hh = lane >> 5;
     const int q0 = qb * kBlockM + wave * 32;
 
@@ -162,10 +179,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     auto load_k = [&](int j, uint16_t *dst) { kfill.load(kbase + (int64_t)j * kTile * D, dst, wave); };
     auto load_v = [&](int j, uint16_t *dst) { vfill.load(vbase + (int64_t)j * D * kTile, dst, wave); };
 
-    // S^T of one 64-key tile from the K buffer `buf`.
+    f32x16 o[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] = (f32x16){};
+    float m_run = 0.f, l = 0.f;         // running max (log2 units), row sum
+    bool first = true;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    // x^T = K . Q'^T - m_run of one 64-key tile from K buffer kl.
     auto scores = [&](const uint16_t *kl, f32x16 &s0, f32x16 &s1) {
-        s0 = (f32x16){};
-        s1 = (f32x16){};
+        const f32x16 init = -m_run;
+        s0 = init;
+        s1 = init;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
             const int ch = (2 * st + hh) ^ swz<KCPR>(m);
@@ -176,15 +201,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
         }
     };
 
-    f32x16 o[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] = (f32x16){};
-    float m_used = -INFINITY, l = 0.f;
-    const float c = a.scale_log2;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-    // Row max of tile j's scores (masking keys past the sequence end on the
-    // last tile) and the lazy running-max update of O and l.
+    // Tile j's row max (masking keys past the sequence end on the last tile);
+    // raise m_run when the tile exceeds it by more than kLazyRescale (always on
+    // the first tile), rescaling O and l and shifting the tile's x.
     auto row_max_update = [&](int j, f32x16 &s0, f32x16 &s1, bool mask) {
         const int valid = n - j * kTile;
         if (mask && valid < kTile) {
@@ -195,30 +214,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
                 if (32 + key >= valid) s1[r] = -INFINITY;
             }
         }
-        float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        mx = row_max2(mx);
-        const bool need = (mx - m_used) * c > kLazyRescale;
+        const float mx = row_max2(lane_max32(s0, s1));
+        const bool need = first || mx > kLazyRescale;
         if (__any(need)) {
-            const float mn = need ? mx : m_used;
-            const float alpha = __builtin_amdgcn_exp2f((m_used - mn) * c);
-            m_used = mn;
-            l *= alpha;
+            const float delta = need ? mx : 0.f;
+            if (!first) {
+                const float alpha = __builtin_amdgcn_exp2f(-delta);
+                l *= alpha;
 #pragma unroll
-            for (int i = 0; i < DB; ++i) o[i] *= alpha;
+                for (int i = 0; i < DB; ++i) o[i] *= alpha;
+            }
+            m_run += delta;
+            s0 -= delta;
+            s1 -= delta;
+            first = false;
         }
     };
-    // p = 2^(s c - m c) in bf16, l += p, O^T += V^T P^T from V buffer `buf`.
+
+    // p = 2^x in bf16, l += p, O^T += V^T P^T from V buffer vl (unscheduled form).
     auto exp_pv = [&](const uint16_t *vl, const f32x16 &s0, const f32x16 &s1) {
-        const float mc = m_used * c;
         uint32_t p0[8], p1[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-            p0[r / 2] = pack2(__builtin_amdgcn_exp2f(fmaf(s0[r], c, -mc)),
-                              __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c, -mc)));
-            p1[r / 2] = pack2(__builtin_amdgcn_exp2f(fmaf(s1[r], c, -mc)),
-                              __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c, -mc)));
+            p0[r / 2] = pack2(__builtin_amdgcn_exp2f(s0[r]), __builtin_amdgcn_exp2f(s0[r + 1]));
+            p1[r / 2] = pack2(__builtin_amdgcn_exp2f(s1[r]), __builtin_amdgcn_exp2f(s1[r + 1]));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -246,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     // Hand-scheduled steady-state body: 2*KSTEPS score MFMAs of tile j+1 then
     // 4*DB P.V MFMAs of tile j, one per chunk; chunk i also issues the LDS
     // fragment read of MFMA i+PD, and each score chunk carries the softmax of
-    // two elements of tile j (fma, exp2, bf16 pack, row-sum dot2).  Scheduling
+    // element pairs of tile j (exp2, bf16 pack, row-sum dot2).  Scheduling
     // barriers keep the chunks in this order, so every fragment read has PD
     // MFMAs to land and the exps run beside the matrix cores.
     constexpr int PD = 3;
@@ -264,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     };
     auto body = [&](const uint16_t *kl, const uint16_t *vl, const f32x16 &c0, const f32x16 &c1,
                     f32x16 &n0, f32x16 &n1) {
-        const float mc = m_used * c;
+        const f32x16 init = -m_run;
         bf16x8 fa[NM];
         uint32_t pw[16];
 #pragma unroll
@@ -275,17 +294,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
             if (i < NQK) {
                 const int st = i >> 1, blk = i & 1;
                 if (blk == 0)
-                    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n0 : (f32x16){}, 0, 0, 0);
+                    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n0 : init, 0, 0, 0);
                 else
-                    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n1 : (f32x16){}, 0, 0, 0);
+                    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n1 : init, 0, 0, 0);
                 constexpr int PIECES = 16 / NQK;        // element pairs of tile j per score chunk
 #pragma unroll
                 for (int q = 0; q < PIECES; ++q) {
                     const int pi = i * PIECES + q;
                     const int e = 2 * pi, sb = e >> 4, r = e & 15;
                     const f32x16 &sc = sb ? c1 : c0;
-                    const uint32_t w = pack2(__builtin_amdgcn_exp2f(fmaf(sc[r], c, -mc)),
-                                             __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c, -mc)));
+                    const uint32_t w = pack2(__builtin_amdgcn_exp2f(sc[r]), __builtin_amdgcn_exp2f(sc[r + 1]));
                     pw[pi] = w;
                     l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l, false);
                 }

@@ -55,6 +55,8 @@ struct PrologueArgs {
     int32_t H;
     int64_t Npad;
     float eps;
+    float q_mult;                // qhat is stored multiplied by this (softmax scale * log2 e
+                                 // for the attention kernel; 1 for the diagnostic export)
     int32_t ntiles;              // Npad / 64
     SeqTable seq;
 };
@@ -65,7 +67,6 @@ struct AttnArgs {
     int64_t o_stride;
     int64_t Npad;
     int32_t H;
-    float scale_log2;            // softmax scale * log2(e)
     int32_t nseq;                // sequences with work, longest first
     int32_t seq_n[kMaxSeqs];
     int32_t seq_cu[kMaxSeqs];

@@ -163,6 +163,7 @@ PrologueArgs prologue_args(const h3attn_params *p, const Plan &pl, const void *q
     a.H = pl.H;
     a.Npad = pl.Npad;
     a.eps = p->eps;
+    a.q_mult = 1.0f;
     a.ntiles = (int32_t)(pl.Npad / kTile);
     a.seq = seq_table(pl);
     return a;
@@ -269,6 +270,7 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     pa.out_hstride = pl.Npad * pl.d;
     pa.out_tstride = pl.d;
     pa.natural = 0;
+    pa.q_mult = scale_log2(p);
     if (stages & 1)
         if ((st = hip_status(launch_prologue(pa, pl.d, hs), "prologue launch")) != H3ATTN_OK) return st;
     if (!(stages & 2)) return ok();
@@ -282,7 +284,6 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     aa.o_stride = p->o_stride;
     aa.Npad = pl.Npad;
     aa.H = pl.H;
-    aa.scale_log2 = scale_log2(p);
     const int64_t items = order_work(pl, aa, nullptr);
     return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "attention launch");
 }

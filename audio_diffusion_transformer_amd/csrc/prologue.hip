@@ -8,7 +8,9 @@
 // and rotates q and k in fp32, and writes the head-major bf16 copies the
 // attention kernel streams (qhat, khat: [H][Npad][d]; vt: V transposed per
 // 64-key tile).  Padding rows of every sequence are written as zeros, so the
-// attention kernel never reads uninitialised memory.
+// attention kernel never reads uninitialised memory.  qhat is stored already
+// multiplied by softmax_scale * log2(e), so the attention kernel's scores come
+// out of the matrix cores in base-2 exponent units.
 //
 // Work split: one workgroup (256 lanes) handles one 64-token tile of one head.
 // d/8 lanes share a (token, head) row, 16 bytes (8 channels) per lane, so
@@ -80,6 +82,10 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
             float x[8], y[8];
             unpack8(raw, x);
             norm_rope8<LPR>(x, which ? wk : wq, cs, inv_d, a.eps, y);
+            if (!which) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] *= a.q_mult;
+            }
             u32x4_t o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = pack_bf16(y[2 * i], y[2 * i + 1]);
