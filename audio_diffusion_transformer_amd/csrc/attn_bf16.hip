@@ -60,6 +60,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLazyRescale = 8.0f;
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt left at their maximum.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// Word 3 of a raw (unformatted, stride 0) buffer descriptor on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
@@ -76,11 +78,12 @@ __device__ __forceinline__ int swz(int row)
     return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// Direct-to-LDS tile fill: a tile of ROWS x CPR 16-byte chunks lies
-// contiguously in global memory; every wave instruction writes 1 KB of LDS,
-// lane L the 16 bytes at offset 16 L, so lane L fetches the global chunk the
-// swizzle places there.  The per-lane global offsets do not depend on the tile
-// and are computed once.
+// Direct-to-LDS tile fill (buffer_load_dwordx4 ... lds): a tile of ROWS x CPR
+// 16-byte chunks lies contiguously in global memory; every wave instruction
+// writes 1 KB of LDS, lane L the 16 bytes at offset 16 L, so lane L fetches
+// the global chunk the swizzle places there.  The per-lane offsets do not
+// depend on the tile and are computed once; the tile's offset is a scalar and
+// the buffer descriptor bounds every access to the sequence's rows.
 template <int ROWS, int CPR>
 struct TileFill {
     static constexpr int KB = ROWS * CPR / 64;   // 1 KB pieces in the tile
@@ -95,14 +98,14 @@ struct TileFill {
             goff[i] = (uint32_t)(row * CPR + ((lane % CPR) ^ swz<CPR>(row))) * 16u;
         }
     }
-    __device__ __forceinline__ void load(const uint16_t *g, uint16_t *lds, int wave) const
+    // Tile at byte offset `toff` (wave-uniform) of the buffer `rsrc`.
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t toff, uint16_t *lds, int wave) const
     {
-        const char *gb = reinterpret_cast<const char *>(g);
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i)
-            __builtin_amdgcn_global_load_lds(gb + goff[i],
-                                             (__attribute__((address_space(3))) void *)(lds + (wave * PER_WAVE + i) * 512),
-                                             16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void *)(lds + (wave * PER_WAVE + i) * 512), 16, goff[i],
+                toff, 0, 0);
     }
 };
 
@@ -176,8 +179,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     vfill.init(wave, lane);
     auto kbuf = [&](int buf) { return buf ? lk1 : lk0; };
     auto vbuf = [&](int buf) { return buf ? lv1 : lv0; };
-    auto load_k = [&](int j, uint16_t *dst) { kfill.load(kbase + (int64_t)j * kTile * D, dst, wave); };
-    auto load_v = [&](int j, uint16_t *dst) { vfill.load(vbase + (int64_t)j * D * kTile, dst, wave); };
+    // buffer descriptors over this (sequence, head)'s padded K rows and V^T tiles
+    const int tbytes = kTile * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(kbase), 0, nt * tbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(vbase), 0, nt * tbytes, kBufferFlags);
+    auto load_k = [&](int j, uint16_t *dst) { kfill.load(krs, (uint32_t)(j * tbytes), dst, wave); };
+    auto load_v = [&](int j, uint16_t *dst) { vfill.load(vrs, (uint32_t)(j * tbytes), dst, wave); };
 
     f32x16 o[DB];
 #pragma unroll
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     // element pairs of tile j (exp2, bf16 pack, row-sum dot2).  Scheduling
     // barriers keep the chunks in this order, so every fragment read has PD
     // MFMAs to land and the exps run beside the matrix cores.
-    constexpr int PD = 3;
+    constexpr int PD = 5;
     constexpr int NQK = 2 * KSTEPS, NM = 2 * KSTEPS + 4 * DB;
     auto frag = [&](int i, const uint16_t *kl, const uint16_t *vl) -> bf16x8 {
         if (i < NQK) {
@@ -291,6 +300,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             if (i + PD < NM) fa[i + PD] = frag(i + PD, kl, vl);
+            // the exp-carrying score chunks issue ahead of the other wave on the SIMD
+            if (i == 0) __builtin_amdgcn_s_setprio(1);
+            if (i == NQK) __builtin_amdgcn_s_setprio(0);
             if (i < NQK) {
                 const int st = i >> 1, blk = i & 1;
                 if (blk == 0)
