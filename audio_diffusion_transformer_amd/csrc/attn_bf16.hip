@@ -47,94 +47,17 @@
 // range.  P is rounded to bf16 for the P.V product and the row sum l adds
 // exactly those rounded values.
 #include "h3_internal.h"
+#include "attn_common.h"
 
 namespace h3 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyRescale = 8.0f;
-// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt left at their maximum.
-constexpr int kWaitVmcnt0 = 0x0F70;
-// Word 3 of a raw (unformatted, stride 0) buffer descriptor on gfx9-family parts.
-constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ uint32_t pack2(float a, float b)
-{
-    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// 16-byte chunk swizzle of an LDS row: rows of 256 bytes (16 chunks) XOR the
-// chunk index with row % 16, rows of 128 bytes (8 chunks) with (row / 2) % 8,
-// so that 16 consecutive rows read at one logical chunk cover all 64 banks.
-template <int CPR>
-__device__ __forceinline__ int swz(int row)
-{
-    return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
-}
-
-// Direct-to-LDS tile fill (buffer_load_dwordx4 ... lds): a tile of ROWS x CPR
-// 16-byte chunks lies contiguously in global memory; every wave instruction
-// writes 1 KB of LDS, lane L the 16 bytes at offset 16 L, so lane L fetches
-// the global chunk the swizzle places there.  The per-lane offsets do not
-// depend on the tile and are computed once; the tile's offset is a scalar and
-// the buffer descriptor bounds every access to the sequence's rows.
-template <int ROWS, int CPR>
-struct TileFill {
-    static constexpr int KB = ROWS * CPR / 64;   // 1 KB pieces in the tile
-    static constexpr int PER_WAVE = KB / 4;
-    static constexpr int RPK = 64 / CPR;         // rows per piece
-    uint32_t goff[PER_WAVE];                     // byte offsets in the global tile
-    __device__ __forceinline__ void init(int wave, int lane)
-    {
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const int row = (wave * PER_WAVE + i) * RPK + lane / CPR;
-            goff[i] = (uint32_t)(row * CPR + ((lane % CPR) ^ swz<CPR>(row))) * 16u;
-        }
-    }
-    // Tile at byte offset `toff` (wave-uniform) of the buffer `rsrc`.
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t toff, uint16_t *lds, int wave) const
-    {
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void *)(lds + (wave * PER_WAVE + i) * 512), 16, goff[i],
-                toff, 0, 0);
-    }
-};
-
-// max / sum of a lane's value and the value of lane l ^ 32 (same query row).
-__device__ __forceinline__ float row_max2(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float row_sum2(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
-// Row maximum of the 32 scores a lane holds (16 of each 32-key block).
-__device__ __forceinline__ float lane_max32(const f32x16 &s0, const f32x16 &s1)
-{
-    float a = max3f(s0[0], s0[1], s0[2]), b = max3f(s1[0], s1[1], s1[2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) {
-        a = max3f(a, s0[r], s0[r + 1]);
-        b = max3f(b, s1[r], s1[r + 1]);
-    }
-    return max3f(a, b, fmaxf(s0[15], s1[15]));
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 {

@@ -23,20 +23,19 @@
 //          with the running max raised only when a tile exceeds it by more
 //          than 1, so p <= 2; P quantised to e4m3 as p * 224 (a fixed per-row
 //          scale mapping the largest possible p to 448); O^T += V8^T . P8^T on
-//          v_mfma_f32_32x32x64_f8f6f4; the row sum adds the unquantised p.
-//          Finally o_c = O_c * vscale_c / (224 * l).
+//          v_mfma_f32_32x32x64_f8f6f4; the row sum l is the sum of the
+//          quantised P (one more FP8 MFMA against a row of ones).  Finally
+//          o_c = O_c * vscale_c / l.
 #include "h3_internal.h"
 #include "norm_rope.h"
+#include "attn_common.h"
 
 namespace h3 {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int QD = 128;               // head dim of the quantised path
 constexpr float kPScale = 224.0f;     // 448 / 2^kQ8Lazy
@@ -53,10 +52,12 @@ __device__ __forceinline__ uint32_t pack_i8x4(int32_t a, int32_t b, int32_t c, i
            ((uint32_t)(d & 0xff) << 24);
 }
 
-// Four fp32 -> four OCP e4m3 bytes (round to nearest even), little-endian.
+// Four fp32 -> four OCP e4m3 bytes (round to nearest even), little-endian.  The
+// first conversion's pass-through operand is arbitrary (its half is overwritten
+// by the second); passing a dead input avoids materialising a zero.
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -283,17 +284,20 @@ __global__ __launch_bounds__(256) void q8_export_kernel(Q8ExportArgs a)
 }
 
 // --------------------------------------------------------------- attention
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
-{
-    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
+// One workgroup = 4 waves x 32 query rows of one (sequence, head).  K8 and
+// V8^T tiles of 64 keys are filled straight into double-buffered LDS by
+// buffer_load ... lds.  The loop is software-pipelined over three tiles so that
+// every step of the steady state carries both matrix-core and vector work: step
+// j issues the INT8 score MFMAs of tile j+1, the FP8 P.V MFMAs of tile j-1
+// (whose P was packed in step j-1; one instruction covers the tile's 64 keys for
+// 32 channels) and, beside them, the exp2 and FP8 packing of tile j.  The row
+// sum comes from the matrix cores too: one more FP8 MFMA per tile multiplies P
+// by a constant row of ones, so l is the sum of the quantised P actually
+// applied to V.
 __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
 {
-    constexpr int PER = kTile * QD / 16 / 256;      // 16-byte chunks per lane per tile (K and V each)
-    __shared__ __attribute__((aligned(16))) int8_t lk[2][kTile * QD];
-    __shared__ __attribute__((aligned(16))) uint8_t lv[2][QD * kTile];
+    __shared__ __attribute__((aligned(16))) int8_t lk0[kTile * QD], lk1[kTile * QD];
+    __shared__ __attribute__((aligned(16))) uint8_t lv0[QD * kTile], lv1[QD * kTile];
 
     const int b = blockIdx.x;
     int si = 0;
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     const int64_t ntiles = a.Npad / kTile;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, hh = lane >> 5;
     const int q0 = qb * kBlockM + wave * 32;
 
@@ -318,114 +322,234 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     }
     const float cq = a.qscale[head * ntiles + (off + q0) / kTile] * a.scale_log2;
     const float *ksc = a.kscale + head * ntiles + off / kTile;
-    const int8_t *kbase = a.k8 + ((int64_t)head * a.Npad + off) * QD;
-    const uint8_t *vbase = a.v8t + ((int64_t)head * ntiles + off / kTile) * (QD * kTile);
     const int nt = (n + kTile - 1) / kTile;
 
-    u32x4_t stk[PER], stv[PER];
-    auto gload = [&](int j) {
-        const u32x4_t *ks = reinterpret_cast<const u32x4_t *>(kbase + (int64_t)j * kTile * QD);
-        const u32x4_t *vs = reinterpret_cast<const u32x4_t *>(vbase + (int64_t)j * QD * kTile);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            stk[i] = ks[tid + 256 * i];
-            stv[i] = vs[tid + 256 * i];
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int g = tid + 256 * i;
-            const int kr = g >> 3, kc = g & 7;
-            *reinterpret_cast<u32x4_t *>(&lk[buf][kr * QD + 16 * (kc ^ (kr & 7))]) = stk[i];
-            const int vr = g >> 2, vc = g & 3;
-            *reinterpret_cast<u32x4_t *>(&lv[buf][vr * kTile + 16 * (vc ^ ((vr >> 1) & 3))]) = stv[i];
-        }
-    };
+    TileFill<kTile, 8> kfill;       // K8 rows: 128 bytes
+    TileFill<QD, 4> vfill;          // V8^T rows: 64 bytes
+    kfill.init(wave, lane);
+    vfill.init(wave, lane);
+    const int tbytes = kTile * QD;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(a.k8 + ((int64_t)head * a.Npad + off) * QD), 0, nt * tbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.v8t + ((int64_t)head * ntiles + off / kTile) * (QD * kTile)), 0, nt * tbytes,
+        kBufferFlags);
+    auto load_k = [&](int j, void *dst) { kfill.load(krs, (uint32_t)(j * tbytes), dst, wave); };
+    auto load_v = [&](int j, void *dst) { vfill.load(vrs, (uint32_t)(j * tbytes), dst, wave); };
 
-    f32x16 o[4];
-#pragma unroll
+    f32x16 o[4], ol = (f32x16){};   // O^T per 32-channel block; ol row 0 = row sum
     for (int i = 0; i < 4; ++i) o[i] = (f32x16){};
-    float m_used = -INFINITY, l = 0.f;
+    // A operand of the row-sum MFMA: channel row 0 all ones (e4m3 1.0 = 0x38), rows 1..31 zero
+    const uint32_t one4 = m == 0 ? 0x38383838u : 0u;
+    const i32x8 ones = {(int)one4, (int)one4, (int)one4, (int)one4, (int)one4, (int)one4, (int)one4, (int)one4};
+    i32x8 pp = (i32x8){};          // FP8 P of the previous tile, whose P.V is still pending
+    float m_run = 0.f;              // running max (log2 units) of the scaled scores
+    bool first = true;
     const float lg2p = __builtin_log2f(kPScale);
+    // The score accumulators start at the bits of 1.5 * 2^23: integer addition of
+    // |S| < 2^22 then leaves the bits of the float 12582912 + S, so no int->float
+    // conversion is needed (|S| <= 127 * 127 * 128 < 2^21).
+    constexpr int32_t kMagicBits = 0x4B400000;
+    constexpr float kMagic = 12582912.0f;
+    // Held in VGPRs for the whole kernel (an opaque copy, so the compiler keeps
+    // the 16-register block live instead of re-materialising it per tile).
+    int32_t magic_v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(kMagicBits));
+    const i32x16 magic = (i32x16){} + magic_v;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int j = 0; j < nt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nt) gload(j + 1);
-
-        i32x16 s0 = (i32x16){}, s1 = (i32x16){};
-        const int8_t *kl = lk[buf];
+    // K fragment of score chunk c: 32-channel step c/2, key block c%2.
+    auto kfrag = [&](const int8_t *kl, int c) -> i32x4 {
+        const int ch = (2 * (c >> 1) + hh) ^ swz<8>(m);
+        return *reinterpret_cast<const i32x4 *>(kl + (32 * (c & 1) + m) * QD + 16 * ch);
+    };
+    auto scores = [&](const int8_t *kl, i32x16 &s0, i32x16 &s1) {
+        s0 = magic;
+        s1 = magic;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int ch = (2 * st + hh) ^ (m & 7);
-            const i32x4 k0 = *reinterpret_cast<const i32x4 *>(kl + m * QD + 16 * ch);
-            const i32x4 k1 = *reinterpret_cast<const i32x4 *>(kl + (32 + m) * QD + 16 * ch);
-            s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qf[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qf[st], s1, 0, 0, 0);
+        for (int c = 0; c < 8; c += 2) {
+            s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kfrag(kl, c), qf[c >> 1], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kfrag(kl, c + 1), qf[c >> 1], s1, 0, 0, 0);
         }
-        const float cs = cq * ksc[j];
-        float f0[16], f1[16];
+    };
+    // V^T fragment of 32-channel block db: the 64 keys of the tile, in the
+    // operand's key order, as two 16-byte pieces.
+    auto vfrag = [&](const uint8_t *vl, int db) -> i32x8 {
+        const int row = 32 * db + m;
+        const int sw = swz<4>(row);
+        const i32x4 va = *reinterpret_cast<const i32x4 *>(vl + row * kTile + 16 * ((2 * hh) ^ sw));
+        const i32x4 vb = *reinterpret_cast<const i32x4 *>(vl + row * kTile + 16 * ((2 * hh + 1) ^ sw));
+        return (i32x8){va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+    };
+    auto pv = [&](const uint8_t *vl, const i32x8 &pf) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vfrag(vl, db), pf, o[db], 0, 0, 0, 0, 0, 0);
+        ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, ol, 0, 0, 0, 0, 0, 0);
+    };
+    // Key (0..63 within the tile) of element r of the lane's score block kb.
+    auto key_of = [&](int kb, int r) { return 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3); };
+    // P word w (keys of elements 4(w%4)..4(w%4)+3 of block w/4) as four e4m3
+    // bytes: e4m3(2^x), x = raw * cs + c0 (the scaled score relative to m_run,
+    // plus log2 224).  This byte order is the FP8 P.V operand's.
+    auto pword = [&](const i32x16 &s0, const i32x16 &s1, int w, float cs, float c0) -> int32_t {
+        const i32x16 &s = w < 4 ? s0 : s1;
+        const int r = 4 * (w & 3);
+        return (int32_t)fp8x4(__builtin_amdgcn_exp2f(fmaf(__int_as_float(s[r]), cs, c0)),
+                              __builtin_amdgcn_exp2f(fmaf(__int_as_float(s[r + 1]), cs, c0)),
+                              __builtin_amdgcn_exp2f(fmaf(__int_as_float(s[r + 2]), cs, c0)),
+                              __builtin_amdgcn_exp2f(fmaf(__int_as_float(s[r + 3]), cs, c0)));
+    };
+    // Row max of tile j's raw scores (monotone in S; keys past the sequence end
+    // excluded on the last tile).  When it exceeds m_run by more than kQ8Lazy
+    // (always on the first tile) m_run is raised: the pending P.V of the
+    // previous tile (V tile in vprev) is applied first, then O and the row sum
+    // are rescaled.  Returns c0 for pword.
+    auto tile_max = [&](int j, float cs, const i32x16 &s0, const i32x16 &s1, bool mask,
+                        const uint8_t *vprev) -> float {
+        float e[32];
+        const int valid = n - j * kTile;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            f0[r] = (float)s0[r] * cs;
-            f1[r] = (float)s1[r] * cs;
-        }
-        const int valid = n - j * kTile;
-        if (valid < kTile) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (key >= valid) f0[r] = -INFINITY;
-                if (32 + key >= valid) f1[r] = -INFINITY;
+            e[r] = __int_as_float(s0[r]);
+            e[16 + r] = __int_as_float(s1[r]);
+            if (mask) {
+                if (key_of(0, r) >= valid) e[r] = -INFINITY;
+                if (key_of(1, r) >= valid) e[16 + r] = -INFINITY;
             }
         }
-        float mx = fmaxf(f0[0], f1[0]);
+        float mx = max3f(e[0], e[1], e[2]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(f0[r], f1[r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool need = mx - m_used > kQ8Lazy;
+        for (int r = 3; r < 31; r += 2) mx = max3f(mx, e[r], e[r + 1]);
+        const float cm = -kMagic * cs;
+        mx = fmaf(row_max2(fmaxf(mx, e[31])), cs, cm) - m_run;
+        const bool need = first || mx > kQ8Lazy;
         if (__any(need)) {
-            const float mn = need ? mx : m_used;
-            const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
-            m_used = mn;
-            l *= alpha;
+            const float delta = need ? mx : 0.f;
+            if (!first) {
+                pv(vprev, pp);
+                pp = (i32x8){};
+                const float alpha = __builtin_amdgcn_exp2f(-delta);
+                ol[0] *= alpha;     // rows 1..31 of the row-sum block are zero
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] *= alpha;
+                for (int i = 0; i < 4; ++i) o[i] *= alpha;
+            }
+            m_run += delta;
+            first = false;
         }
-        const float sub = m_used - lg2p;          // p * 224 = 2^(s - m + log2 224)
+        return lg2p - m_run + cm;
+    };
+
+    // Steady-state step (hand-scheduled): chunk i issues score MFMA i of the
+    // next tile (K in kl), one FP8 MFMA of the pending P.V (row sum at chunk 0,
+    // channel block db at chunk 2db+1; V of the previous tile in vprev) and P
+    // word i of the current tile (raw scores c0s/c1s).  LDS fragments are read
+    // two chunks ahead.
+    auto body = [&](const int8_t *kl, const uint8_t *vprev, const i32x16 &c0s, const i32x16 &c1s, float cs,
+                    float c0, i32x16 &n0, i32x16 &n1) {
+        i32x4 kf[8];
+        i32x8 vf[4];
+        i32x8 pn;
+        kf[0] = kfrag(kl, 0);
+        kf[1] = kfrag(kl, 1);
+        vf[0] = vfrag(vprev, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i + 2 < 8) kf[i + 2] = kfrag(kl, i + 2);
+            if (i == 1 || i == 3 || i == 5) vf[(i + 1) >> 1] = vfrag(vprev, (i + 1) >> 1);
+            const int st = i >> 1;
+            if ((i & 1) == 0)
+                n0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[i], qf[st], st ? n0 : magic, 0, 0, 0);
+            else
+                n1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[i], qf[st], st ? n1 : magic, 0, 0, 0);
+            if (i == 0)
+                ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pp, ol, 0, 0, 0, 0, 0, 0);
+            else if (i & 1)
+                o[i >> 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[i >> 1], pp, o[i >> 1], 0, 0, 0, 0, 0, 0);
+            // The empty asm consumes the word here: without it the compiler
+            // sinks every exp to the end of the step, where pn is first read.
+            int32_t w = pword(c0s, c1s, i, cs, c0);
+            asm volatile("" : "+v"(w));
+            pn[i] = w;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pp = pn;
+    };
+
+    // ---- prologue: K0 and K1 resident, scores of tile 0.  V tile 0 also goes
+    // to the buffer the first step reads as "previous tile": its pending P is
+    // zero, so that P.V adds nothing (and the buffer holds finite values).
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(0, lk0);
+    if (nt > 1) load_k(1, lk1);
+    load_v(0, lv1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    i32x16 sa0, sa1, sb0, sb1;
+    scores(lk0, sa0, sa1);
+    __syncthreads();
+
+    // Step j: K(j+2) -> kbuf[j%2], V(j) -> vbuf[j%2]; reads K(j+1) from
+    // kbuf[(j+1)%2] and V(j-1) from vbuf[(j-1)%2].  The K scale of the next tile
+    // is loaded a step ahead so that the wait before each barrier covers it.
+    float ks0 = ksc[0];
+    int j = 0;
+    for (; j + 3 < nt; j += 2) {
+        const float ks1 = ksc[j + 1];
+        load_k(j + 2, lk0);
+        load_v(j, lv0);
+        float cs = cq * ks0;
+        float c0 = tile_max(j, cs, sa0, sa1, false, lv1);
+        body(lk1, lv1, sa0, sa1, cs, c0, sb0, sb1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        ks0 = ksc[j + 2];
+        load_k(j + 3, lk1);
+        load_v(j + 1, lv1);
+        cs = cq * ks1;
+        c0 = tile_max(j + 1, cs, sb0, sb1, false, lv0);
+        body(lk0, lv0, sb0, sb1, cs, c0, sa0, sa1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+    }
+    for (; j + 1 < nt; ++j) {
+        const uint8_t *vp = ((j - 1) & 1) ? lv1 : lv0;
+        if (j + 2 < nt) load_k(j + 2, (j & 1) ? lk1 : lk0);
+        load_v(j, (j & 1) ? lv1 : lv0);
+        const float cs = cq * ksc[j];
+        const float c0 = tile_max(j, cs, sa0, sa1, false, vp);
+        body(((j + 1) & 1) ? lk1 : lk0, vp, sa0, sa1, cs, c0, sb0, sb1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        sa0 = sb0;
+        sa1 = sb1;
+    }
+    // last tile (keys past the sequence end masked): its V is loaded here
+    load_v(j, (j & 1) ? lv1 : lv0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    {
+        const uint8_t *vp = ((j - 1) & 1) ? lv1 : lv0, *vl = (j & 1) ? lv1 : lv0;
+        const float cs = cq * ksc[j];
+        const float c0 = tile_max(j, cs, sa0, sa1, true, vp);
+        pv(vp, pp);
+        const int valid = n - j * kTile;
         i32x8 pf;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
-            const float *src = w < 4 ? f0 + 4 * w : f1 + 4 * (w - 4);
-            const float p0 = __builtin_amdgcn_exp2f(src[0] - sub);
-            const float p1 = __builtin_amdgcn_exp2f(src[1] - sub);
-            const float p2 = __builtin_amdgcn_exp2f(src[2] - sub);
-            const float p3 = __builtin_amdgcn_exp2f(src[3] - sub);
-            l += (p0 + p1) + (p2 + p3);
-            pf[w] = (int32_t)fp8x4(p0, p1, p2, p3);
-        }
-
-        const uint8_t *vl = lv[buf];
+            const i32x16 &s = w < 4 ? sa0 : sa1;
+            float e[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int row = 32 * db + m;
-            const int sw = (row >> 1) & 3;
-            const i32x4 va = *reinterpret_cast<const i32x4 *>(vl + row * kTile + 16 * ((2 * hh) ^ sw));
-            const i32x4 vb = *reinterpret_cast<const i32x4 *>(vl + row * kTile + 16 * ((2 * hh + 1) ^ sw));
-            const i32x8 vf = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-            o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[db], 0, 0, 0, 0, 0, 0);
+            for (int t = 0; t < 4; ++t) {
+                const int r = 4 * (w & 3) + t;
+                e[t] = key_of(w >> 2, r) < valid ? __builtin_amdgcn_exp2f(fmaf(__int_as_float(s[r]), cs, c0)) : 0.f;
+            }
+            pf[w] = (int32_t)fp8x4(e[0], e[1], e[2], e[3]);
         }
-
-        if (j + 1 < nt) lstore(buf ^ 1);
-        __syncthreads();
+        pv(vl, pf);
     }
 
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = 1.0f / lt;
+    // row sum: channel row 0 of the ones block lives in register 0 of the lanes with hh = 0
+    const float inv = 1.0f / row_sum2(hh == 0 ? ol[0] : 0.f);
     const int qrow = q0 + m;
     if (qrow < n) {
         const float *vs = a.vscale + ((int64_t)a.seq_idx[si] * a.H + head) * QD;
@@ -436,8 +560,8 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
             for (int i = 0; i < 4; ++i) {
                 const int d0 = 32 * db + 8 * i + 4 * hh;
                 const f32x4_t sc = *reinterpret_cast<const f32x4_t *>(vs + d0);
-                const u32x2_t w = {pack_bf16(o[db][4 * i] * sc[0] * inv, o[db][4 * i + 1] * sc[1] * inv),
-                                   pack_bf16(o[db][4 * i + 2] * sc[2] * inv, o[db][4 * i + 3] * sc[3] * inv)};
+                const u32x2_t w = {pack2(o[db][4 * i] * sc[0] * inv, o[db][4 * i + 1] * sc[1] * inv),
+                                   pack2(o[db][4 * i + 2] * sc[2] * inv, o[db][4 * i + 3] * sc[3] * inv)};
                 *reinterpret_cast<u32x2_t *>(op + d0) = w;
             }
         }

@@ -179,9 +179,18 @@ def main():
     summary = ("attn_q8_%s_pmc.md" if w.quantized else "attn_bf16_%s_pmc.md") % w.name
     traffic = measured_traffic(kernel_file, summary)
     N, H, d = w.N, w.H, w.d
-    pro_bytes = 3 * N * H * d * 2 + 3 * N * H * d * 2 + N * (d // 2) * 8   # read q,k,v,table; write 3 copies
+    if w.quantized:
+        # pass 1 reads q, k, v and the table and writes q8; pass 3 re-reads k, v and the
+        # table and writes k8 and v8 (per-tile scales and sums are negligible)
+        pro_bytes = 5 * N * H * d * 2 + 3 * N * H * d + 2 * N * (d // 2) * 8
+        metric = ("attention TFLOP/s (INT8 QK, FP8 PV) and %% of fp8 MFMA peak at N=%d packed tokens, "
+                  "H=%d, d=%d" % (N, H, d))
+    else:
+        # read q, k, v and the table; write qhat, khat and the transposed V copy
+        pro_bytes = 3 * N * H * d * 2 + 3 * N * H * d * 2 + N * (d // 2) * 8
+        metric = METRIC if w.name == "joint" else METRIC.replace("N=125k", "N=%d" % N)
     res = {
-        "metric": METRIC if w.name == "joint" else METRIC.replace("N=125k", "N=%d" % N),
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
