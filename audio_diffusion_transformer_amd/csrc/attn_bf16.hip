@@ -58,6 +58,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyRescale = 8.0f;
+// Largest score bound (log2 units) for which the fixed shift is used.
+constexpr float kFixedShiftMax = 48.0f;
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 {
@@ -115,14 +117,51 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[i] = (f32x16){};
     float m_run = 0.f, l = 0.f;         // running max (log2 units), row sum
+    // -m_run in all 16 registers: the accumulator start of every score MFMA
+    // chain.  It changes only when m_run is raised, and is kept opaque so that
+    // the compiler holds it instead of rebuilding the splat for every tile.
+    f32x16 ninit = (f32x16){};
     bool first = true;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+    // Fixed shift.  Softmax is unchanged by a per-row shift, and every score of
+    // the row is at most |q'| * max_k |k| (Cauchy-Schwarz; q' already carries
+    // scale * log2 e, the norms are those of the stored bf16 rows).  When that
+    // bound mb is small enough for every row of the wave, m_run = mb for the
+    // whole row: p = 2^(s - mb) <= 1, and even the row's largest p stays a
+    // normal number (s_max >= -mb, so p_max >= 2^-2mb), so no running max, no
+    // rescale and no per-tile row maximum are needed.  Larger bounds keep the
+    // lazily rescaled running max.
+    bool fixed_shift;
+    {
+        float qn2 = 0.f;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = (float)qf[s][i];
+                qn2 = fmaf(x, x, qn2);
+            }
+        qn2 = row_sum2(qn2);
+        const float *kn = a.knorm + (int64_t)head * (a.Npad / kTile) + off / kTile;
+        float kmax = 0.f;
+        for (int i = lane; i < nt; i += 64) kmax = fmaxf(kmax, kn[i]);
+#pragma unroll
+        for (int mm = 32; mm >= 1; mm >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, mm));
+        const float mb = sqrtf(qn2) * kmax * (1.0f + 1.0f / 1024);
+        fixed_shift = __all(mb <= kFixedShiftMax);
+        if (fixed_shift) {
+            m_run = mb;
+            ninit = -m_run;
+            asm volatile("" : "+v"(ninit));
+            first = false;
+        }
+    }
+
     // x^T = K . Q'^T - m_run of one 64-key tile from K buffer kl.
     auto scores = [&](const uint16_t *kl, f32x16 &s0, f32x16 &s1) {
-        const f32x16 init = -m_run;
-        s0 = init;
-        s1 = init;
+        s0 = ninit;
+        s1 = ninit;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
             const int ch = (2 * st + hh) ^ swz<KCPR>(m);
@@ -146,6 +185,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
                 if (32 + key >= valid) s1[r] = -INFINITY;
             }
         }
+        if (fixed_shift) return;
         const float mx = row_max2(lane_max32(s0, s1));
         const bool need = first || mx > kLazyRescale;
         if (__any(need)) {
@@ -157,6 +197,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
                 for (int i = 0; i < DB; ++i) o[i] *= alpha;
             }
             m_run += delta;
+            ninit = -m_run;
+            asm volatile("" : "+v"(ninit));
             s0 -= delta;
             s1 -= delta;
             first = false;
@@ -215,7 +257,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     };
     auto body = [&](const uint16_t *kl, const uint16_t *vl, const f32x16 &c0, const f32x16 &c1,
                     f32x16 &n0, f32x16 &n1) {
-        const f32x16 init = -m_run;
         bf16x8 fa[NM];
         uint32_t pw[16];
 #pragma unroll
@@ -229,9 +270,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
             if (i < NQK) {
                 const int st = i >> 1, blk = i & 1;
                 if (blk == 0)
-                    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n0 : init, 0, 0, 0);
+                    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n0 : ninit, 0, 0, 0);
                 else
-                    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n1 : init, 0, 0, 0);
+                    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], qf[st], st ? n1 : ninit, 0, 0, 0);
                 constexpr int PIECES = 16 / NQK;        // element pairs of tile j per score chunk
 #pragma unroll
                 for (int q = 0; q < PIECES; ++q) {

@@ -16,6 +16,8 @@ constexpr int kTile = 64;        // key tile (and quantisation block) in tokens
 //   vt         : bf16 [H][Npad/64][d][64]  (V transposed per 64-key tile; the
 //                keys inside each 32-key half are stored in the order the
 //                P.V matrix-core operand consumes them, see attn_bf16.hip)
+//   knorm      : fp32 [H][Npad/64]  largest |khat| (2-norm of the stored bf16
+//                row) of each 64-token tile; 0 for padding tiles
 // Quantised path:
 //   q8, k8     : int8 [H][Npad][d]
 //   v8t        : fp8  [H][Npad/64][d][64]  (transposed; key order of the FP8 P.V operand)
@@ -27,7 +29,7 @@ struct Plan {
     int64_t N, Npad;
     int32_t cu[kMaxSeqs + 1];    // packed token starts
     int32_t off[kMaxSeqs + 1];   // padded starts (multiples of kSeqPad)
-    size_t qhat, khat, vt;       // byte offsets into the workspace
+    size_t qhat, khat, vt, knorm; // byte offsets into the workspace
     size_t q8, k8, v8t, qscale, kscale, ksum, vmax, kmean, vscale;
     size_t bytes_bf16, bytes_q8;
 };
@@ -50,6 +52,7 @@ struct PrologueArgs {
     // h*out_hstride + t*out_tstride + c.  When `natural` is set, t is the packed
     // token and padding rows are skipped (diagnostic export).
     uint16_t *qhat, *khat, *vt;
+    float *knorm;                // per-tile max |khat| (not written when natural is set)
     int64_t out_hstride, out_tstride;
     int32_t natural;
     int32_t H;
@@ -63,6 +66,7 @@ struct PrologueArgs {
 
 struct AttnArgs {
     const uint16_t *qhat, *khat, *vt;
+    const float *knorm;
     uint16_t *out;
     int64_t o_stride;
     int64_t Npad;

@@ -92,6 +92,7 @@ h3attn_status make_plan(const h3attn_params *p, const int32_t *cu, Plan *pl)
     pl->qhat = take(H * Np * d * 2);
     pl->khat = take(H * Np * d * 2);
     pl->vt = take(H * Np * d * 2);
+    pl->knorm = take(H * T * 4);
     pl->bytes_bf16 = std::max<size_t>(at, 256);   // never 0: 0 reports an error
     at = 0;
     pl->q8 = take(H * Np * d);
@@ -267,6 +268,7 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     pa.qhat = reinterpret_cast<uint16_t *>(ws + pl.qhat);
     pa.khat = reinterpret_cast<uint16_t *>(ws + pl.khat);
     pa.vt = reinterpret_cast<uint16_t *>(ws + pl.vt);
+    pa.knorm = reinterpret_cast<float *>(ws + pl.knorm);
     pa.out_hstride = pl.Npad * pl.d;
     pa.out_tstride = pl.d;
     pa.natural = 0;
@@ -280,6 +282,7 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     aa.qhat = pa.qhat;
     aa.khat = pa.khat;
     aa.vt = pa.vt;
+    aa.knorm = pa.knorm;
     aa.out = static_cast<uint16_t *>(out);
     aa.o_stride = p->o_stride;
     aa.Npad = pl.Npad;

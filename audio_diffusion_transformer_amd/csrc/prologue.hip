@@ -12,6 +12,11 @@
 // multiplied by softmax_scale * log2(e), so the attention kernel's scores come
 // out of the matrix cores in base-2 exponent units.
 //
+// It also records, per 64-token tile and head, the largest 2-norm of the stored
+// (bf16-rounded) khat rows.  With |qhat| this bounds every score of a query row
+// (Cauchy-Schwarz), which lets the attention kernel fix its softmax shift up
+// front.
+//
 // Work split: one workgroup (256 lanes) handles one 64-token tile of one head.
 // d/8 lanes share a (token, head) row, 16 bytes (8 channels) per lane, so
 // every global access is a coalesced 16-byte vector access and the RMSNorm
@@ -48,6 +53,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
     constexpr int LPR = D / 8;          // lanes per (token, head) row
     constexpr int RPP = 256 / LPR;      // rows per pass
     __shared__ __attribute__((aligned(16))) uint16_t vl[D][64 + 8];
+    __shared__ float kred[4];
 
     const int H = a.H;
     const int b = blockIdx.x;
@@ -65,6 +71,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
     float wq[8], wk[8];
     load_w8(a.norm_w, h, D, c, wq);
     load_w8(a.norm_w, H + h, D, c, wk);
+    float kn2 = 0.f;                    // largest |khat|^2 of the rows this lane saw
 
 #pragma unroll
     for (int pass = 0; pass < kTile / RPP; ++pass) {
@@ -90,6 +97,19 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = pack_bf16(y[2 * i], y[2 * i + 1]);
             if (!ok) o = (u32x4_t){0u, 0u, 0u, 0u};
+            if (which) {
+                // squared norm of the stored row: the lane's 8 rounded values,
+                // then a butterfly over the row's LPR lanes
+                float ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = __uint_as_float(o[i] << 16), hi = __uint_as_float(o[i] & 0xffff0000u);
+                    ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+                }
+#pragma unroll
+                for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+                kn2 = fmaxf(kn2, ss);
+            }
             if (ok || !a.natural) {
                 uint16_t *dst = (which ? a.khat : a.qhat) + h * a.out_hstride + orow * a.out_tstride + 8 * c;
                 *reinterpret_cast<u32x4_t *>(dst) = o;
@@ -107,7 +127,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a)
         }
     }
     if (a.natural) return;
+#pragma unroll
+    for (int m = 32; m >= LPR; m >>= 1) kn2 = fmaxf(kn2, __shfl_xor(kn2, m));
+    if ((t & 63) == 0) kred[t >> 6] = kn2;
     __syncthreads();
+    if (t == 0)
+        a.knorm[(int64_t)h * a.ntiles + gt] = sqrtf(fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3])));
     uint16_t *vt = a.vt + ((int64_t)h * a.ntiles + gt) * (D * kTile);
 #pragma unroll
     for (int g = t; g < D * 8; g += 256) {

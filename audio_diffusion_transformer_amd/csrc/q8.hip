@@ -170,20 +170,36 @@ __global__ __launch_bounds__(256) void q8_pass1_kernel(Q8Args a)
 }
 
 // ------------------------------------------------------------------ reduce
-__global__ __launch_bounds__(128) void q8_reduce_kernel(Q8Args a)
+// One workgroup per (sequence, head): thread (g, c) folds the per-tile partials
+// of channel c for tiles g, g+8, g+16, ...; the 8 groups are then combined in
+// LDS in group order, so the result does not depend on timing.
+constexpr int kReduceGroups = 8;
+__global__ __launch_bounds__(kReduceGroups * QD) void q8_reduce_kernel(Q8Args a)
 {
-    const int s = blockIdx.x / a.H, h = blockIdx.x % a.H, c = threadIdx.x;
+    __shared__ float rs[kReduceGroups][QD], rm[kReduceGroups][QD];
+    const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
+    const int c = threadIdx.x % QD, g = threadIdx.x / QD;
     const int n = a.seq.cu[s + 1] - a.seq.cu[s];
     const int t0 = a.seq.off[s] / kTile, nt = (n + kTile - 1) / kTile;
     float sum = 0.f, mx = 0.f;
-    for (int i = 0; i < nt; ++i) {
+#pragma unroll 4
+    for (int i = g; i < nt; i += kReduceGroups) {
         const int64_t o = ((int64_t)h * a.ntiles + t0 + i) * QD + c;
         sum += a.ksum[o];
         mx = fmaxf(mx, a.vmax[o]);
     }
-    const int64_t o = ((int64_t)s * a.H + h) * QD + c;
-    a.kmean[o] = n > 0 ? sum / (float)n : 0.f;
-    a.vscale[o] = mx > 0.f ? mx / 448.0f : 1.0f;
+    rs[g][c] = sum;
+    rm[g][c] = mx;
+    __syncthreads();
+    if (g == 0) {
+        for (int k = 1; k < kReduceGroups; ++k) {
+            sum += rs[k][c];
+            mx = fmaxf(mx, rm[k][c]);
+        }
+        const int64_t o = ((int64_t)s * a.H + h) * QD + c;
+        a.kmean[o] = n > 0 ? sum / (float)n : 0.f;
+        a.vscale[o] = mx > 0.f ? mx / 448.0f : 1.0f;
+    }
 }
 
 // ------------------------------------------------------------------ pass 3
@@ -577,7 +593,7 @@ hipError_t launch_q8_prep(const Q8Args &a, int d, hipStream_t st)
     hipLaunchKernelGGL(q8_pass1_kernel, grid, dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(q8_reduce_kernel, dim3((unsigned)(a.seq.S * a.H)), dim3(QD), 0, st, a);
+    hipLaunchKernelGGL(q8_reduce_kernel, dim3((unsigned)(a.seq.S * a.H)), dim3(kReduceGroups * QD), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(q8_pass3_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();

@@ -112,12 +112,13 @@ def test_workspace_errors():
 
 
 def test_workspace_size_layout():
-    # three head-major bf16 copies; every sequence padded to 256 tokens
+    # three head-major bf16 copies and one fp32 key-norm per 64-token tile and
+    # head; every sequence padded to 256 tokens, every region to 256 bytes
     p = _params()
     cu = [0, 18144, 63394, 70594]
     got = h.h3attn_workspace_size(_params(num_seqs=3), cu)
     npad = sum(-(-(cu[i + 1] - cu[i]) // 256) * 256 for i in range(3))
-    assert got == 3 * 24 * npad * 128 * 2
+    assert got == 3 * 24 * npad * 128 * 2 + -(-(24 * (npad // 64) * 4) // 256) * 256
     assert h.h3attn_workspace_size(p, [0, 0]) == 256     # empty input is valid; 0 means error
     with pytest.raises(h.H3AttnError):
         h.h3attn_workspace_size(_params(head_dim=80), [0, 10])
