@@ -1,0 +1,84 @@
+"""GPU parity at the edges of the boundary's limits, against the fp64 oracle.
+
+- the largest batch the ABI takes (64 sequences), with ragged lengths from
+  empty through single tokens, audio-only sequences and lengths on 64- and
+  256-token boundaries, through both the bf16 and the quantised path;
+- single-token sequences only (every tile has one valid key);
+- a non-default softmax scale and RMSNorm epsilon.
+
+All rows are compared (the cases are small).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from audio_diffusion_transformer_amd import h3attn as h, synth
+from audio_diffusion_transformer_amd.synth import Seq
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+def _max_batch() -> synth.Workload:
+    rng = np.random.default_rng(2024)
+    seqs = []
+    special = [0, 1, 63, 64, 65, 255, 256, 257]
+    for i in range(h.H3ATTN_MAX_SEQS):
+        if i < len(special):
+            seqs.append(Seq(1, 1, special[i]))
+        elif i % 9 == 0:
+            seqs.append(Seq(0, 1, 1, int(rng.integers(1, 40))))      # audio only
+        else:
+            seqs.append(Seq(1, int(rng.integers(1, 4)), int(rng.integers(1, 60)), int(rng.integers(0, 3)) * 7))
+    return synth.Workload("max_batch_64", H=2, d=128, seqs=tuple(seqs), split=(32, 48, 48),
+                          k_offset_std=0.5, seed=21)
+
+
+def _all_rows(w, inp, out_bits, gate, label, scale=None):
+    p = oracle.Problem.from_workload(w, inp, scale=scale)
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    ref = p.attention_rows(rows, nthreads=G.oracle_threads())
+    G.check(G.metrics(G.gpu_rows(out_bits, rows, w.H), ref), gate, label)
+
+
+@pytest.mark.parametrize("quantized", [False, True])
+def test_largest_batch_of_sequences(torch_dev, quantized):
+    w = _max_batch()
+    assert len(w.seqs) == h.H3ATTN_MAX_SEQS
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized=quantized, label="max_batch_64"))
+    _all_rows(w, inp, out, G.Q8_GATE if quantized else G.BF16_GATE,
+              "max_batch_64" + ("_q8" if quantized else ""))
+
+
+def test_single_token_sequences(torch_dev):
+    w = synth.Workload("single_tokens", H=3, d=128, seqs=tuple(Seq(1, 1, 1) for _ in range(17)),
+                       split=(32, 48, 48), seed=22)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, label="single_tokens"))
+    # one key per sequence: softmax weight 1, so the output is that token's v (to bf16 rounding)
+    v = synth.f32_from_bf16_bits(inp["v"]).astype(np.float64)
+    got = G.decode(out)
+    assert np.abs(got - v).max() <= 2.0 ** -8 * np.abs(v).max()
+    _all_rows(w, inp, out, G.BF16_GATE, "single_tokens")
+
+
+def test_softmax_scale_and_eps(torch_dev):
+    w = synth.Workload("scale_eps", H=2, d=128, seqs=(Seq(3, 9, 10, 30), Seq(2, 5, 7)), split=(32, 48, 48),
+                       eps=1e-3, seed=23)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    scale = 0.05
+    G.announce("scale_eps workload=%s N=%d scale=%g eps=%g" % (w.name, w.N, scale, w.eps))
+    o = h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], eps=w.eps, softmax_scale=scale)
+    torch_dev.cuda.synchronize()
+    _all_rows(w, inp, G.bits(o), G.BF16_GATE, "scale_eps", scale=scale)
