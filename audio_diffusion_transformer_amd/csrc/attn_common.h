@@ -55,7 +55,16 @@ struct TileFill {
             goff[i] = (uint32_t)(row * CPR + ((lane % CPR) ^ swz<CPR>(row))) * 16u;
         }
     }
-    // Tile at byte offset `toff` (wave-uniform) of the buffer `rsrc`.
+    // Piece i (< PER_WAVE) of this wave's share of the tile at byte offset
+    // `toff` (wave-uniform) of the buffer `rsrc`.
+    __device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rsrc, uint32_t toff, void *lds, int wave,
+                                               int i) const
+    {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void *)(static_cast<char *>(lds) + (wave * PER_WAVE + i) * 1024),
+            16, goff[i], toff, 0, 0);
+    }
+    // This wave's whole share at once.
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t toff, void *lds, int wave) const
     {
 #pragma unroll

@@ -459,9 +459,13 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     // next tile (K in kl), one FP8 MFMA of the pending P.V (row sum at chunk 0,
     // channel block db at chunk 2db+1; V of the previous tile in vprev) and P
     // word i of the current tile (raw scores c0s/c1s).  LDS fragments are read
-    // two chunks ahead.
+    // two chunks ahead.  The fills of K tile kj (into kdst) and V tile vj (into
+    // vdst) go out one 1 KB piece per chunk in chunks 0-3 (a negative tile
+    // index skips them), so their issue overlaps the matrix cores.
+    constexpr int KP = decltype(kfill)::PER_WAVE, VP = decltype(vfill)::PER_WAVE;
+    static_assert(KP + VP <= 8, "fill pieces must fit in the step's chunks");
     auto body = [&](const int8_t *kl, const uint8_t *vprev, const i32x16 &c0s, const i32x16 &c1s, float cs,
-                    float c0, i32x16 &n0, i32x16 &n1) {
+                    float c0, i32x16 &n0, i32x16 &n1, int kj, void *kdst, int vj, void *vdst) {
         i32x4 kf[8];
         i32x8 vf[4];
         i32x8 pn;
@@ -471,6 +475,9 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i + 2 < 8) kf[i + 2] = kfrag(kl, i + 2);
+            if (kj >= 0 && i < KP) kfill.load_piece(krs, (uint32_t)(kj * tbytes), kdst, wave, i);
+            else if (vj >= 0 && i >= KP && i < KP + VP)
+                vfill.load_piece(vrs, (uint32_t)(vj * tbytes), vdst, wave, i - KP);
             if (i == 1 || i == 3 || i == 5) vf[(i + 1) >> 1] = vfrag(vprev, (i + 1) >> 1);
             const int st = i >> 1;
             if ((i & 1) == 0)
@@ -511,19 +518,15 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     int j = 0;
     for (; j + 3 < nt; j += 2) {
         const float ks1 = ksc[j + 1];
-        load_k(j + 2, lk0);
-        load_v(j, lv0);
         float cs = cq * ks0;
         float c0 = tile_max(j, cs, sa0, sa1, false, lv1);
-        body(lk1, lv1, sa0, sa1, cs, c0, sb0, sb1);
+        body(lk1, lv1, sa0, sa1, cs, c0, sb0, sb1, j + 2, lk0, j, lv0);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         ks0 = ksc[j + 2];
-        load_k(j + 3, lk1);
-        load_v(j + 1, lv1);
         cs = cq * ks1;
         c0 = tile_max(j + 1, cs, sb0, sb1, false, lv0);
-        body(lk0, lv0, sb0, sb1, cs, c0, sa0, sa1);
+        body(lk0, lv0, sb0, sb1, cs, c0, sa0, sa1, j + 3, lk1, j + 1, lv1);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
     }
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
         load_v(j, (j & 1) ? lv1 : lv0);
         const float cs = cq * ksc[j];
         const float c0 = tile_max(j, cs, sa0, sa1, false, vp);
-        body(((j + 1) & 1) ? lk1 : lk0, vp, sa0, sa1, cs, c0, sb0, sb1);
+        body(((j + 1) & 1) ? lk1 : lk0, vp, sa0, sa1, cs, c0, sb0, sb1, -1, nullptr, -1, nullptr);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         sa0 = sb0;
