@@ -98,6 +98,11 @@ WORKLOADS: Dict[str, Workload] = {
         "joint", H=24, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128,
         k_offset_std=0.5, seed=1003,
         description="joint t31 x h48 x w84 video + 250 audio = 125,242 tokens, H=24, d=128"),
+    "joint_h3": Workload(
+        "joint_h3", H=3, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128,
+        k_offset_std=0.5, seed=1006,
+        description="one GPU's share of the joint workload under 8-way head sharding: "
+                    "125,242 tokens, H=3, d=128"),
     "ragged": Workload(
         "ragged", H=24, d=128,
         seqs=(Seq(14, 36, 36), Seq(25, 30, 60, 250), Seq(8, 30, 30)), split=_SPLIT128,

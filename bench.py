@@ -53,6 +53,35 @@ def measured_traffic(kernel_file: str, summary: str):
     return float(t.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_copy_rate(torch, dev, mib: int = 1024, reps: int = 5) -> float:
+    """GB/s (read + write bytes) of a plain device-to-device copy, the practical
+    rate of mixed HBM traffic the prologue is compared with."""
+    src = torch.empty(mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(w, inputs, seconds: float, threads: int):
     """Time the fp64 CPU oracle on sampled query rows of one head (full key set)."""
     import oracle
@@ -77,10 +106,13 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
     fixed = max(t1 - per_row * probe, 0.0)
     nrows = int(max(probe, min(n, (seconds - fixed) / per_row)))
     t = run(nrows)
+    value = nrows * flops_per_row / t / 1e12
     return {
-        "value": round(nrows * flops_per_row / t / 1e12, 6),
+        "value": round(value, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
+        "extrapolated_full_s": round(w.flops() / (value * 1e12), 1),
         "kind": "oracle",
         "sample": "%d query rows of head %d (of %d x %d rows), each over all %d keys; fp64; "
                   "the keys' RMSNorm+RoPE included; %.1f s" % (nrows, head, w.N, w.H, n, t),
@@ -168,6 +200,8 @@ def main():
     ms_step = total_ms / K
     att_avg = float(np.mean(att_ms))
     pro_avg = float(np.mean(pro_ms))
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    copy_gbps = device_copy_rate(torch, dev)        # after the timed region
     print("[bench] %d steps: %.3f ms/step (attention %.3f, prologue %.3f), wall %.3f s" % (
         K, ms_step, att_avg, pro_avg, wall), file=sys.stderr, flush=True)
 
@@ -188,7 +222,8 @@ def main():
     else:
         # read q, k, v and the table; write qhat, khat and the transposed V copy
         pro_bytes = 3 * N * H * d * 2 + 3 * N * H * d * 2 + N * (d // 2) * 8
-        metric = METRIC if w.name == "joint" else METRIC.replace("N=125k", "N=%d" % N)
+        metric = METRIC if w.name == "joint" else (
+            "attention TFLOP/s and %% of bf16 MFMA peak at N=%d packed tokens, H=%d, d=%d" % (N, H, d))
     res = {
         "metric": metric,
         "value": round(value, 3),
@@ -209,9 +244,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_q8_kernel" if w.quantized else "attn_bf16_kernel<128>",
                      "avg_ms": round(att_avg, 4)},
+        "step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p50": round(float(np.percentile(step_ms, 50)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4)},
         "kernels": {"prologue_avg_ms": round(pro_avg, 4),
                     "prologue_GBps": round(pro_bytes / (pro_avg * 1e-3) / 1e9, 1),
                     "prologue_hbm_frac": round(pro_bytes / (pro_avg * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4),
+                    "device_copy_GBps": round(copy_gbps, 1),
+                    "prologue_copy_frac": round(pro_bytes / (pro_avg * 1e-3) / 1e9 / copy_gbps, 4),
                     "attention_avg_ms": round(att_avg, 4)},
         "cpu_baseline": None,
     }

@@ -76,7 +76,7 @@ def test_prologue_stage_all_rows(torch_dev, name):
             name, "qk"[which], float((err - bound).max()))
 
 
-@pytest.mark.parametrize("name", ["video", "joint", "ragged"])
+@pytest.mark.parametrize("name", ["video", "joint", "ragged", "joint_h3"])
 def test_attention_full_size_sampled_rows(torch_dev, name):
     w = synth.WORKLOADS[name]
     inp = synth.generate(w)
