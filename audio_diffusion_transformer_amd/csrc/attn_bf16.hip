@@ -5,8 +5,8 @@
 // "H3-specific attention backend" the page "H3 Runtime Current State" lists
 // under "Owned Performance Kernels".  It consumes the prologue's head-major
 // qhat / khat and per-tile transposed V, and computes, for each query row,
-// the softmax over the keys of its own sequence with an online (running-max)
-// softmax, never materialising the N x N score matrix.
+// the softmax over the keys of its own sequence tile by tile (an online
+// softmax), never materialising the N x N score matrix.
 //
 // Work decomposition.  One workgroup = 4 waves = 128 query rows of one
 // (sequence, head); each wave owns 32 query rows.  Workgroups are ordered
@@ -30,22 +30,25 @@
 // read.
 //
 // Pipelining.  K and V^T tiles of 64 keys are double-buffered in LDS and
-// filled straight from global memory by global_load_lds_dwordx4 (no staging
-// registers).  K runs one tile ahead of V: iteration j issues the scores of
-// tile j+1 (matrix cores) next to the softmax of tile j (vector ALUs), which
-// do not depend on each other, then the P.V product of tile j; the loads of K
-// tile j+2 and V tile j+1 are in flight meanwhile, and one barrier per tile
-// hands the buffers over.  LDS rows are XOR swizzled at 16-byte granularity so
-// the 16-byte fragment reads of each group of 16 lanes hit distinct banks.
+// filled straight from global memory by buffer_load_dwordx4 ... lds (no
+// staging registers; the buffer descriptor bounds every access).  K runs one
+// tile ahead of V: iteration j issues the scores of tile j+1 (matrix cores)
+// next to the softmax of tile j (vector ALUs), which do not depend on each
+// other, then the P.V product of tile j; the loads of K tile j+2 and V tile
+// j+1 are in flight meanwhile, and one barrier per tile hands the buffers
+// over.  LDS rows are XOR swizzled at 16-byte granularity so the 16-byte
+// fragment reads of each group of 16 lanes hit distinct banks.
 //
-// Online softmax in base 2.  The prologue stores qhat * scale * log2(e), and
-// each score MFMA chain starts from -m instead of 0, where m is the running
-// row maximum (log2 units): the matrix cores deliver x = s*scale*log2(e) - m
-// directly and p = 2^x needs no further VALU work.  m is raised only when a
-// tile's maximum exceeds it by more than 8, so O and l are rescaled (and that
-// tile's x shifted) rarely; p stays below 2^8, well inside bf16 and fp32
-// range.  P is rounded to bf16 for the P.V product and the row sum l adds
-// exactly those rounded values.
+// Softmax in base 2.  The prologue stores qhat * scale * log2(e), and each
+// score MFMA chain starts from -m instead of 0 (the splat -m is held in
+// registers), so the matrix cores deliver x = s*scale*log2(e) - m directly and
+// p = 2^x needs no further VALU work.  m is fixed per row to the bound
+// |qhat'| * max|khat| when that bound is at most 48 (softmax does not depend
+// on the shift; every p <= 1 and none underflows), which needs neither a
+// per-tile row maximum nor a rescale.  Otherwise m is a running maximum raised
+// only when a tile exceeds it by more than 8, so O and l are rescaled rarely
+// and p stays below 2^8.  P is rounded to bf16 for the P.V product and the
+// row sum l adds exactly those rounded values.
 #include "h3_internal.h"
 #include "attn_common.h"
 
