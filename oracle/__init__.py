@@ -86,6 +86,10 @@ def _bind(L):
                                      P(C.c_double), P(C.c_double), P(C.c_double), P(C.c_int8)]
     L.orc_q8_v_quant.argtypes = [P(_Problem), C.c_int32, C.c_int32, P(C.c_double),
                                  P(C.c_double), P(C.c_uint8)]
+    L.orc_q8_softmax_pv.argtypes = [P(C.c_double), C.c_int64, P(C.c_double), C.c_int, P(C.c_double)]
+    L.orc_q8_attention_rows.restype = C.c_int
+    L.orc_q8_attention_rows.argtypes = [P(_Problem), P(C.c_int64), C.c_int64, P(C.c_double),
+                                        P(C.c_double), C.c_int]
     L.orc_e4m3_encode.restype = C.c_uint8
     L.orc_e4m3_encode.argtypes = [C.c_double]
     L.orc_e4m3_decode.restype = C.c_double
@@ -196,6 +200,17 @@ class Problem:
             raise ValueError("oracle: bad quantisation block")
         return scale.value, ratio[:rows], codes[:rows]
 
+    def q8_attention_rows(self, rows, nthreads: int = 0, kmean=None) -> np.ndarray:
+        """Output rows of the quantised path taken step by step (orc_q8_attention_rows)."""
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        km = np.ascontiguousarray(self.q8_kmean(nthreads) if kmean is None else kmean, dtype=np.float64)
+        out = np.zeros((len(rows), self.d), dtype=np.float64)
+        st = self.L.orc_q8_attention_rows(C.byref(self.pr), _ptr(rows, C.c_int64), len(rows),
+                                          _ptr(km, C.c_double), _ptr(out, C.c_double), int(nthreads))
+        if st != 0:
+            raise ValueError("oracle: row outside every sequence")
+        return out
+
     def q8_v_quant(self, seq: int, head: int):
         n = int(self.cu[seq + 1] - self.cu[seq])
         scale = np.zeros(self.d, dtype=np.float64)
@@ -204,6 +219,18 @@ class Problem:
         self.L.orc_q8_v_quant(C.byref(self.pr), int(seq), int(head), _ptr(scale, C.c_double),
                               _ptr(ratio, C.c_double), _ptr(codes, C.c_uint8))
         return scale, ratio[:n], codes[:n]
+
+
+def q8_softmax_pv(x, vdec, library=None) -> np.ndarray:
+    """The quantised path's softmax and P.V for one row: log2-unit scores x [n],
+    decoded V [n, d] (see orc_q8_softmax_pv)."""
+    L = library or lib()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    vdec = np.ascontiguousarray(vdec, dtype=np.float64)
+    n, d = vdec.shape
+    out = np.zeros(d, dtype=np.float64)
+    L.orc_q8_softmax_pv(_ptr(x, C.c_double), n, _ptr(vdec, C.c_double), d, _ptr(out, C.c_double))
+    return out
 
 
 def attention_core(qhat, khat, v, scale: float, library=None) -> np.ndarray:

@@ -27,7 +27,13 @@
  * The quantised-path helpers (orc_q8_*) state the INT8 / FP8 e4m3 quantisers
  * of the block-quantised attention variant by their definitions (symmetric
  * round-to-nearest-even INT8 with one scale per 64-token block, OCP e4m3fn
- * with round-to-nearest-even and saturation at 448).
+ * with round-to-nearest-even and saturation at 448).  orc_q8_softmax_pv and
+ * orc_q8_attention_rows emulate that variant's attention step by step in fp64:
+ * integer dot products of the codes, 64-key tiles in key order, a base-2 running
+ * maximum moved only when a tile's maximum exceeds it by more than 1, e4m3
+ * probabilities 224 * 2^(s - m), and a row sum over those quantised
+ * probabilities.  Each of these is a reading of the page "H3 Runtime Current
+ * State" (the quantised attention it lists), stated where it is used.
  */
 #include <math.h>
 #include <pthread.h>
@@ -467,4 +473,130 @@ int orc_q8_v_quant(const orc_problem *p, int32_t seq, int32_t head, double *scal
             codes_out[j * d + c] = orc_e4m3_encode(r);
         }
     return (int)n;
+}
+
+/* --------------------------------- quantised attention, step by step (fp64) */
+
+/* The quantised path's softmax and P.V for one query row, in the order the
+ * path takes them.  x[j] is key j's score in log2 units (scores of the
+ * quantised codes times their scales, softmax scale and log2 e), vdec [n][d]
+ * the decoded V (e4m3 value times the channel scale).  Keys are taken in
+ * tiles of 64.  A running maximum m starts at the first tile's maximum; a
+ * later tile moves it to that tile's maximum only when that exceeds m by more
+ * than 1, and then the sums so far are scaled by 2^(m_old - m_new).  Each
+ * key's probability is quantised as P = e4m3(224 * 2^(x - m)) (so P <= 448),
+ * O += P v and l += P (the sum of the quantised P), and o = O / l. */
+void orc_q8_softmax_pv(const double *x, int64_t n, const double *vdec, int d, double *out)
+{
+    double m = 0.0, l = 0.0;
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t t0 = 0; t0 < n; t0 += 64) {
+        int64_t t1 = t0 + 64 < n ? t0 + 64 : n;
+        double mx = -INFINITY;
+        for (int64_t j = t0; j < t1; ++j) if (x[j] > mx) mx = x[j];
+        if (t0 == 0) {
+            m = mx;
+        } else if (mx - m > 1.0) {
+            double alpha = exp2(m - mx);
+            l *= alpha;
+            for (int c = 0; c < d; ++c) out[c] *= alpha;
+            m = mx;
+        }
+        for (int64_t j = t0; j < t1; ++j) {
+            double P = orc_e4m3_decode(orc_e4m3_encode(224.0 * exp2(x[j] - m)));
+            l += P;
+            for (int c = 0; c < d; ++c) out[c] += P * vdec[j * d + c];
+        }
+    }
+    for (int c = 0; c < d; ++c) out[c] = n > 0 ? out[c] / l : 0.0;
+}
+
+typedef struct {
+    const orc_problem *p;
+    int32_t seq, head;
+    int64_t n;                 /* keys of the sequence */
+    const int64_t *rows;       /* the rows of this (seq, head) */
+    const int8_t *qcodes;      /* [n][d]: codes of the query blocks that are needed */
+    const double *qscale;      /* [n/64 rounded up] */
+    const int8_t *kcodes;      /* [n][d] */
+    const double *kscale;      /* [n/64 rounded up] */
+    const double *vdec;        /* [n][d] */
+    double *out;               /* [rows][d] */
+} q8row_ctx;
+
+static void q8row_body(void *c, int64_t i)
+{
+    q8row_ctx *x = c;
+    const orc_problem *p = x->p;
+    int d = p->d;
+    int64_t qi = x->rows[i] / p->H - p->cu[x->seq];
+    const int8_t *q = x->qcodes + qi * d;
+    double qs = x->qscale[qi / 64] * p->scale / log(2.0);
+    double *s = malloc(sizeof(double) * (x->n > 0 ? x->n : 1));
+    for (int64_t j = 0; j < x->n; ++j) {
+        int64_t dot = 0;
+        for (int cc = 0; cc < d; ++cc) dot += (int64_t)q[cc] * x->kcodes[j * d + cc];
+        s[j] = (double)dot * qs * x->kscale[j / 64];
+    }
+    orc_q8_softmax_pv(s, x->n, x->vdec, d, x->out + i * d);
+    free(s);
+}
+
+/* Output rows (token * H + head) of the quantised path, taken step by step:
+ * the K mean of each sequence and head (orc_q8_kmean), INT8 codes of qhat and
+ * of khat - mean per 64-token block (orc_q8_block_quant), FP8 codes of v with
+ * one scale per channel (orc_q8_v_quant), the exact integer score of the codes
+ * times both block scales, the softmax scale and log2 e, then
+ * orc_q8_softmax_pv.  kmean is [S][H][d] from orc_q8_kmean.  Rows are
+ * processed one (sequence, head) at a time; returns -1 for a row outside every
+ * sequence. */
+int orc_q8_attention_rows(const orc_problem *p, const int64_t *rows, int64_t nrows, const double *kmean,
+                          double *out, int nthreads)
+{
+    int d = p->d;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t tok = rows[i] / p->H;
+        if (tok < 0 || tok >= p->cu[p->S]) return -1;
+    }
+    int64_t *sel = malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
+    int64_t *pos = malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
+    for (int32_t s = 0; s < p->S; ++s) {
+        int64_t n = p->cu[s + 1] - p->cu[s];
+        if (n == 0) continue;
+        int64_t nb = (n + 63) / 64;
+        for (int32_t h = 0; h < p->H; ++h) {
+            int64_t m = 0;
+            for (int64_t i = 0; i < nrows; ++i) {
+                int64_t tok = rows[i] / p->H;
+                if (rows[i] % p->H == h && tok >= p->cu[s] && tok < p->cu[s + 1]) {
+                    sel[m] = rows[i];
+                    pos[m] = i;
+                    ++m;
+                }
+            }
+            if (m == 0) continue;
+            int8_t *kc = malloc((size_t)n * d), *qc = calloc((size_t)n * d, 1);
+            uint8_t *vc = malloc((size_t)n * d);
+            double *ks = malloc(sizeof(double) * nb), *qs = calloc(nb, sizeof(double));
+            double *ratio = malloc(sizeof(double) * (size_t)n * d), *vsc = malloc(sizeof(double) * d);
+            double *vdec = malloc(sizeof(double) * (size_t)n * d);
+            char *need = calloc(nb, 1);
+            for (int64_t b = 0; b < nb; ++b)
+                orc_q8_block_quant(p, 1, s, h, (int32_t)b, kmean, &ks[b], ratio, kc + b * 64 * d);
+            for (int64_t i = 0; i < m; ++i) need[(sel[i] / p->H - p->cu[s]) / 64] = 1;
+            for (int64_t b = 0; b < nb; ++b)
+                if (need[b]) orc_q8_block_quant(p, 0, s, h, (int32_t)b, kmean, &qs[b], ratio, qc + b * 64 * d);
+            orc_q8_v_quant(p, s, h, vsc, ratio, vc);
+            for (int64_t j = 0; j < n; ++j)
+                for (int c = 0; c < d; ++c) vdec[j * d + c] = orc_e4m3_decode(vc[j * d + c]) * vsc[c];
+            double *o = malloc(sizeof(double) * (size_t)m * d);
+            q8row_ctx ctx = {p, s, h, n, sel, qc, qs, kc, ks, vdec, o};
+            parallel_for(m, nthreads, q8row_body, &ctx);
+            for (int64_t i = 0; i < m; ++i) memcpy(out + pos[i] * d, o + i * d, sizeof(double) * d);
+            free(o); free(kc); free(qc); free(vc); free(ks); free(qs); free(ratio); free(vsc); free(vdec); free(need);
+        }
+    }
+    free(sel);
+    free(pos);
+    return 0;
 }

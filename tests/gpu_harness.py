@@ -78,6 +78,12 @@ SHARP_GATE = dict(max_abs=6e-2, mean_abs=6e-3, rel_l2=1.5e-2, cosine=0.9999)
 # measured error (rel-L2 0.034-0.039, cosine >= 0.9992 on every case) plus margin;
 # an all-zero output (rel-L2 1) or a dropped V scale would fail them.
 Q8_GATE = dict(mean_abs=2e-2, rel_l2=0.06, cosine=0.998)
+# Quantised path against the oracle's step-by-step emulation of it (same codes,
+# scales, tiles, lazy maximum and e4m3 probabilities): what is left is the fp32
+# arithmetic, the bf16 output rounding (unit roundoff 2^-9) and the odd code that
+# fp32 rounds across a boundary.  Measured: rel-L2 0.0024-0.0026 (against 0.034-0.039
+# for the exact oracle), cosine >= 0.999996, max-abs <= 0.016; the gate is twice that.
+Q8_EMULATION_GATE = dict(max_abs=4e-2, mean_abs=1e-3, rel_l2=5e-3, cosine=0.99999)
 
 
 def check(m: Dict[str, float], gate: Dict[str, float], label: str):

@@ -49,6 +49,12 @@ MUTANTS = {
     "e4m3_subnormal_step": ("double q = nearbyint(a / ldexp(1.0, -9));", "double q = nearbyint(a / ldexp(1.0, -10));"),
     "v_scale_fnuz_max": ("scale_out[c] = amax > 0 ? amax / 448.0 : 1.0;",
                          "scale_out[c] = amax > 0 ? amax / 240.0 : 1.0;"),
+    "q8_rescale_on_any_rise": ("} else if (mx - m > 1.0) {", "} else if (mx - m > 0.0) {"),
+    "q8_rowsum_unquantised": ("            l += P;\n", "            l += 224.0 * exp2(x[j] - m);\n"),
+    "q8_p_scale_448": ("orc_e4m3_encode(224.0 * exp2(x[j] - m))", "orc_e4m3_encode(448.0 * exp2(x[j] - m))"),
+    "q8_score_natural_log": ("x->qscale[qi / 64] * p->scale / log(2.0)", "x->qscale[qi / 64] * p->scale"),
+    "q8_first_block_kscale": ("s[j] = (double)dot * qs * x->kscale[j / 64];",
+                              "s[j] = (double)dot * qs * x->kscale[0];"),
 }
 
 

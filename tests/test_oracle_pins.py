@@ -394,3 +394,55 @@ def test_int8_quantiser_ties_to_even():
     assert scale == 1.0 / 32
     np.testing.assert_array_equal(ratio[0], row)
     np.testing.assert_array_equal(codes[0, :7], [127, 2, -4, 0, 2, 15, 3])
+
+
+# ------------------------------------------- quantised attention, step by step
+
+def _expand(spec, n, width=None):
+    """{"index": value, ..., "default": value} -> array of n entries."""
+    default = spec["default"]
+    out = np.array([spec.get(str(i), default) for i in range(n)], dtype=np.float64)
+    return out
+
+
+def test_q8_softmax_pv_constant_value_returns_it():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(200) * 4
+    v = np.tile(np.array([0.5, -3.0, 7.25]), (200, 1))
+    np.testing.assert_allclose(oracle.q8_softmax_pv(x, v, library=L()), v[0], rtol=1e-13)
+
+
+def test_q8_softmax_pv_single_key_and_equal_scores():
+    v = np.array([[1.5, -2.0, 4.0]])
+    np.testing.assert_allclose(oracle.q8_softmax_pv(np.array([3.7]), v, library=L()), v[0], rtol=1e-14)
+    # equal scores: every P is 224, so the output is the plain mean
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((130, 4))
+    out = oracle.q8_softmax_pv(np.full(130, 0.3), v, library=L())
+    np.testing.assert_allclose(out, v.mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_q8_softmax_pv_golden_lazy_rescale_and_ties():
+    with open(os.path.join(GOLDEN, "q8_softmax_pv.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        n = c["n"]
+        x = _expand(c["x"], n)
+        vd = c["v"]["default"]
+        v = np.array([c["v"].get(str(i), vd) for i in range(n)], dtype=np.float64)
+        got = oracle.q8_softmax_pv(x, v, library=L())
+        np.testing.assert_allclose(got, c["expected"], rtol=1e-13, err_msg=c["name"])
+
+
+def test_q8_rows_track_exact_attention():
+    """The step-by-step quantised path stays within the quantised tolerance of
+    exact attention (a sanity check of its scaling; the exact error is the
+    quantisation's own)."""
+    p = _problem([(2, 5, 7, 9), (1, 3, 4, 0)], H=2, d=32, split=(8, 12, 12), seed=8)
+    rows = _all_rows(p)
+    q8 = p.q8_attention_rows(rows)
+    ex = p.attention_rows(rows)
+    err = np.abs(q8 - ex)
+    rel_l2 = np.linalg.norm(q8 - ex) / np.linalg.norm(ex)
+    assert err.mean() < 2e-2 and rel_l2 < 0.06, (err.mean(), rel_l2)
+    assert np.corrcoef(q8.ravel(), ex.ravel())[0, 1] > 0.998
