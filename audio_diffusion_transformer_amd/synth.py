@@ -13,6 +13,10 @@ Q10) describe these packed sequences but publish no tensors, so every value is
 drawn here: Q/K/V ~ N(0, 1) rounded once to bf16 (round to nearest even),
 RMSNorm weights 1 + 0.1 N(0, 1) in fp32, and for the joint workload a
 per-(head, channel) mean offset N(0, 0.5^2) added to raw K before rounding.
+Workloads with a model dimension D start one step earlier, at the attention
+layer's input: hidden states x ~ N(0, 1) [N, D] and a QKV weight
+W ~ N(0, 1/D) [3*H*d, D], both rounded once to bf16, so the projected q, k, v
+have unit variance like the direct inputs (the pages publish no weights).
 
 Random streams come from numpy's Philox counter-based generator, one
 independent child stream per tensor (``SeedSequence.spawn``).
@@ -58,6 +62,7 @@ class Workload:
     seed: int = 0
     quantized: bool = False
     sharp: bool = False                  # diagnostic: per-token scale + larger weights
+    model_dim: int = 0                   # D > 0: inputs are hidden states x [N, D] and W_qkv
     description: str = ""
 
     @property
@@ -76,6 +81,10 @@ class Workload:
     def flops(self) -> float:
         """Attention FLOP count 4 * sum(n_i^2) * d * H (QK^T and PV, exps excluded)."""
         return 4.0 * sum(float(s.n) ** 2 for s in self.seqs) * self.d * self.H
+
+    def proj_flops(self) -> float:
+        """QKV projection FLOP count 2 * N * D * 3*H*d (0 without a model dimension)."""
+        return 2.0 * self.N * self.model_dim * 3 * self.H * self.d
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -112,6 +121,18 @@ WORKLOADS: Dict[str, Workload] = {
         "q8", H=24, d=128, seqs=(Seq(36, 30, 54),), split=_SPLIT128, seed=1005,
         quantized=True,
         description="INT8-QK / FP8-PV path at the 58,320-token video shape"),
+    "proj_tiny": Workload(
+        "proj_tiny", H=2, d=64, seqs=(Seq(4, 8, 8),), split=(16, 24, 24), seed=1011, model_dim=128,
+        description="QKV projection (D=128) + attention on the t4 x h8 x w8 grid, H=2, d=64"),
+    "proj_joint": Workload(
+        "proj_joint", H=24, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128, seed=1013,
+        model_dim=3072,
+        description="QKV projection (D=3072) + attention on the joint 125,242-token sequence, H=24"),
+    "proj_joint_h3": Workload(
+        "proj_joint_h3", H=3, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128, seed=1016,
+        model_dim=3072,
+        description="one GPU's share of proj_joint under 8-way head sharding: full hidden states "
+                    "x [125242, 3072], the 3 heads' rows of W"),
 }
 
 
@@ -148,11 +169,26 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
     Returns q, k, v as uint16 bf16 bits of shape [N, H, d] (token-major,
     token stride H*d), norm_w float32 [2, H, d] (q weights then k weights),
     k_offset float32 [H, d] (zeros when unused) and cu_seqlens int32 [S+1].
+    With a model dimension D the inputs are instead x (bf16 bits [N, D]) and
+    w_qkv (bf16 bits [3*H*d, D]); q, k and v are then not drawn.
     """
     ss = np.random.SeedSequence(w.seed)
-    kids = ss.spawn(8)
+    kids = ss.spawn(10)
     gen = [np.random.Generator(np.random.Philox(k)) for k in kids]
     N, H, d = w.N, w.H, w.d
+    if w.model_dim > 0:
+        if w.sharp or w.k_offset_std > 0:
+            raise ValueError("projection workloads draw plain hidden states")
+        D = w.model_dim
+        x = _normal_bf16(gen[8], (N, D))
+        w_qkv = np.empty((3 * H * d, D), dtype=np.uint16)
+        for r0 in range(0, 3 * H * d, 1024):
+            r1 = min(3 * H * d, r0 + 1024)
+            w_qkv[r0:r1] = bf16_bits_from_f32(
+                gen[9].standard_normal((r1 - r0, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(D)))
+        norm_w = (1.0 + 0.1 * gen[3].standard_normal((2, H, d))).astype(np.float32)
+        return {"x": x, "w_qkv": w_qkv, "norm_w": norm_w, "k_offset": np.zeros((H, d), dtype=np.float32),
+                "cu_seqlens": w.cu_seqlens()}
     k_offset = np.zeros((H, d), dtype=np.float32)
     if w.k_offset_std > 0:
         k_offset = (gen[4].standard_normal((H, d)) * w.k_offset_std).astype(np.float32)

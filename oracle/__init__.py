@@ -49,7 +49,9 @@ class _Problem(C.Structure):
                 ("q", C.POINTER(C.c_uint16)), ("k", C.POINTER(C.c_uint16)),
                 ("v", C.POINTER(C.c_uint16)),
                 ("q_stride", C.c_int64), ("k_stride", C.c_int64), ("v_stride", C.c_int64),
-                ("norm_w", C.POINTER(C.c_float))]
+                ("norm_w", C.POINTER(C.c_float)),
+                ("qf", C.POINTER(C.c_double)), ("kf", C.POINTER(C.c_double)),
+                ("vf", C.POINTER(C.c_double))]
 
 
 _lib = None
@@ -74,6 +76,7 @@ def _bind(L):
     L.orc_token_pos.argtypes = [P(_Problem), C.c_int64, P(C.c_int32), P(C.c_int32), P(C.c_int32)]
     L.orc_rope_angles.argtypes = [P(_Problem), C.c_int32, P(C.c_int32), P(C.c_double)]
     L.orc_rmsnorm.argtypes = [P(C.c_uint16), P(C.c_float), C.c_int, C.c_double, P(C.c_double)]
+    L.orc_rmsnorm_f64.argtypes = [P(C.c_double), P(C.c_float), C.c_int, C.c_double, P(C.c_double)]
     L.orc_rope_rotate.argtypes = [P(C.c_double), P(C.c_double), C.c_int, P(C.c_double)]
     L.orc_prologue_rows.argtypes = [P(_Problem), C.c_int, P(C.c_int64), C.c_int64,
                                     P(C.c_double), C.c_int]
@@ -105,8 +108,9 @@ class Problem:
     """One oracle problem; keeps the numpy buffers it points into alive.
 
     ``seqs`` is a list of (T, Hg, Wg, n_audio); q, k, v are uint16 bf16 bits
-    [N, H, d] (any token stride is taken from the array's first stride);
-    norm_w is float32 [2, H, d].
+    [N, H, d] or float64 values [N, H, d] (the fp64 outputs of a QKV
+    projection, see ``project``); any token stride is taken from the array's
+    first stride.  norm_w is float32 [2, H, d].
     """
 
     def __init__(self, H: int, d: int, seqs: Sequence, split, q, k, v, norm_w,
@@ -132,15 +136,18 @@ class Problem:
         pr.theta, pr.eps, pr.scale = float(theta), float(eps), self.scale
         pr.cu = _ptr(self.cu, C.c_int32)
         pr.seqs = self._seqs
-        pr.q, pr.k, pr.v = (_ptr(x, C.c_uint16) for x in (self.q, self.k, self.v))
-        pr.q_stride, pr.k_stride, pr.v_stride = (x.strides[0] // 2 for x in (self.q, self.k, self.v))
+        bits = [x if x.dtype == np.uint16 else None for x in (self.q, self.k, self.v)]
+        vals = [x if x.dtype == np.float64 else None for x in (self.q, self.k, self.v)]
+        pr.q, pr.k, pr.v = (_ptr(x, C.c_uint16) if x is not None else None for x in bits)
+        pr.qf, pr.kf, pr.vf = (_ptr(x, C.c_double) if x is not None else None for x in vals)
+        pr.q_stride, pr.k_stride, pr.v_stride = (x.strides[0] // x.itemsize for x in (self.q, self.k, self.v))
         pr.norm_w = _ptr(self.norm_w, C.c_float)
         self.pr = pr
 
     def _prep(self, x):
         x = np.asarray(x)
-        assert x.dtype == np.uint16 and x.ndim == 3 and x.shape[1:] == (self.H, self.d)
-        if x.strides[1] != self.d * 2 or x.strides[2] != 2:
+        assert x.dtype in (np.uint16, np.float64) and x.ndim == 3 and x.shape[1:] == (self.H, self.d)
+        if x.strides[1] != self.d * x.itemsize or x.strides[2] != x.itemsize:
             x = np.ascontiguousarray(x)
         return x
 
@@ -148,6 +155,18 @@ class Problem:
     def from_workload(cls, w, inputs, **kw):
         return cls(w.H, w.d, w.seqs, w.split, inputs["q"], inputs["k"], inputs["v"],
                    inputs["norm_w"], theta=w.theta, eps=w.eps, **kw)
+
+    @classmethod
+    def from_projection(cls, w, inputs, proj=None, **kw):
+        """The problem whose q, k, v are the fp64 QKV projection of the
+        hidden states inputs["x"] by inputs["w_qkv"] (``project``); ``proj``
+        may pass that projection in when it is already computed."""
+        if proj is None:
+            proj = project(inputs["x"], inputs["w_qkv"])
+        hd = w.H * w.d
+        assert proj.shape == (w.N, 3 * hd)
+        q, k, v = (proj[:, i * hd:(i + 1) * hd].reshape(w.N, w.H, w.d) for i in range(3))
+        return cls(w.H, w.d, w.seqs, w.split, q, k, v, inputs["norm_w"], theta=w.theta, eps=w.eps, **kw)
 
     # -- queries -----------------------------------------------------------
     def attention_rows(self, rows, nthreads: int = 0) -> np.ndarray:
@@ -231,6 +250,34 @@ def q8_softmax_pv(x, vdec, library=None) -> np.ndarray:
     out = np.zeros(d, dtype=np.float64)
     L.orc_q8_softmax_pv(_ptr(x, C.c_double), n, _ptr(vdec, C.c_double), d, _ptr(out, C.c_double))
     return out
+
+
+def project(x_bits, w_bits, rows=None, chunk: int = 8192) -> np.ndarray:
+    """QKV projection of hidden states: y[t, f] = sum_c x[t, c] * W[f, c].
+
+    The attention layer's input projection that the page "H3 Runtime Current
+    State" names ("attention QKV" under its tensor-parallel GEMMs) and that the
+    GEMM share in question 4 of "Buyer Questions: Current Evidence Status"
+    measures; the pages print no formula, so this is the textbook linear map
+    without bias, W in the [out_features, in_features] layout with the q, k and
+    v features in that order, each head-major.  x: uint16 bf16 bits [N, D];
+    W: uint16 bf16 bits [F, D]; the result is fp64 [len(rows) or N, F].  Every
+    product of two bf16 values is exact in fp64; the matrix product (numpy's,
+    a library primitive) sums them in fp64.
+    """
+    x = np.asarray(x_bits)
+    wt = np.asarray(w_bits)
+    assert x.dtype == np.uint16 and wt.dtype == np.uint16 and x.shape[1] == wt.shape[1]
+    wf = _bf16_bits_to_f64(wt).T.copy()
+    idx = np.arange(x.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((len(idx), wt.shape[0]), dtype=np.float64)
+    for i0 in range(0, len(idx), chunk):
+        out[i0:i0 + chunk] = _bf16_bits_to_f64(x[idx[i0:i0 + chunk]]) @ wf
+    return out
+
+
+def _bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def attention_core(qhat, khat, v, scale: float, library=None) -> np.ndarray:

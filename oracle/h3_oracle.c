@@ -58,6 +58,10 @@ typedef struct {
     const uint16_t *q, *k, *v;  /* bf16 bits */
     int64_t q_stride, k_stride, v_stride;   /* elements between tokens */
     const float *norm_w;        /* [2][H][d]: q weights then k weights */
+    /* fp64 rows used in place of the bf16 q, k, v when non-NULL (same token
+     * strides): the outputs of the QKV projection, which the fused projection
+     * path never rounds before the norm (q, k) or before storing (v). */
+    const double *qf, *kf, *vf;
 } orc_problem;
 
 /* ------------------------------------------------------------------ basics */
@@ -127,16 +131,22 @@ void orc_rope_angles(const orc_problem *p, int32_t is_audio, const int32_t pos[3
     }
 }
 
-/* RMSNorm of one row of d bf16 values with weights w. */
-void orc_rmsnorm(const uint16_t *x, const float *w, int d, double eps, double *y)
+/* RMSNorm of one row of d values with weights w. */
+void orc_rmsnorm_f64(const double *x, const float *w, int d, double eps, double *y)
 {
     double ss = 0.0;
-    for (int c = 0; c < d; ++c) {
-        double xc = orc_bf16_to_f64(x[c]);
-        ss += xc * xc;
-    }
+    for (int c = 0; c < d; ++c) ss += x[c] * x[c];
     double r = 1.0 / sqrt(ss / d + eps);
-    for (int c = 0; c < d; ++c) y[c] = orc_bf16_to_f64(x[c]) * r * (double)w[c];
+    for (int c = 0; c < d; ++c) y[c] = x[c] * r * (double)w[c];
+}
+
+/* The same for a row of d bf16 values. */
+void orc_rmsnorm(const uint16_t *x, const float *w, int d, double eps, double *y)
+{
+    double *xf = malloc(sizeof(double) * d);
+    for (int c = 0; c < d; ++c) xf[c] = orc_bf16_to_f64(x[c]);
+    orc_rmsnorm_f64(xf, w, d, eps, y);
+    free(xf);
 }
 
 /* Rotate interleaved pairs (2j, 2j+1) of x by phi[j]. */
@@ -157,12 +167,15 @@ static int prologue_one(const orc_problem *p, int which, int64_t token, int head
     int32_t s, is_audio, pos[3];
     orc_token_pos(p, token, &s, &is_audio, pos);
     if (s < 0) return -1;
-    const uint16_t *x = which == 0 ? p->q + token * p->q_stride + (int64_t)head * d
-                                   : p->k + token * p->k_stride + (int64_t)head * d;
+    const int64_t at = token * (which == 0 ? p->q_stride : p->k_stride) + (int64_t)head * d;
+    const double *xf = which == 0 ? p->qf : p->kf;
     const float *w = p->norm_w + ((int64_t)which * p->H + head) * d;
     double *nrm = malloc(sizeof(double) * d);
     double *phi = malloc(sizeof(double) * (d / 2));
-    orc_rmsnorm(x, w, d, p->eps, nrm);
+    if (xf)
+        orc_rmsnorm_f64(xf + at, w, d, p->eps, nrm);
+    else
+        orc_rmsnorm((which == 0 ? p->q : p->k) + at, w, d, p->eps, nrm);
     orc_rope_angles(p, is_audio, pos, phi);
     orc_rope_rotate(nrm, phi, d, out);
     free(nrm);
@@ -290,8 +303,9 @@ static void key_body(void *c, int64_t j)
     const orc_problem *p = x->p;
     int64_t tok = p->cu[x->s] + j;
     if (prologue_one(p, 1, tok, x->head, x->khat + j * p->d)) x->status = -1;
-    const uint16_t *vr = p->v + tok * p->v_stride + (int64_t)x->head * p->d;
-    for (int c = 0; c < p->d; ++c) x->vv[j * p->d + c] = orc_bf16_to_f64(vr[c]);
+    const int64_t at = tok * p->v_stride + (int64_t)x->head * p->d;
+    for (int c = 0; c < p->d; ++c)
+        x->vv[j * p->d + c] = p->vf ? p->vf[at + c] : orc_bf16_to_f64(p->v[at + c]);
 }
 
 static void row_body(void *c, int64_t i)
@@ -457,6 +471,7 @@ int orc_q8_v_quant(const orc_problem *p, int32_t seq, int32_t head, double *scal
 {
     int d = p->d;
     int64_t n = p->cu[seq + 1] - p->cu[seq];
+    if (p->vf) return -1;   /* the quantised path takes bf16 v only */
     for (int c = 0; c < d; ++c) {
         double amax = 0.0;
         for (int64_t j = 0; j < n; ++j) {

@@ -53,6 +53,9 @@ MUTANTS = {
     "q8_rowsum_unquantised": ("            l += P;\n", "            l += 224.0 * exp2(x[j] - m);\n"),
     "q8_p_scale_448": ("orc_e4m3_encode(224.0 * exp2(x[j] - m))", "orc_e4m3_encode(448.0 * exp2(x[j] - m))"),
     "q8_score_natural_log": ("x->qscale[qi / 64] * p->scale / log(2.0)", "x->qscale[qi / 64] * p->scale"),
+    "projected_k_from_q": ("const double *xf = which == 0 ? p->qf : p->kf;",
+                           "const double *xf = which == 0 ? p->qf : p->qf;"),
+    "projected_v_channel": ("p->vf ? p->vf[at + c] :", "p->vf ? p->vf[at + (c ^ 1)] :"),
     "q8_first_block_kscale": ("s[j] = (double)dot * qs * x->kscale[j / 64];",
                               "s[j] = (double)dot * qs * x->kscale[0];"),
 }

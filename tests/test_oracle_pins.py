@@ -446,3 +446,68 @@ def test_q8_rows_track_exact_attention():
     rel_l2 = np.linalg.norm(q8 - ex) / np.linalg.norm(ex)
     assert err.mean() < 2e-2 and rel_l2 < 0.06, (err.mean(), rel_l2)
     assert np.corrcoef(q8.ravel(), ex.ravel())[0, 1] > 0.998
+
+
+# ---------------------------------------------------------- QKV projection
+
+def test_projection_matches_exact_sums():
+    # every product of two bf16 values is exact in fp64; math.fsum rounds their sum once
+    rng = np.random.default_rng(40)
+    x = _bf16(rng.standard_normal((5, 48)))
+    w = _bf16(rng.standard_normal((7, 48)) * 0.2)
+    got = oracle.project(x, w)
+    xf, wf = _f(x), _f(w)
+    for t in range(5):
+        for f in range(7):
+            terms = [xf[t, c] * wf[f, c] for c in range(48)]
+            assert abs(got[t, f] - math.fsum(terms)) <= 1e-14 * sum(abs(a) for a in terms)
+    assert np.array_equal(oracle.project(x, w, rows=[3, 1]), got[[3, 1]])
+
+
+def _permutation_projection(seed=41, H=2, d=16):
+    """A workload whose QKV weight is three different channel permutations
+    (entries exactly 1), so q, k and v are exact copies of permuted x."""
+    rng = np.random.default_rng(seed)
+    D = H * d
+    w = synth.Workload("perm", H=H, d=d, seqs=(synth.Seq(2, 3, 4, 5), synth.Seq(1, 2, 2)),
+                       split=(4, 6, 6), model_dim=D)
+    x = _bf16(rng.standard_normal((w.N, D)))
+    perms = [rng.permutation(D) for _ in range(3)]
+    wq = np.zeros((3 * D, D), dtype=np.uint16)
+    for i, pm in enumerate(perms):
+        wq[i * D + np.arange(D), pm] = 0x3F80          # bf16 1.0
+    nw = (1 + 0.1 * rng.standard_normal((2, H, d))).astype(np.float32)
+    direct = [x[:, pm].reshape(w.N, H, d) for pm in perms]
+    return w, {"x": x, "w_qkv": wq, "norm_w": nw}, direct
+
+
+def test_projection_with_permutation_weights_equals_direct_inputs():
+    # pins the fp64-input path, the q | k | v order of the features and their
+    # head-major layout against the bf16 path fed the same values directly
+    w, inp, direct = _permutation_projection()
+    pp = oracle.Problem.from_projection(w, inp, library=L())
+    pd = oracle.Problem(w.H, w.d, w.seqs, w.split, *direct, inp["norm_w"], library=L())
+    rows = np.arange(w.N * w.H)
+    for which in (0, 1):
+        np.testing.assert_array_equal(pp.prologue_rows(which, rows), pd.prologue_rows(which, rows))
+    np.testing.assert_array_equal(pp.attention_rows(rows), pd.attention_rows(rows))
+
+
+def test_projection_scale_leaves_qk_and_scales_output():
+    # W -> 2W (exact in bf16): RMSNorm removes the factor from q and k, v doubles,
+    # so the attention output doubles
+    rng = np.random.default_rng(42)
+    w = synth.Workload("scale", H=2, d=16, seqs=(synth.Seq(2, 3, 3, 4),), split=(4, 6, 6),
+                       model_dim=64, eps=1e-12)
+    x = _bf16(rng.standard_normal((w.N, 64)))
+    wq = _bf16(rng.standard_normal((96, 64)) * 0.125)
+    w2 = _bf16(2.0 * _f(wq))
+    nw = (1 + 0.1 * rng.standard_normal((2, 2, 16))).astype(np.float32)
+    rows = np.arange(w.N * w.H)
+    p1 = oracle.Problem.from_projection(w, {"x": x, "w_qkv": wq, "norm_w": nw}, library=L())
+    p2 = oracle.Problem.from_projection(w, {"x": x, "w_qkv": w2, "norm_w": nw}, library=L())
+    for which in (0, 1):
+        np.testing.assert_allclose(p2.prologue_rows(which, rows), p1.prologue_rows(which, rows),
+                                   rtol=0, atol=1e-10)
+    o1 = p1.attention_rows(rows)
+    np.testing.assert_allclose(p2.attention_rows(rows), 2.0 * o1, rtol=0, atol=1e-10 * np.abs(o1).max())
