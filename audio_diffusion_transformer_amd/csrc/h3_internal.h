@@ -125,12 +125,37 @@ struct Q8ExportArgs {
     SeqTable seq;
 };
 
+// Fused QKV projection + RMSNorm + RoPE + layout (qkv_proj.hip).  x is bf16
+// [N][D] (token stride x_stride), w is bf16 [3*H*d][D] with the q, k and v
+// output features in that order, each head-major.  The outputs are those of
+// the prologue: qhat, khat [H][Npad][d] (qhat times q_mult), vt per 64-key
+// tile, knorm per tile; with `natural` set they are instead qhat, khat and the
+// projected v at packed tokens, [N][H][d], padding skipped.
+struct ProjArgs {
+    const uint16_t *x, *w;
+    int64_t x_stride;            // elements between tokens of x
+    int32_t model_dim;           // D, a multiple of 32
+    const float *norm_w, *rope;
+    uint16_t *qhat, *khat, *vt;
+    float *knorm;
+    int64_t out_hstride, out_tstride;
+    int32_t natural;
+    int32_t H;
+    int64_t Npad;
+    int32_t ntiles;              // Npad / 64
+    int32_t nblk;                // Npad / 256 token blocks
+    float eps;
+    float q_mult;
+    SeqTable seq;
+};
+
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_prologue(const PrologueArgs &a, int d, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_t st);
 hipError_t launch_q8_prep(const Q8Args &a, int d, hipStream_t st);
 hipError_t launch_attn_q8(const Q8AttnArgs &a, int d, int64_t nitems, hipStream_t st);
 hipError_t launch_q8_export(const Q8ExportArgs &a, hipStream_t st);
+hipError_t launch_qkv_proj(const ProjArgs &a, int d, hipStream_t st);
 
 // Queries per workgroup of the attention kernels (work-item granularity).
 constexpr int kBlockM = 128;

@@ -322,6 +322,128 @@ h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void 
     return hip_status(launch_prologue(pa, pl.d, static_cast<hipStream_t>(stream)), "prologue launch");
 }
 
+// Checks of the projection entry points' own arguments; fills the plan.  The
+// q/k/v strides of the params are not read by these entry points.
+static h3attn_status proj_plan(const h3attn_params *p, int32_t model_dim, int64_t x_stride,
+                               const int32_t *cu, Plan &pl)
+{
+    if (!p) return fail(H3ATTN_ERR_INVALID_ARG, "params is NULL");
+    h3attn_params pp = *p;
+    pp.q_stride = pp.k_stride = pp.v_stride = (int64_t)p->num_heads * p->head_dim;
+    h3attn_status st = make_plan(&pp, cu, &pl);
+    if (st != H3ATTN_OK) return st;
+    if (model_dim < 32 || model_dim % 32)
+        return fail(H3ATTN_ERR_INVALID_ARG, "model_dim must be a positive multiple of 32 (got %d)", model_dim);
+    if (x_stride < model_dim || x_stride % 8)
+        return fail(H3ATTN_ERR_INVALID_ARG, "x_stride %lld must be >= model_dim %d and a multiple of 8",
+                    (long long)x_stride, model_dim);
+    // 32-bit buffer offsets: one 256-token block of x, one head's rows of W
+    if ((int64_t)255 * x_stride * 2 + (int64_t)model_dim * 2 >= ((int64_t)1 << 31))
+        return fail(H3ATTN_ERR_UNSUPPORTED, "x_stride %lld is too large", (long long)x_stride);
+    if ((int64_t)pl.d * model_dim * 2 >= ((int64_t)1 << 31))
+        return fail(H3ATTN_ERR_UNSUPPORTED, "model_dim %d is too large", model_dim);
+    return H3ATTN_OK;
+}
+
+static ProjArgs proj_args(const h3attn_params *p, const Plan &pl, int32_t model_dim, const void *x,
+                          int64_t x_stride, const void *w_qkv, const float *norm_w, const float *rope)
+{
+    ProjArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = static_cast<const uint16_t *>(w_qkv);
+    a.x_stride = x_stride;
+    a.model_dim = model_dim;
+    a.norm_w = norm_w;
+    a.rope = rope;
+    a.H = pl.H;
+    a.Npad = pl.Npad;
+    a.ntiles = (int32_t)(pl.Npad / kTile);
+    a.nblk = (int32_t)(pl.Npad / kSeqPad);
+    a.eps = p->eps;
+    a.q_mult = 1.0f;
+    a.seq = seq_table(pl);
+    return a;
+}
+
+h3attn_status h3attn_fwd_proj_stages(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                                     const void *w_qkv, const float *norm_w, const float *rope_tables,
+                                     const int32_t *cu_seqlens_host, void *out, void *workspace,
+                                     size_t workspace_bytes, void *stream, int stages)
+{
+    Plan pl;
+    h3attn_status st = proj_plan(p, model_dim, x_stride, cu_seqlens_host, pl);
+    if (st != H3ATTN_OK) return st;
+    if (stages < 1 || stages > 3) return fail(H3ATTN_ERR_INVALID_ARG, "stages must be 1, 2 or 3 (got %d)", stages);
+    if (pl.N == 0) return ok();
+    if ((st = check_ptrs(x, w_qkv, x, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
+    if (!workspace) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(H3ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < pl.bytes_bf16)
+        return fail(H3ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes_bf16);
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+
+    ProjArgs pa = proj_args(p, pl, model_dim, x, x_stride, w_qkv, norm_w, rope_tables);
+    pa.qhat = reinterpret_cast<uint16_t *>(ws + pl.qhat);
+    pa.khat = reinterpret_cast<uint16_t *>(ws + pl.khat);
+    pa.vt = reinterpret_cast<uint16_t *>(ws + pl.vt);
+    pa.knorm = reinterpret_cast<float *>(ws + pl.knorm);
+    pa.out_hstride = pl.Npad * pl.d;
+    pa.out_tstride = pl.d;
+    pa.natural = 0;
+    pa.q_mult = scale_log2(p);
+    if (stages & 1)
+        if ((st = hip_status(launch_qkv_proj(pa, pl.d, hs), "projection launch")) != H3ATTN_OK) return st;
+    if (!(stages & 2)) return ok();
+
+    AttnArgs aa;
+    std::memset(&aa, 0, sizeof aa);
+    aa.qhat = pa.qhat;
+    aa.khat = pa.khat;
+    aa.vt = pa.vt;
+    aa.knorm = pa.knorm;
+    aa.out = static_cast<uint16_t *>(out);
+    aa.o_stride = p->o_stride;
+    aa.Npad = pl.Npad;
+    aa.H = pl.H;
+    const int64_t items = order_work(pl, aa, nullptr);
+    return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "attention launch");
+}
+
+h3attn_status h3attn_fwd_proj(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                              const void *w_qkv, const float *norm_w, const float *rope_tables,
+                              const int32_t *cu_seqlens_host, void *out, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    return h3attn_fwd_proj_stages(p, model_dim, x, x_stride, w_qkv, norm_w, rope_tables, cu_seqlens_host, out,
+                                  workspace, workspace_bytes, stream, 3);
+}
+
+h3attn_status h3attn_proj_prologue(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                                   const void *w_qkv, const float *norm_w, const float *rope_tables,
+                                   const int32_t *cu_seqlens_host, void *q_hat, void *k_hat, void *v_out,
+                                   void *stream)
+{
+    Plan pl;
+    h3attn_status st = proj_plan(p, model_dim, x_stride, cu_seqlens_host, pl);
+    if (st != H3ATTN_OK) return st;
+    if (pl.N == 0) return ok();
+    if ((st = check_ptrs(x, w_qkv, k_hat, norm_w, rope_tables, q_hat)) != H3ATTN_OK) return st;
+    if (!v_out) return fail(H3ATTN_ERR_INVALID_ARG, "v_out is NULL");
+    if (!aligned(v_out, 16)) return fail(H3ATTN_ERR_INVALID_ARG, "v_out is not 16-byte aligned");
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    ProjArgs pa = proj_args(p, pl, model_dim, x, x_stride, w_qkv, norm_w, rope_tables);
+    pa.qhat = static_cast<uint16_t *>(q_hat);
+    pa.khat = static_cast<uint16_t *>(k_hat);
+    pa.vt = static_cast<uint16_t *>(v_out);
+    pa.out_hstride = pl.d;
+    pa.out_tstride = (int64_t)pl.H * pl.d;
+    pa.natural = 1;
+    return hip_status(launch_qkv_proj(pa, pl.d, static_cast<hipStream_t>(stream)), "projection launch");
+}
+
 static h3attn_status q8_common(const h3attn_params *p, const void *q, const void *k, const void *v,
                                const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
                                const void *out, void *workspace, size_t workspace_bytes, Plan &pl, Q8Args &qa)

@@ -25,7 +25,8 @@ H3ATTN_ERR_HIP = 5
 H3ATTN_MAX_SEQS = 64
 
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
-            "h3attn_fwd_q8_stages", "h3attn_prologue",
+            "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
+            "h3attn_proj_prologue",
             "h3attn_q8_prologue", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
@@ -64,6 +65,15 @@ def lib():
         for name in ("h3attn_fwd_stages", "h3attn_fwd_q8_stages"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = fwd_args + [C.c_int]
+        proj_args = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp, P(C.c_int32), vp, vp,
+                     C.c_size_t, vp]
+        L.h3attn_fwd_proj.restype = C.c_int
+        L.h3attn_fwd_proj.argtypes = proj_args
+        L.h3attn_fwd_proj_stages.restype = C.c_int
+        L.h3attn_fwd_proj_stages.argtypes = proj_args + [C.c_int]
+        L.h3attn_proj_prologue.restype = C.c_int
+        L.h3attn_proj_prologue.argtypes = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp,
+                                           P(C.c_int32), vp, vp, vp, vp]
         L.h3attn_prologue.restype = C.c_int
         L.h3attn_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, P(C.c_int32), vp, vp, vp]
         L.h3attn_q8_prologue.restype = C.c_int
@@ -210,6 +220,61 @@ def h3attn_prologue(q, k, norm_w, rope_tables, cu_seqlens, q_hat=None, k_hat=Non
                                  _dev_ptr(rope_tables), _cu_ptr(cu), _dev_ptr(q_hat),
                                  _dev_ptr(k_hat), _stream_ptr(stream)))
     return q_hat, k_hat
+
+
+def proj_raw(params, model_dim: int, x, x_stride: int, w_qkv, norm_w, rope_tables, cu_seqlens, out,
+             workspace, workspace_bytes, stream, stages: int = 3) -> int:
+    """Direct call of h3attn_fwd_proj (_stages when ``stages`` is not 3) with
+    integer device pointers; returns the status code."""
+    cu = _cu_array(cu_seqlens)
+    args = (C.byref(params), int(model_dim), x, int(x_stride), w_qkv, norm_w, rope_tables, _cu_ptr(cu),
+            out, workspace, workspace_bytes, stream)
+    if stages != 3:
+        return int(lib().h3attn_fwd_proj_stages(*args, int(stages)))
+    return int(lib().h3attn_fwd_proj(*args))
+
+
+def _proj_params(x, w_qkv, num_heads: int, head_dim: int, num_seqs: int, o_stride: int, eps, softmax_scale):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [N, D] with contiguous channels")
+    hd = num_heads * head_dim
+    if w_qkv.dim() != 2 or tuple(w_qkv.shape) != (3 * hd, x.shape[1]) or not w_qkv.is_contiguous():
+        raise ValueError("w_qkv must be a contiguous [3*H*d, D] tensor")
+    return make_params(num_heads, head_dim, num_seqs, hd, hd, hd, o_stride, eps, softmax_scale)
+
+
+def h3attn_fwd_proj(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: int, head_dim: int, out=None,
+                    workspace=None, eps: float = 1e-6, softmax_scale: float = 0.0, stream=None,
+                    stages: int = 3):
+    """out[N, H, d] (bf16) = attention of the fused QKV projection of hidden
+    states x [N, D] (bf16) by w_qkv [3*H*d, D] (bf16), with the RMSNorm + RoPE
+    prologue (include/h3attn.h, h3attn_fwd_proj)."""
+    import torch
+    N, D = x.shape
+    if out is None:
+        out = torch.empty((N, num_heads, head_dim), dtype=torch.bfloat16, device=x.device)
+    cu = _cu_array(cu_seqlens)
+    params = _proj_params(x, w_qkv, num_heads, head_dim, len(cu) - 1, out.stride(0), eps, softmax_scale)
+    if workspace is None:
+        workspace = torch.empty(h3attn_workspace_size(params, cu), dtype=torch.uint8, device=x.device)
+    _check(proj_raw(params, D, _dev_ptr(x), x.stride(0), _dev_ptr(w_qkv), _dev_ptr(norm_w),
+                    _dev_ptr(rope_tables), cu, _dev_ptr(out), _dev_ptr(workspace),
+                    workspace.numel() * workspace.element_size(), _stream_ptr(stream), stages))
+    return out
+
+
+def h3attn_proj_prologue(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: int, head_dim: int,
+                         eps: float = 1e-6, stream=None):
+    """Stage 1 of h3attn_fwd_proj in natural layouts: (q_hat, k_hat, v), each bf16 [N, H, d]."""
+    import torch
+    N, D = x.shape
+    cu = _cu_array(cu_seqlens)
+    res = [torch.empty((N, num_heads, head_dim), dtype=torch.bfloat16, device=x.device) for _ in range(3)]
+    params = _proj_params(x, w_qkv, num_heads, head_dim, len(cu) - 1, num_heads * head_dim, eps, 0.0)
+    _check(lib().h3attn_proj_prologue(C.byref(params), D, _dev_ptr(x), x.stride(0), _dev_ptr(w_qkv),
+                                      _dev_ptr(norm_w), _dev_ptr(rope_tables), _cu_ptr(cu),
+                                      *[_dev_ptr(t) for t in res], _stream_ptr(stream)))
+    return tuple(res)
 
 
 def h3attn_q8_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,

@@ -168,6 +168,49 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
                                  float *v_scale, void *stream);
 
 /*
+ * QKV projection fused with the same prologue, then the attention: the
+ * attention layer from its input hidden states.  The page "H3 Runtime Current
+ * State" lists the attention QKV projection among the block's GEMMs (about 27%
+ * of a block together, "Buyer Questions: Current Evidence Status", question
+ * 4); the pages give no formula, so this is the plain linear map without bias:
+ *   [q | k | v]_t = x_t . W^T,  W = w_qkv [3*H*d][model_dim] (nn.Linear layout),
+ * output features q first, then k, then v, each head-major (feature h*d + c of
+ * its part).  q and k are normalised and rotated in fp32 straight from the
+ * fp32 accumulators (they are never rounded before the norm); v is rounded to
+ * bf16 once.  Then exactly the attention of h3attn_fwd.
+ *   model_dim   D: positive multiple of 32
+ *   x           device bf16, token t channel c at x[t*x_stride + c]; x_stride >= D,
+ *               multiple of 8
+ *   w_qkv       device bf16 [3*H*d][D], rows contiguous
+ *   norm_w, rope_tables, cu_seqlens_host, out, workspace, stream: as h3attn_fwd
+ *               (workspace >= h3attn_workspace_size(p, cu, 0) bytes)
+ * The q_stride, k_stride and v_stride of `p` are not read.  x, w_qkv, norm_w,
+ * rope_tables and out must be 16-byte aligned.
+ */
+h3attn_status h3attn_fwd_proj(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                              const void *w_qkv, const float *norm_w, const float *rope_tables,
+                              const int32_t *cu_seqlens_host, void *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* The two stages of h3attn_fwd_proj (1: projection + prologue into the
+ * workspace, 2: attention, 3: both); same contract as h3attn_fwd_stages. */
+h3attn_status h3attn_fwd_proj_stages(const h3attn_params *p, int32_t model_dim, const void *x,
+                                     int64_t x_stride, const void *w_qkv, const float *norm_w,
+                                     const float *rope_tables, const int32_t *cu_seqlens_host,
+                                     void *out, void *workspace, size_t workspace_bytes,
+                                     void *stream, int stages);
+
+/*
+ * Diagnostic: stage 1 of h3attn_fwd_proj exported in natural layouts, by the
+ * same kernel: q_hat and k_hat (normalised and rotated, bf16; q_hat without the
+ * softmax scale) and the projected v_out (bf16), each device [N][H][d].
+ */
+h3attn_status h3attn_proj_prologue(const h3attn_params *p, int32_t model_dim, const void *x,
+                                   int64_t x_stride, const void *w_qkv, const float *norm_w,
+                                   const float *rope_tables, const int32_t *cu_seqlens_host,
+                                   void *q_hat, void *k_hat, void *v_out, void *stream);
+
+/*
  * Host helpers that fill RoPE tables (fp32 (cos, sin) pairs) on the host.
  * Video: a T x Hg x Wg latent grid in t-major raster order (token n has
  * t = n / (Hg*Wg), y = (n / Wg) % Hg, x = n % Wg, all 0-based); dims [0, dt)

@@ -26,8 +26,9 @@ def oracle_threads() -> int:
 def to_device(inputs: Dict[str, np.ndarray], w: synth.Workload, device="cuda:0"):
     import torch
     t = {}
-    for key in ("q", "k", "v"):
-        t[key] = torch.from_numpy(inputs[key].view(np.int16)).to(device).view(torch.bfloat16)
+    for key in ("q", "k", "v", "x", "w_qkv"):
+        if key in inputs:
+            t[key] = torch.from_numpy(inputs[key].view(np.int16)).to(device).view(torch.bfloat16)
     t["norm_w"] = torch.from_numpy(inputs["norm_w"]).to(device)
     t["rope"] = torch.from_numpy(h.rope_table(w.seqs, w.split, w.d, w.theta)).to(device)
     t["cu"] = inputs["cu_seqlens"]
@@ -40,6 +41,17 @@ def run(w: synth.Workload, t, quantized=False, out=None, workspace=None, stream=
         label, w.name, w.seed, w.N, w.H, w.d, "h3attn_fwd_q8" if quantized else "h3attn_fwd"))
     o = h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], out=out,
                      workspace=workspace, eps=w.eps, stream=stream, quantized=quantized)
+    torch.cuda.synchronize()
+    return o
+
+
+def run_proj(w: synth.Workload, t, out=None, workspace=None, x=None, label=""):
+    """h3attn_fwd_proj on uploaded hidden states (``x`` overrides t["x"], e.g. a strided view)."""
+    import torch
+    announce("%s workload=%s seed=%d N=%d H=%d d=%d D=%d entry=h3attn_fwd_proj" % (
+        label, w.name, w.seed, w.N, w.H, w.d, w.model_dim))
+    o = h.h3attn_fwd_proj(t["x"] if x is None else x, t["w_qkv"], t["norm_w"], t["rope"], t["cu"], w.H, w.d,
+                          out=out, workspace=workspace, eps=w.eps)
     torch.cuda.synchronize()
     return o
 

@@ -211,3 +211,43 @@ def test_quantised_path_argument_errors():
     assert _call(ws_bytes=need - 1, quantized=True) == h.H3ATTN_ERR_WORKSPACE
     assert _call(quantized=True, stages=5) == h.H3ATTN_ERR_INVALID_ARG
     assert _call(ptrs={"v": 0}, quantized=True) == h.H3ATTN_ERR_INVALID_ARG
+
+
+def _proj_call(params=None, model_dim=3072, x_stride=3072, cu=(0, 1000), ws_bytes=1 << 40, ptrs=None,
+               stages=3):
+    params = params if params is not None else _params()
+    p = dict(x=FAKE, w=FAKE, norm_w=FAKE, rope=FAKE, out=FAKE, ws=FAKE * 256)
+    p.update(ptrs or {})
+    return h.proj_raw(params, model_dim, p["x"], x_stride, p["w"], p["norm_w"], p["rope"], np.array(cu, np.int32),
+                      p["out"], p["ws"], ws_bytes, None, stages)
+
+
+@pytest.mark.parametrize("kw,msg,code", [
+    (dict(model_dim=0), "model_dim", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(model_dim=3000), "model_dim", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(x_stride=3064), "x_stride", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(x_stride=3076), "x_stride", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(x_stride=1 << 23), "x_stride", h.H3ATTN_ERR_UNSUPPORTED),
+    (dict(model_dim=1 << 23, x_stride=1 << 23), "too large", h.H3ATTN_ERR_UNSUPPORTED),
+    (dict(stages=0), "stages", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"x": 0}), "NULL", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"w": FAKE + 4}), "aligned", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"ws": 0}), "workspace", h.H3ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=4096), "needs", h.H3ATTN_ERR_WORKSPACE),
+    (dict(params=_params(num_heads=0)), "num_heads", h.H3ATTN_ERR_INVALID_ARG),
+])
+def test_projection_argument_errors(kw, msg, code):
+    assert _proj_call(**kw) == code
+    assert msg in h.last_error()
+
+
+def test_projection_ignores_qkv_strides_and_accepts_empty_input():
+    # the q/k/v strides of the params are not read by the projection entry points
+    p = _params(q_stride=8, k_stride=8, v_stride=8)
+    assert _proj_call(p, cu=(0, 0)) == h.H3ATTN_OK
+    assert _proj_call(p, cu=(0, 0), ptrs={"x": 0, "w": 0}) == h.H3ATTN_OK    # N = 0 reads nothing
+
+
+@pytest.mark.skipif(_gpu_present(), reason="checks the no-device error path; a GPU is present")
+def test_projection_valid_call_without_gpu_reports_device_error():
+    assert _proj_call() == h.H3ATTN_ERR_DEVICE
