@@ -12,6 +12,12 @@ is measured live over the timed region.
 Prints one JSON line: whole-step attention TFLOP/s (4 * sum n_i^2 * d * H per
 step), the attention kernel's roofline against the bf16 dense MFMA peak, and
 the CPU oracle's throughput on a bounded sample of the same workload.
+
+With a projection workload (``--workload proj_joint``) a step starts from the
+hidden states: the fused QKV projection + prologue kernel, then the attention
+kernel (h3attn_fwd_proj_stages 1 and 2); the step's FLOP count adds the
+projection's 2 * N * D * 3*H*d, and the line also reports the projection
+kernel beside the vendor-library GEMM plus the separate prologue.
 """
 from __future__ import annotations
 
@@ -82,18 +88,40 @@ def device_copy_rate(torch, dev, mib: int = 1024, reps: int = 5) -> float:
     return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def one_head_problem(w, inputs, head: int):
+    """The oracle problem of one head of a projection workload: its q, k, v
+    rows of W_qkv, projected in fp64 (heads are independent)."""
+    import oracle
+    hd = w.H * w.d
+    sel = np.concatenate([part * hd + head * w.d + np.arange(w.d) for part in range(3)])
+    w1 = w.replace(H=1)
+    sub = {"x": inputs["x"], "w_qkv": np.ascontiguousarray(inputs["w_qkv"][sel]),
+           "norm_w": np.ascontiguousarray(inputs["norm_w"][:, [head]])}
+    return w1, oracle.Problem.from_projection(w1, sub)
+
+
 def cpu_baseline(w, inputs, seconds: float, threads: int):
     """Time the fp64 CPU oracle on sampled query rows of one head (full key set)."""
     import oracle
-    p = oracle.Problem.from_workload(w, inputs)
-    n = w.seqs[0].n
     rng = np.random.default_rng(w.seed + 99)
     head = int(rng.integers(w.H))
+    n = w.seqs[0].n
     flops_per_row = 4.0 * n * w.d
+    proj_s = 0.0
+    if w.model_dim > 0:
+        # the one head's fp64 projection of every token is part of the timed work
+        t0 = time.perf_counter()
+        w1, p = one_head_problem(w, inputs, head)
+        proj_s = time.perf_counter() - t0
+        H_rows, head_row = 1, 0
+        flops_per_row += 2.0 * w.model_dim * 3 * w.d        # the row's share of the projection
+    else:
+        p = oracle.Problem.from_workload(w, inputs)
+        H_rows, head_row = w.H, head
 
     def run(nrows):
         toks = np.sort(rng.choice(n, size=nrows, replace=False)).astype(np.int64)
-        rows = toks * w.H + head
+        rows = toks * H_rows + head_row
         t0 = time.perf_counter()
         p.attention_rows(rows, nthreads=threads)
         return time.perf_counter() - t0
@@ -106,17 +134,63 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
     fixed = max(t1 - per_row * probe, 0.0)
     nrows = int(max(probe, min(n, (seconds - fixed) / per_row)))
     t = run(nrows)
+    if w.model_dim > 0:
+        # the head's projection time is spread over all n of its rows
+        t += proj_s * nrows / n
     value = nrows * flops_per_row / t / 1e12
+    sample = ("%d query rows of head %d (of %d x %d rows), each over all %d keys; fp64; "
+              "the keys' RMSNorm+RoPE included; %.1f s" % (nrows, head, w.N, w.H, n, t))
+    if w.model_dim > 0:
+        sample += ("; plus the head's fp64 QKV projection of all tokens (%.1f s, %.0f%% of it "
+                   "charged to the sampled rows)" % (proj_s, 100.0 * nrows / n))
     return {
         "value": round(value, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "cpu_model": cpu_model(),
-        "extrapolated_full_s": round(w.flops() / (value * 1e12), 1),
+        "extrapolated_full_s": round((w.flops() + w.proj_flops()) / (value * 1e12), 1),
         "kind": "oracle",
-        "sample": "%d query rows of head %d (of %d x %d rows), each over all %d keys; fp64; "
-                  "the keys' RMSNorm+RoPE included; %.1f s" % (nrows, head, w.N, w.H, n, t),
+        "sample": sample,
     }
+
+
+def library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream, reps: int = 5):
+    """The unfused alternative, timed after the timed region: the QKV product on
+    the vendor library (torch.mm, hipBLASLt) into a bf16 [N, 3*H*d] buffer,
+    then this library's prologue reading q, k and v as strided views of it."""
+    hd = w.H * w.d
+    y = torch.empty((w.N, 3 * hd), dtype=torch.bfloat16, device=x.device)
+    wt = wq.t()
+    q, k, v = (y[:, i * hd:(i + 1) * hd].view(w.N, w.H, w.d) for i in range(3))
+    out = torch.empty((w.N, w.H, w.d), dtype=torch.bfloat16, device=x.device)
+    params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
+    ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
+
+    def prologue():
+        st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, int(stream.cuda_stream), False, 1)
+        if st != 0:
+            raise RuntimeError(h.last_error())
+
+    torch.mm(x, wt, out=y)
+    prologue()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    gemm, pro = [], []
+    for _ in range(reps):
+        ev[0].record(stream)
+        torch.mm(x, wt, out=y)
+        ev[1].record(stream)
+        prologue()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        gemm.append(ev[0].elapsed_time(ev[1]))
+        pro.append(ev[1].elapsed_time(ev[2]))
+    del y, out
+    g, p = float(np.mean(gemm)), float(np.mean(pro))
+    return {"library_gemm_ms": round(g, 4),
+            "library_gemm_TFLOPs": round(w.proj_flops() / (g * 1e-3) / 1e12, 1),
+            "unfused_prologue_ms": round(p, 4),
+            "unfused_total_ms": round(g + p, 4)}
 
 
 def main():
@@ -141,22 +215,29 @@ def main():
     from audio_diffusion_transformer_amd import synth
 
     w = synth.WORKLOADS[args.workload]
+    proj = w.model_dim > 0
     t0 = time.time()
     inp = synth.generate(w)
     dev = torch.device("cuda:0")
-    q = torch.from_numpy(inp["q"].view(np.int16)).to(dev).view(torch.bfloat16)
-    k = torch.from_numpy(inp["k"].view(np.int16)).to(dev).view(torch.bfloat16)
-    v = torch.from_numpy(inp["v"].view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
     norm_w = torch.from_numpy(inp["norm_w"]).to(dev)
     rope = torch.from_numpy(h.rope_table(w.seqs, w.split, w.d, w.theta)).to(dev)
     cu = inp["cu_seqlens"]
-    out = torch.empty_like(q)
-    params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
+    out = torch.empty((w.N, w.H, w.d), dtype=torch.bfloat16, device=dev)
+    if proj:
+        x, wq = up(inp["x"]), up(inp["w_qkv"])
+        params = h._proj_params(x, wq, w.H, w.d, len(cu) - 1, out.stride(0), w.eps, 0.0)
+    else:
+        q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
+        params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
+        ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
     ws_bytes = h.h3attn_workspace_size(params, cu, w.quantized)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
-    ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
     torch.cuda.synchronize()
     print("[bench] inputs ready for %s (N=%d) in %.1f s" % (w.name, w.N, time.time() - t0),
           file=sys.stderr, flush=True)
@@ -172,8 +253,12 @@ def main():
         del src, dst
 
     def stage(sid):
-        st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp,
-                       w.quantized, sid)
+        if proj:
+            st = h.proj_raw(params, w.model_dim, x.data_ptr(), x.stride(0), wq.data_ptr(), norm_w.data_ptr(),
+                            rope.data_ptr(), cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp, sid)
+        else:
+            st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp,
+                           w.quantized, sid)
         if st != 0:
             raise RuntimeError("%s: %s" % (h.status_string(st), h.last_error()))
 
@@ -202,13 +287,14 @@ def main():
     pro_avg = float(np.mean(pro_ms))
     step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
     copy_gbps = device_copy_rate(torch, dev)        # after the timed region
-    print("[bench] %d steps: %.3f ms/step (attention %.3f, prologue %.3f), wall %.3f s" % (
-        K, ms_step, att_avg, pro_avg, wall), file=sys.stderr, flush=True)
+    print("[bench] %d steps: %.3f ms/step (attention %.3f, %s %.3f), wall %.3f s" % (
+        K, ms_step, att_avg, "projection" if proj else "prologue", pro_avg, wall), file=sys.stderr, flush=True)
+    unfused = library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream) if proj else None
 
-    flops = w.flops()
+    flops = w.flops() + w.proj_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     peak = MI355X_FP8_DENSE_TFLOPS if w.quantized else MI355X_BF16_DENSE_TFLOPS
-    achieved = flops / (att_avg * 1e-3) / 1e12
+    achieved = w.flops() / (att_avg * 1e-3) / 1e12
     kernel_file = "q8.hip" if w.quantized else "attn_bf16.hip"
     summary = ("attn_q8_%s_pmc.md" if w.quantized else "attn_bf16_%s_pmc.md") % w.name
     traffic = measured_traffic(kernel_file, summary)
@@ -219,6 +305,11 @@ def main():
         pro_bytes = 5 * N * H * d * 2 + 3 * N * H * d + 2 * N * (d // 2) * 8
         metric = ("attention TFLOP/s (INT8 QK, FP8 PV) and %% of fp8 MFMA peak at N=%d packed tokens, "
                   "H=%d, d=%d" % (N, H, d))
+    elif proj:
+        # read x, W and the table; write qhat, khat and the transposed V copy
+        pro_bytes = N * w.model_dim * 2 + 3 * H * d * w.model_dim * 2 + N * (d // 2) * 8 + 3 * N * H * d * 2
+        metric = ("attention layer (QKV projection D=%d + attention) TFLOP/s at N=%d packed tokens, "
+                  "H=%d, d=%d" % (w.model_dim, N, H, d))
     else:
         # read q, k, v and the table; write qhat, khat and the transposed V copy
         pro_bytes = 3 * N * H * d * 2 + 3 * N * H * d * 2 + N * (d // 2) * 8
@@ -255,6 +346,16 @@ def main():
                     "attention_avg_ms": round(att_avg, 4)},
         "cpu_baseline": None,
     }
+    if proj:
+        pf = w.proj_flops() / (pro_avg * 1e-3) / 1e12
+        kern = res["kernels"]
+        for key in ("prologue_avg_ms", "prologue_GBps", "prologue_hbm_frac", "prologue_copy_frac"):
+            kern.pop(key)
+        kern.update({"projection_avg_ms": round(pro_avg, 4), "projection_TFLOPs": round(pf, 1),
+                     "projection_frac": round(pf / MI355X_BF16_DENSE_TFLOPS, 4),
+                     "projection_min_bytes": pro_bytes})
+        kern.update(unfused)
+        res["config"]["model_dim"] = w.model_dim
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         print("[bench] timing the CPU oracle on %d threads" % threads, file=sys.stderr, flush=True)

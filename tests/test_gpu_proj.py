@@ -4,8 +4,9 @@ h3attn_proj_prologue) against the fp64 oracle's projection
 
 Stage parity: the normalised, rotated q and k and the projected v of the
 natural-layout export are compared element by element, |GPU - oracle| <=
-2^-8 |oracle| + 1e-5 (bf16 storage rounds to 2^-9 relative; the fp32 matrix
-product adds ~1e-6 absolute).  End to end: the attention output at the bf16
+2^-8 |oracle| + 1e-5 (storing in bf16 rounds to within 2^-8 relative, the
+unit roundoff of its 8-bit significand; the fp32 matrix product and the fp32
+norm and rotation add a few 1e-6 absolute).  End to end: the attention output at the bf16
 gates.  Small cases cover every token and row: ragged and empty sequences,
 audio tokens, both head dims, model dims of 1, 2, 3 and 5 pipeline slabs and
 hidden states read through a token stride wider than the model dim.  The
