@@ -28,7 +28,7 @@ from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["Seq", "Workload", "WORKLOADS", "generate", "sample_rows",
+__all__ = ["Seq", "Workload", "WORKLOADS", "generate", "generate_out", "sample_rows",
            "bf16_bits_from_f32", "f32_from_bf16_bits", "total_tokens"]
 
 
@@ -207,6 +207,28 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
         norm_w = (1.0 + 0.1 * gen[3].standard_normal((2, H, d))).astype(np.float32)
     return {"q": q, "k": k, "v": v, "norm_w": norm_w, "k_offset": k_offset,
             "cu_seqlens": w.cu_seqlens()}
+
+
+def generate_out(w: Workload) -> Dict[str, np.ndarray]:
+    """Inputs of the output projection with its gated residual for workload
+    ``w`` (independent child streams of the workload seed; the draws of
+    ``generate`` are unchanged): a stand-in attention output attn ~ 0.1 N(0, 1)
+    [N, H*d] (the size of the attention outputs of these workloads), the
+    weight w_o ~ N(0, 1/(H*d)) [D, H*d] and the residual resid ~ N(0, 1)
+    [N, D], all bf16 bits, and one fp32 gate per sequence and channel,
+    gate ~ 1 + 0.5 N(0, 1) [S, D].  D is the model dimension (H*d without one)."""
+    kids = np.random.SeedSequence(w.seed).spawn(14)[10:]
+    gen = [np.random.Generator(np.random.Philox(k)) for k in kids]
+    N, hd = w.N, w.H * w.d
+    D = w.model_dim if w.model_dim > 0 else hd
+    attn = np.empty((N, hd), dtype=np.uint16)
+    for r0 in range(0, N, 1 << 15):
+        r1 = min(N, r0 + (1 << 15))
+        attn[r0:r1] = bf16_bits_from_f32(gen[0].standard_normal((r1 - r0, hd), dtype=np.float32) * np.float32(0.1))
+    w_o = bf16_bits_from_f32(gen[1].standard_normal((D, hd), dtype=np.float32) * np.float32(1.0 / np.sqrt(hd)))
+    resid = _normal_bf16(gen[2], (N, D))
+    gate = (1.0 + 0.5 * gen[3].standard_normal((w.S, D))).astype(np.float32)
+    return {"attn": attn, "w_o": w_o, "resid": resid, "gate": gate, "cu_seqlens": w.cu_seqlens()}
 
 
 def sample_rows(w: Workload, n_rows: int, seed: int | None = None) -> np.ndarray:

@@ -276,6 +276,41 @@ def project(x_bits, w_bits, rows=None, chunk: int = 8192) -> np.ndarray:
     return out
 
 
+def out_proj(attn, w_o, cu_seqlens, gate=None, resid=None, rows=None, chunk: int = 8192) -> np.ndarray:
+    """Output projection with the gated residual of a DiT-style block:
+    y[t, c] = resid[t, c] + gate[s(t), c] * sum_k attn[t, k] * W_o[c, k].
+
+    The page "Buyer Questions: Current Evidence Status" (question 4) counts the
+    block's GEMMs and its "gates" apart from attention, and the page
+    "Open-H3-Regenerate-2K" lists an adaLN table among the model files; the
+    pages give no formula, so this is the plain reading: the bias-free linear
+    map W_o ([D, H*d], nn.Linear layout) of the attention output, scaled per
+    channel by the gate of the token's sequence and added to the residual.
+    attn: uint16 bf16 bits or float64 [N, H*d]; w_o: uint16 bf16 bits [D, H*d];
+    gate: float32 [S, D] (None: 1); resid: uint16 bf16 bits [N, D] (None: 0);
+    cu_seqlens: [S+1].  Returns fp64 [len(rows) or N, D]; the matrix product
+    (numpy's, a library step) sums exact products in fp64.
+    """
+    a = np.asarray(attn)
+    w = _bf16_bits_to_f64(np.asarray(w_o)).T.copy()
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    idx = np.arange(a.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    seq = np.searchsorted(cu, idx, side="right") - 1
+    assert np.all((seq >= 0) & (seq < len(cu) - 1) & (idx < cu[-1])), "token outside every sequence"
+    out = np.empty((len(idx), w.shape[1]), dtype=np.float64)
+    for i0 in range(0, len(idx), chunk):
+        sl = idx[i0:i0 + chunk]
+        ai = a[sl]
+        ai = _bf16_bits_to_f64(ai) if ai.dtype == np.uint16 else np.asarray(ai, dtype=np.float64)
+        y = ai @ w
+        if gate is not None:
+            y *= np.asarray(gate, dtype=np.float64)[seq[i0:i0 + chunk]]
+        if resid is not None:
+            y += _bf16_bits_to_f64(np.asarray(resid)[sl])
+        out[i0:i0 + chunk] = y
+    return out
+
+
 def _bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 

@@ -511,3 +511,39 @@ def test_projection_scale_leaves_qk_and_scales_output():
                                    rtol=0, atol=1e-10)
     o1 = p1.attention_rows(rows)
     np.testing.assert_allclose(p2.attention_rows(rows), 2.0 * o1, rtol=0, atol=1e-10 * np.abs(o1).max())
+
+
+# ------------------------------------------------------ output projection
+
+def test_out_proj_matches_exact_sums_with_gate_and_residual():
+    rng = np.random.default_rng(50)
+    cu = np.array([0, 3, 3, 7], dtype=np.int32)                 # includes an empty sequence
+    a = _bf16(rng.standard_normal((7, 40)))
+    w = _bf16(rng.standard_normal((6, 40)) * 0.2)
+    g = rng.standard_normal((3, 6)).astype(np.float32)
+    r = _bf16(rng.standard_normal((7, 6)))
+    got = oracle.out_proj(a, w, cu, gate=g, resid=r)
+    af, wf, rf = _f(a), _f(w), _f(r)
+    for t in range(7):
+        s = 0 if t < 3 else 2
+        for c in range(6):
+            terms = [af[t, k] * wf[c, k] for k in range(40)]
+            want = rf[t, c] + float(g[s, c]) * math.fsum(terms)
+            assert abs(got[t, c] - want) <= 1e-14 * (abs(rf[t, c]) + abs(float(g[s, c])) * sum(abs(x) for x in terms))
+    assert np.array_equal(oracle.out_proj(a, w, cu, gate=g, resid=r, rows=[6, 0]), got[[6, 0]])
+
+
+def test_out_proj_identity_weight_gate_per_sequence():
+    # W_o = I: y = resid + gate[s] * attn, with the gate switching exactly at the sequence boundary
+    rng = np.random.default_rng(51)
+    cu = np.array([0, 5, 9], dtype=np.int32)
+    a = _bf16(rng.standard_normal((9, 8)))
+    eye = np.zeros((8, 8), dtype=np.uint16)
+    eye[np.arange(8), np.arange(8)] = 0x3F80
+    g = np.array([[2.0] * 8, [-0.5] * 8], dtype=np.float32)
+    r = _bf16(rng.standard_normal((9, 8)))
+    got = oracle.out_proj(a, eye, cu, gate=g, resid=r)
+    want = _f(r) + np.where(np.arange(9)[:, None] < 5, 2.0, -0.5) * _f(a)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(oracle.out_proj(a, eye, cu), _f(a))                   # gate 1, no residual
+    np.testing.assert_array_equal(oracle.out_proj(a, eye, cu, gate=np.zeros((2, 8), np.float32), resid=r), _f(r))
