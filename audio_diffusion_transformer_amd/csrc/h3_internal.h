@@ -149,6 +149,26 @@ struct ProjArgs {
     SeqTable seq;
 };
 
+// Output projection with the gated residual (out_proj.hip):
+//   out[t][c] = resid[t][c] + gate[s(t)][c] * sum_k attn[t][k] * w[c][k]
+// attn bf16 [N][K] (K = H*d), w bf16 [D][K], gate fp32 [S][D] (null: 1),
+// resid bf16 [N][D] (null: 0), out bf16 [N][D] (may be resid itself).
+struct OutProjArgs {
+    const uint16_t *attn, *w;
+    int64_t attn_stride;
+    int32_t K;                   // H * d, a multiple of 32
+    int32_t model_dim;           // D, a multiple of 128
+    const float *gate;
+    const uint16_t *resid;
+    int64_t resid_stride;
+    uint16_t *out;
+    int64_t out_stride;
+    int64_t N;
+    int32_t nblk;                // ceil(N / 256)
+    int32_t S;
+    int32_t cu[kMaxSeqs + 1];
+};
+
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_prologue(const PrologueArgs &a, int d, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_t st);
@@ -156,6 +176,7 @@ hipError_t launch_q8_prep(const Q8Args &a, int d, hipStream_t st);
 hipError_t launch_attn_q8(const Q8AttnArgs &a, int d, int64_t nitems, hipStream_t st);
 hipError_t launch_q8_export(const Q8ExportArgs &a, hipStream_t st);
 hipError_t launch_qkv_proj(const ProjArgs &a, int d, hipStream_t st);
+hipError_t launch_out_proj(const OutProjArgs &a, hipStream_t st);
 
 // Queries per workgroup of the attention kernels (work-item granularity).
 constexpr int kBlockM = 128;

@@ -444,6 +444,78 @@ h3attn_status h3attn_proj_prologue(const h3attn_params *p, int32_t model_dim, co
     return hip_status(launch_qkv_proj(pa, pl.d, static_cast<hipStream_t>(stream)), "projection launch");
 }
 
+h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model_dim, int32_t num_seqs,
+                              const int32_t *cu_seqlens_host, const void *attn, int64_t attn_stride,
+                              const void *w_o, const float *gate, const void *resid, int64_t resid_stride,
+                              void *out, int64_t out_stride, void *stream)
+{
+    if (num_heads < 1) return fail(H3ATTN_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", num_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(H3ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+    if (num_seqs < 1 || num_seqs > H3ATTN_MAX_SEQS)
+        return fail(H3ATTN_ERR_INVALID_ARG, "num_seqs must be in [1, %d] (got %d)", H3ATTN_MAX_SEQS, num_seqs);
+    if (!cu_seqlens_host) return fail(H3ATTN_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+    const int32_t *cu = cu_seqlens_host;
+    if (cu[0] != 0) return fail(H3ATTN_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+    for (int s = 0; s < num_seqs; ++s)
+        if (cu[s + 1] < cu[s])
+            return fail(H3ATTN_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", s, cu[s], cu[s + 1]);
+    if (model_dim < 128 || model_dim % 128)
+        return fail(H3ATTN_ERR_INVALID_ARG, "model_dim must be a positive multiple of 128 (got %d)", model_dim);
+    const int64_t K = (int64_t)num_heads * head_dim;
+    if (attn_stride < K || attn_stride % 8)
+        return fail(H3ATTN_ERR_INVALID_ARG, "attn_stride %lld must be >= num_heads*head_dim %lld and a multiple of 8",
+                    (long long)attn_stride, (long long)K);
+    if (out_stride < model_dim || out_stride % 8)
+        return fail(H3ATTN_ERR_INVALID_ARG, "out_stride %lld must be >= model_dim %d and a multiple of 8",
+                    (long long)out_stride, model_dim);
+    if (resid && (resid_stride < model_dim || resid_stride % 8))
+        return fail(H3ATTN_ERR_INVALID_ARG, "resid_stride %lld must be >= model_dim %d and a multiple of 8",
+                    (long long)resid_stride, model_dim);
+    // 32-bit buffer offsets: one 256-token block of attn, 256 rows of W_o
+    if ((int64_t)255 * attn_stride * 2 + K * 2 >= ((int64_t)1 << 31))
+        return fail(H3ATTN_ERR_UNSUPPORTED, "attn_stride %lld is too large", (long long)attn_stride);
+    if ((int64_t)256 * K * 2 >= ((int64_t)1 << 31))
+        return fail(H3ATTN_ERR_UNSUPPORTED, "num_heads * head_dim %lld is too large", (long long)K);
+    const int64_t N = cu[num_seqs];
+    if (N == 0) return ok();
+    const void *ps[3] = {attn, w_o, out};
+    const char *names[3] = {"attn", "w_o", "out"};
+    for (int i = 0; i < 3; ++i) {
+        if (!ps[i]) return fail(H3ATTN_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(ps[i], 16)) return fail(H3ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (gate && !aligned(gate, 16)) return fail(H3ATTN_ERR_INVALID_ARG, "gate is not 16-byte aligned");
+    if (resid && !aligned(resid, 16)) return fail(H3ATTN_ERR_INVALID_ARG, "resid is not 16-byte aligned");
+    if (resid && resid != out) {
+        // out may be the residual itself (same pointer and stride) but not a partial overlap of it
+        const char *r0 = static_cast<const char *>(resid), *o0 = static_cast<const char *>(out);
+        const char *r1 = r0 + ((N - 1) * resid_stride + model_dim) * 2, *o1 = o0 + ((N - 1) * out_stride + model_dim) * 2;
+        if (r0 < o1 && o0 < r1) return fail(H3ATTN_ERR_INVALID_ARG, "out overlaps resid without being resid");
+    }
+    if (resid && resid == out && resid_stride != out_stride)
+        return fail(H3ATTN_ERR_INVALID_ARG, "out is resid but with another stride");
+    h3attn_status st = check_device();
+    if (st != H3ATTN_OK) return st;
+    OutProjArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.attn = static_cast<const uint16_t *>(attn);
+    a.w = static_cast<const uint16_t *>(w_o);
+    a.attn_stride = attn_stride;
+    a.K = (int32_t)K;
+    a.model_dim = model_dim;
+    a.gate = gate;
+    a.resid = static_cast<const uint16_t *>(resid);
+    a.resid_stride = resid_stride;
+    a.out = static_cast<uint16_t *>(out);
+    a.out_stride = out_stride;
+    a.N = N;
+    a.nblk = (int32_t)((N + 255) / 256);
+    a.S = num_seqs;
+    for (int s = 0; s <= num_seqs; ++s) a.cu[s] = cu[s];
+    return hip_status(launch_out_proj(a, static_cast<hipStream_t>(stream)), "output projection launch");
+}
+
 static h3attn_status q8_common(const h3attn_params *p, const void *q, const void *k, const void *v,
                                const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
                                const void *out, void *workspace, size_t workspace_bytes, Plan &pl, Q8Args &qa)

@@ -26,7 +26,7 @@ H3ATTN_MAX_SEQS = 64
 
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
             "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
-            "h3attn_proj_prologue",
+            "h3attn_proj_prologue", "h3attn_out_proj",
             "h3attn_q8_prologue", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
@@ -74,6 +74,9 @@ def lib():
         L.h3attn_proj_prologue.restype = C.c_int
         L.h3attn_proj_prologue.argtypes = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp,
                                            P(C.c_int32), vp, vp, vp, vp]
+        L.h3attn_out_proj.restype = C.c_int
+        L.h3attn_out_proj.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, P(C.c_int32), vp, C.c_int64,
+                                      vp, vp, vp, C.c_int64, vp, C.c_int64, vp]
         L.h3attn_prologue.restype = C.c_int
         L.h3attn_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, P(C.c_int32), vp, vp, vp]
         L.h3attn_q8_prologue.restype = C.c_int
@@ -275,6 +278,41 @@ def h3attn_proj_prologue(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: i
                                       _dev_ptr(norm_w), _dev_ptr(rope_tables), _cu_ptr(cu),
                                       *[_dev_ptr(t) for t in res], _stream_ptr(stream)))
     return tuple(res)
+
+
+def out_proj_raw(num_heads: int, head_dim: int, model_dim: int, cu_seqlens, attn, attn_stride: int, w_o, gate,
+                 resid, resid_stride: int, out, out_stride: int, stream) -> int:
+    """Direct call of h3attn_out_proj with integer device pointers (0 for NULL); returns the status."""
+    cu = _cu_array(cu_seqlens)
+    return int(lib().h3attn_out_proj(int(num_heads), int(head_dim), int(model_dim), len(cu) - 1, _cu_ptr(cu),
+                                     attn, int(attn_stride), w_o, gate, resid, int(resid_stride), out,
+                                     int(out_stride), stream))
+
+
+def h3attn_out_proj(attn, w_o, cu_seqlens, gate=None, resid=None, out=None, stream=None):
+    """out[N, D] (bf16) = resid + gate[seq] * (attn . w_o^T): attn [N, H, d] or [N, H*d] bf16,
+    w_o [D, H*d] bf16, gate fp32 [S, D] or None, resid [N, D] bf16 or None; out may be resid."""
+    import torch
+    N = attn.shape[0]
+    if attn.dim() == 3:
+        H, d = attn.shape[1], attn.shape[2]
+        if attn.stride(2) != 1 or attn.stride(1) != d:
+            raise ValueError("attn must have contiguous heads and channels")
+    else:
+        raise ValueError("attn must be [N, H, d]")
+    D = w_o.shape[0]
+    if not w_o.is_contiguous() or w_o.shape[1] != H * d:
+        raise ValueError("w_o must be a contiguous [D, H*d] tensor")
+    if out is None:
+        out = torch.empty((N, D), dtype=torch.bfloat16, device=attn.device)
+    for t in (out, resid):
+        if t is not None and (t.dim() != 2 or t.shape[1] != D or t.stride(1) != 1):
+            raise ValueError("out / resid must be [N, D] with contiguous channels")
+    cu = _cu_array(cu_seqlens)
+    _check(out_proj_raw(H, d, D, cu, _dev_ptr(attn), attn.stride(0), _dev_ptr(w_o), _dev_ptr(gate),
+                        _dev_ptr(resid), resid.stride(0) if resid is not None else 0, _dev_ptr(out),
+                        out.stride(0), _stream_ptr(stream)))
+    return out
 
 
 def h3attn_q8_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,

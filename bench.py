@@ -193,6 +193,34 @@ def library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_byte
             "unfused_total_ms": round(g + p, 4)}
 
 
+def library_out_proj(torch, w, attn, w_o, gate, resid, stream, reps: int = 5):
+    """The unfused output projection, timed after the timed region: torch.mm
+    (hipBLASLt) of the attention output by W_o^T, then the gated residual as
+    one torch elementwise kernel (the workload has one sequence, so its gate
+    row broadcasts)."""
+    a2 = attn.view(w.N, w.H * w.d)
+    wt = w_o.t()
+    g = gate[0].to(torch.bfloat16)
+    y = torch.mm(a2, wt)
+    z = torch.addcmul(resid, y, g)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    mm, ew = [], []
+    for _ in range(reps):
+        ev[0].record(stream)
+        torch.mm(a2, wt, out=y)
+        ev[1].record(stream)
+        torch.addcmul(resid, y, g, out=z)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        mm.append(ev[0].elapsed_time(ev[1]))
+        ew.append(ev[1].elapsed_time(ev[2]))
+    del y, z
+    m_, e_ = float(np.mean(mm)), float(np.mean(ew))
+    return {"library_out_gemm_ms": round(m_, 4), "library_gated_residual_ms": round(e_, 4),
+            "unfused_out_total_ms": round(m_ + e_, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +258,11 @@ def main():
     if proj:
         x, wq = up(inp["x"]), up(inp["w_qkv"])
         params = h._proj_params(x, wq, w.H, w.d, len(cu) - 1, out.stride(0), w.eps, 0.0)
+        gout = synth.generate_out(w)
+        w_o, resid = up(gout["w_o"]), up(gout["resid"])
+        gate = torch.from_numpy(gout["gate"]).to(dev)
+        y = torch.empty((w.N, w.model_dim), dtype=torch.bfloat16, device=dev)
+        del gout
     else:
         q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
         params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
@@ -253,7 +286,10 @@ def main():
         del src, dst
 
     def stage(sid):
-        if proj:
+        if proj and sid == 4:
+            st = h.out_proj_raw(w.H, w.d, w.model_dim, cu, out.data_ptr(), out.stride(0), w_o.data_ptr(),
+                                gate.data_ptr(), resid.data_ptr(), resid.stride(0), y.data_ptr(), y.stride(0), sp)
+        elif proj:
             st = h.proj_raw(params, w.model_dim, x.data_ptr(), x.stride(0), wq.data_ptr(), norm_w.data_ptr(),
                             rope.data_ptr(), cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp, sid)
         else:
@@ -262,13 +298,16 @@ def main():
         if st != 0:
             raise RuntimeError("%s: %s" % (h.status_string(st), h.last_error()))
 
+    nst = 3 if proj else 2                  # launches per step: [projection or prologue,] attention[, output projection]
     for _ in range(args.warmup):
         stage(1)
         stage(2)
+        if proj:
+            stage(4)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
@@ -277,21 +316,28 @@ def main():
         ev[i][1].record(stream)
         stage(2)
         ev[i][2].record(stream)
+        if proj:
+            stage(4)
+            ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    total_ms = ev[0][0].elapsed_time(ev[K - 1][nst])
     pro_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     att_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
     ms_step = total_ms / K
     att_avg = float(np.mean(att_ms))
     pro_avg = float(np.mean(pro_ms))
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    outp_avg = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])) if proj else 0.0
+    step_ms = [ev[i][0].elapsed_time(ev[i][nst]) for i in range(K)]
     copy_gbps = device_copy_rate(torch, dev)        # after the timed region
     print("[bench] %d steps: %.3f ms/step (attention %.3f, %s %.3f), wall %.3f s" % (
         K, ms_step, att_avg, "projection" if proj else "prologue", pro_avg, wall), file=sys.stderr, flush=True)
     unfused = library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream) if proj else None
+    if proj:
+        unfused.update(library_out_proj(torch, w, out, w_o, gate, resid, stream))
+    out_flops = 2.0 * w.N * w.H * w.d * w.model_dim if proj else 0.0
 
-    flops = w.flops() + w.proj_flops()
+    flops = w.flops() + w.proj_flops() + out_flops
     value = flops / (ms_step * 1e-3) / 1e12
     peak = MI355X_FP8_DENSE_TFLOPS if w.quantized else MI355X_BF16_DENSE_TFLOPS
     achieved = w.flops() / (att_avg * 1e-3) / 1e12
@@ -308,8 +354,8 @@ def main():
     elif proj:
         # read x, W and the table; write qhat, khat and the transposed V copy
         pro_bytes = N * w.model_dim * 2 + 3 * H * d * w.model_dim * 2 + N * (d // 2) * 8 + 3 * N * H * d * 2
-        metric = ("attention layer (QKV projection D=%d + attention) TFLOP/s at N=%d packed tokens, "
-                  "H=%d, d=%d" % (w.model_dim, N, H, d))
+        metric = ("attention layer (QKV projection + RMSNorm/RoPE, attention, output projection with gated "
+                  "residual; D=%d) TFLOP/s at N=%d packed tokens, H=%d, d=%d" % (w.model_dim, N, H, d))
     else:
         # read q, k, v and the table; write qhat, khat and the transposed V copy
         pro_bytes = 3 * N * H * d * 2 + 3 * N * H * d * 2 + N * (d // 2) * 8
@@ -351,9 +397,12 @@ def main():
         kern = res["kernels"]
         for key in ("prologue_avg_ms", "prologue_GBps", "prologue_hbm_frac", "prologue_copy_frac"):
             kern.pop(key)
+        of = out_flops / (outp_avg * 1e-3) / 1e12
         kern.update({"projection_avg_ms": round(pro_avg, 4), "projection_TFLOPs": round(pf, 1),
                      "projection_frac": round(pf / MI355X_BF16_DENSE_TFLOPS, 4),
-                     "projection_min_bytes": pro_bytes})
+                     "projection_min_bytes": pro_bytes,
+                     "out_proj_avg_ms": round(outp_avg, 4), "out_proj_TFLOPs": round(of, 1),
+                     "out_proj_frac": round(of / MI355X_BF16_DENSE_TFLOPS, 4)})
         kern.update(unfused)
         res["config"]["model_dim"] = w.model_dim
     if not args.no_cpu_baseline:

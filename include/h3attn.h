@@ -211,6 +211,36 @@ h3attn_status h3attn_proj_prologue(const h3attn_params *p, int32_t model_dim, co
                                    void *q_hat, void *k_hat, void *v_out, void *stream);
 
 /*
+ * Output projection of the attention output with the gated residual of a
+ * DiT-style (adaLN) block.  The page "Buyer Questions: Current Evidence
+ * Status", question 4, counts the block's GEMMs (about 27%) and its "gates"
+ * (about 2%) beside attention; the pages give no formula, so this is the plain
+ * reading:
+ *   out[t][c] = resid[t][c] + gate[s(t)][c] * sum_k attn[t][k] * w_o[c][k]
+ * with s(t) the sequence of packed token t and k over the H*d attention
+ * channels.  fp32 accumulation, gate and residual applied in fp32, one
+ * rounding to bf16.
+ *   num_heads, head_dim  H >= 1, d in {64, 128}: attn has K = H*d channels
+ *   model_dim    D: positive multiple of 128 (output channels)
+ *   num_seqs, cu_seqlens_host  as h3attn_workspace_size (HOST int32 [S+1])
+ *   attn         device bf16, token t channel k at attn[t*attn_stride + k] (the
+ *                [N][H][d] output of h3attn_fwd is this with attn_stride = o_stride)
+ *   w_o          device bf16 [D][K], rows contiguous (nn.Linear layout)
+ *   gate         device fp32 [S][D], or NULL for a gate of 1
+ *   resid        device bf16, token stride resid_stride, or NULL for none
+ *   out          device bf16, token stride out_stride; may be resid itself
+ *                (same pointer and stride) for an in-place residual update,
+ *                must not otherwise overlap any input
+ * Strides are in elements: attn_stride >= K, resid_stride and out_stride >= D,
+ * all multiples of 8; every non-NULL pointer 16-byte aligned.  No workspace.
+ * When N = 0 nothing is read, written or launched.
+ */
+h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model_dim, int32_t num_seqs,
+                              const int32_t *cu_seqlens_host, const void *attn, int64_t attn_stride,
+                              const void *w_o, const float *gate, const void *resid, int64_t resid_stride,
+                              void *out, int64_t out_stride, void *stream);
+
+/*
  * Host helpers that fill RoPE tables (fp32 (cos, sin) pairs) on the host.
  * Video: a T x Hg x Wg latent grid in t-major raster order (token n has
  * t = n / (Hg*Wg), y = (n / Wg) % Hg, x = n % Wg, all 0-based); dims [0, dt)

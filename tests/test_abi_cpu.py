@@ -251,3 +251,39 @@ def test_projection_ignores_qkv_strides_and_accepts_empty_input():
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device error path; a GPU is present")
 def test_projection_valid_call_without_gpu_reports_device_error():
     assert _proj_call() == h.H3ATTN_ERR_DEVICE
+
+
+def _out_call(H=24, d=128, D=3072, cu=(0, 1000), attn_stride=3072, resid_stride=3072, out_stride=3072,
+              ptrs=None):
+    p = dict(attn=FAKE, w=FAKE, gate=FAKE, resid=FAKE * 4, out=FAKE * 64)
+    p.update(ptrs or {})
+    return h.out_proj_raw(H, d, D, np.array(cu, np.int32), p["attn"], attn_stride, p["w"], p["gate"], p["resid"],
+                          resid_stride, p["out"], out_stride, None)
+
+
+@pytest.mark.parametrize("kw,msg,code", [
+    (dict(H=0), "num_heads", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(d=96), "head_dim", h.H3ATTN_ERR_UNSUPPORTED),
+    (dict(D=3000), "model_dim", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(D=64), "model_dim", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(cu=(1, 10)), "cu_seqlens[0]", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(cu=(0, 10, 5)), "decreases", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(attn_stride=3064), "attn_stride", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(out_stride=3076), "out_stride", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(resid_stride=8), "resid_stride", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(attn_stride=1 << 23), "attn_stride", h.H3ATTN_ERR_UNSUPPORTED),
+    (dict(ptrs={"w": 0}), "NULL", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"attn": FAKE + 2}), "aligned", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"gate": FAKE + 4}), "aligned", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"out": FAKE * 4 + 1024}), "overlaps", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"out": FAKE * 4}, out_stride=3080), "stride", h.H3ATTN_ERR_INVALID_ARG),
+])
+def test_out_proj_argument_errors(kw, msg, code):
+    assert _out_call(**kw) == code
+    assert msg in h.last_error()
+
+
+def test_out_proj_empty_input_and_null_gate_residual():
+    assert _out_call(cu=(0, 0), ptrs={"attn": 0, "w": 0, "out": 0}) == h.H3ATTN_OK
+    if not _gpu_present():
+        assert _out_call(ptrs={"gate": 0, "resid": 0}) == h.H3ATTN_ERR_DEVICE   # valid up to the device check
