@@ -187,6 +187,91 @@ class Problem:
             raise ValueError("oracle: row outside every sequence")
         return out
 
+    # -- block-sparse attention (kept 64-key tiles per 128-row query block) --
+    def sparse_items(self):
+        """(sequence, head, query block) work items in the order block-sparse
+        tile lists are laid out: sequence-major, then head, then 128-row block."""
+        items = []
+        for s in range(len(self.cu) - 1):
+            n = int(self.cu[s + 1] - self.cu[s])
+            for hh in range(self.H):
+                for qb in range((n + 127) // 128):
+                    items.append((s, hh, qb))
+        return items
+
+    def sparse_attention_rows(self, rows, tiles, tiles_per_block: int, nthreads: int = 0) -> np.ndarray:
+        """Attention of the rows (token * H + head) over only the keys of the
+        64-key tiles kept for their 128-row query block: tiles is int32
+        [items, tiles_per_block] (items as sparse_items()); of an item's row
+        the first min(tiles_per_block, ceil(n_s / 64)) entries are tile
+        indices within the sequence, the rest are ignored.  The softmax runs
+        over the kept keys only (exactly the plain definition restricted to
+        them); a row with no kept key gets 0."""
+        rows = np.asarray(rows, dtype=np.int64)
+        tiles = np.asarray(tiles)
+        items = self.sparse_items()
+        index = {it: i for i, it in enumerate(items)}
+        out = np.zeros((len(rows), self.d), dtype=np.float64)
+        groups = {}
+        for r_i, r in enumerate(rows.tolist()):
+            tok, hh = divmod(r, self.H)
+            s = int(np.searchsorted(self.cu, tok, side="right") - 1)
+            qb = (tok - int(self.cu[s])) // 128
+            groups.setdefault((s, hh, qb), []).append(r_i)
+        for (s, hh, qb), idx in groups.items():
+            n = int(self.cu[s + 1] - self.cu[s])
+            L = min(tiles_per_block, (n + 63) // 64)
+            kept = sorted(set(int(t) for t in tiles[index[(s, hh, qb)], :L]))
+            keys = np.concatenate([np.arange(64 * t, min(64 * t + 64, n)) for t in kept]) + int(self.cu[s]) \
+                if kept else np.zeros(0, dtype=np.int64)
+            krows = keys.astype(np.int64) * self.H + hh
+            qrows = rows[idx]
+            if len(keys) == 0:
+                continue
+            khat = self.prologue_rows(1, krows, nthreads)
+            vv = self.value_rows(krows)
+            qhat = self.prologue_rows(0, qrows, nthreads)
+            out[idx] = attention_core(qhat, khat, vv, self.scale, library=self.L)
+        return out
+
+    def value_rows(self, rows) -> np.ndarray:
+        """v of the rows (token * H + head), fp64."""
+        rows = np.asarray(rows, dtype=np.int64)
+        tok, hh = rows // self.H, rows % self.H
+        vv = self.v[tok, hh]
+        return vv.astype(np.float64) if vv.dtype == np.float64 else _bf16_bits_to_f64(vv)
+
+    def sparse_select(self, tiles_per_block: int) -> np.ndarray:
+        """Top-k kept tiles per (sequence, head, 128-row query block) by pooled
+        score: qbar = mean of the block's qhat' rows (qhat * scale * log2 e),
+        kbar_t = mean of tile t's khat rows, both from the values rounded to bf16
+        as the attention path stores them, score_t = qbar . kbar_t (fp64).  The
+        min(tiles_per_block, ceil(n_s / 64)) best tiles (ties to the lower index)
+        in ascending order, the rest of the row -1.  Returns (tiles [items, k],
+        scores: list of per-item fp64 score vectors) for checking a selection."""
+        items = self.sparse_items()
+        out = -np.ones((len(items), tiles_per_block), dtype=np.int32)
+        scores = []
+        mult = self.scale / np.log(2.0)
+        cache = {}
+        for i, (s, hh, qb) in enumerate(items):
+            n = int(self.cu[s + 1] - self.cu[s])
+            if (s, hh) not in cache:
+                rr = (np.arange(n, dtype=np.int64) + int(self.cu[s])) * self.H + hh
+                kh = _round_bf16(self.prologue_rows(1, rr))
+                qh = _round_bf16(self.prologue_rows(0, rr) * mult)
+                nt = (n + 63) // 64
+                kbar = np.stack([kh[64 * t:64 * t + 64].mean(axis=0) for t in range(nt)])
+                cache = {(s, hh): (qh, kbar)}
+            qh, kbar = cache[(s, hh)]
+            qbar = qh[128 * qb:128 * qb + 128].mean(axis=0)
+            sc = kbar @ qbar
+            L = min(tiles_per_block, len(sc))
+            order = sorted(range(len(sc)), key=lambda t: (-sc[t], t))[:L]
+            out[i, :L] = sorted(order)
+            scores.append(sc)
+        return out, scores
+
     def token_pos(self, token: int):
         s, a = C.c_int32(), C.c_int32()
         pos = (C.c_int32 * 3)()
@@ -309,6 +394,13 @@ def out_proj(attn, w_o, cu_seqlens, gate=None, resid=None, rows=None, chunk: int
             y += _bf16_bits_to_f64(np.asarray(resid)[sl])
         out[i0:i0 + chunk] = y
     return out
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 values rounded to bf16 (to nearest, ties to even) and back, via fp32."""
+    f = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((f + np.uint32(0x7FFF) + ((f >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)) << np.uint32(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def _bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:

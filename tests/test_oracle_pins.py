@@ -547,3 +547,69 @@ def test_out_proj_identity_weight_gate_per_sequence():
     np.testing.assert_array_equal(got, want)
     np.testing.assert_array_equal(oracle.out_proj(a, eye, cu), _f(a))                   # gate 1, no residual
     np.testing.assert_array_equal(oracle.out_proj(a, eye, cu, gate=np.zeros((2, 8), np.float32), resid=r), _f(r))
+
+
+# ------------------------------------------------- block-sparse attention
+
+def _sparse_case(seed=60, rope=True):
+    seqs = [(2, 9, 11, 30), (1, 3, 5, 0)]                      # 228 and 15 tokens
+    return _problem(seqs, H=2, d=16, split=(4, 6, 6), seed=seed, rope=rope)
+
+
+def test_sparse_attention_keeping_every_tile_is_dense_attention():
+    p = _sparse_case()
+    rows = _all_rows(p)
+    items = p.sparse_items()
+    tiles = np.tile(np.arange(8, dtype=np.int32), (len(items), 1))   # 8 >= ceil(228 / 64)
+    np.testing.assert_allclose(p.sparse_attention_rows(rows, tiles, 8), p.attention_rows(rows), rtol=0, atol=1e-14)
+
+
+def test_sparse_attention_matches_torch_sdpa_on_kept_keys():
+    # a subset of tiles per query block: softmax over exactly the kept keys, against
+    # torch's fp64 SDPA on the gathered qhat / khat / v
+    p = _sparse_case(seed=61)
+    rng = np.random.default_rng(61)
+    items = p.sparse_items()
+    k = 2
+    tiles = np.full((len(items), k), -1, dtype=np.int32)
+    for i, (s, hh, qb) in enumerate(items):
+        n = int(p.cu[s + 1] - p.cu[s])
+        nt = (n + 63) // 64
+        tiles[i, :min(k, nt)] = np.sort(rng.choice(nt, min(k, nt), replace=False))
+    rows = _all_rows(p)
+    got = p.sparse_attention_rows(rows, tiles, k)
+    for i, (s, hh, qb) in enumerate(items):
+        n = int(p.cu[s + 1] - p.cu[s])
+        q_tok = np.arange(128 * qb, min(128 * qb + 128, n)) + int(p.cu[s])
+        kept = [int(t) for t in tiles[i] if t >= 0]
+        k_tok = np.concatenate([np.arange(64 * t, min(64 * t + 64, n)) for t in kept]) + int(p.cu[s])
+        qh = torch.from_numpy(p.prologue_rows(0, q_tok * p.H + hh))
+        kh = torch.from_numpy(p.prologue_rows(1, k_tok * p.H + hh))
+        vv = torch.from_numpy(p.value_rows(k_tok * p.H + hh))
+        want = F.scaled_dot_product_attention(qh[None], kh[None], vv[None], scale=p.scale)[0].numpy()
+        np.testing.assert_allclose(got[q_tok * p.H + hh], want, rtol=0, atol=1e-12)
+
+
+def test_sparse_select_closed_form_ranking():
+    # no RoPE, unit norm weights, q constant over the query block and k constant within each
+    # tile: qhat = sqrt(d) v/|v|, khat_t = sqrt(d) u_t/|u_t| with u_t = a_t v + b_t e (e orthogonal
+    # to v, |e| = |v|), so the pooled score ranks the tiles by a_t / sqrt(a_t^2 + b_t^2)
+    d, H = 16, 1
+    seqs = [(1, 8, 40, 0)]                                        # 320 tokens: 3 query blocks, 5 tiles
+    N = 320
+    v = np.zeros(d); v[0] = 1.0
+    e = np.zeros(d); e[1] = 1.0
+    cosines = np.array([0.2, 0.9, -0.5, 0.6, 0.95])
+    q = np.tile(v, (N, 1))
+    k = np.zeros((N, d))
+    for t in range(5):
+        a = cosines[t]
+        k[64 * t:64 * t + 64] = a * v + np.sqrt(1 - a * a) * e
+    w = np.ones((2, H, d), dtype=np.float32)
+    p = oracle.Problem(H, d, seqs, (4, 6, 6), _bf16(q[:, None, :]), _bf16(k[:, None, :]),
+                       _bf16(np.zeros((N, 1, d))), w, rope=False, library=L())
+    tiles, scores = p.sparse_select(3)
+    want = sorted(np.argsort(-cosines)[:3])                      # tiles 4, 1, 3
+    for i in range(tiles.shape[0]):
+        assert list(tiles[i]) == want
+        assert np.argmax(scores[i]) == 4
