@@ -63,7 +63,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLazyRescale = 8.0f;
 // Largest score bound (log2 units) for which the fixed shift is used.
 constexpr float kFixedShiftMax = 48.0f;
-template <int D>
+// SPARSE: visit only the 64-key tiles listed for this query block (block-sparse
+// attention, a.tiles); otherwise every tile of the sequence.
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 {
     constexpr int KSTEPS = D / 16;          // k-steps of the S^T product
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     // other, and need not wait for the fill before reading.
     __shared__ __attribute__((aligned(16))) uint16_t lk0[kTile * D], lk1[kTile * D];
     __shared__ __attribute__((aligned(16))) uint16_t lv0[D * kTile], lv1[D * kTile];
+    __shared__ int32_t ltiles[SPARSE ? kMaxSparseTiles : 1];     // the block's tile list
 
     // ---- work item: (sequence, head, 128-row query block)
     const int b = blockIdx.x;
@@ -100,7 +103,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 
     const uint16_t *kbase = a.khat + ((int64_t)head * a.Npad + off) * D;
     const uint16_t *vbase = a.vt + ((int64_t)head * (a.Npad / kTile) + off / kTile) * (D * kTile);
-    const int nt = (n + kTile - 1) / kTile;
+    const int ntk = (n + kTile - 1) / kTile;           // tiles of the sequence
+    int nt = ntk;                                     // tiles this block visits
+    if constexpr (SPARSE) {
+        // the list, clamped to the sequence's tiles, goes to LDS; each visit
+        // reads its entry back as a wave-uniform scalar
+        nt = min(a.tpb, ntk);
+        const int32_t *lst = a.tiles + ((int64_t)a.seq_item_base[si] + (int64_t)head * nqb + qb) * a.tpb;
+        for (int i = threadIdx.x; i < nt; i += 256) ltiles[i] = min(max(lst[i], 0), ntk - 1);
+        __syncthreads();
+    }
+    auto tix = [&](int j) -> int {
+        if constexpr (SPARSE)
+            return __builtin_amdgcn_readfirstlane(ltiles[j]);
+        else
+            return j;
+    };
     TileFill<kTile, KCPR> kfill;
     TileFill<D, 8> vfill;
     kfill.init(wave, lane);
@@ -110,11 +128,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     // buffer descriptors over this (sequence, head)'s padded K rows and V^T tiles
     const int tbytes = kTile * D * 2;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(kbase), 0, nt * tbytes, kBufferFlags);
+        const_cast<uint16_t *>(kbase), 0, ntk * tbytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(vbase), 0, nt * tbytes, kBufferFlags);
-    auto load_k = [&](int j, uint16_t *dst) { kfill.load(krs, (uint32_t)(j * tbytes), dst, wave); };
-    auto load_v = [&](int j, uint16_t *dst) { vfill.load(vrs, (uint32_t)(j * tbytes), dst, wave); };
+        const_cast<uint16_t *>(vbase), 0, ntk * tbytes, kBufferFlags);
+    auto load_k = [&](int j, uint16_t *dst) { kfill.load(krs, (uint32_t)(tix(j) * tbytes), dst, wave); };
+    auto load_v = [&](int j, uint16_t *dst) { vfill.load(vrs, (uint32_t)(tix(j) * tbytes), dst, wave); };
 
     f32x16 o[DB];
 #pragma unroll
@@ -148,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
         qn2 = row_sum2(qn2);
         const float *kn = a.knorm + (int64_t)head * (a.Npad / kTile) + off / kTile;
         float kmax = 0.f;
-        for (int i = lane; i < nt; i += 64) kmax = fmaxf(kmax, kn[i]);
+        for (int i = lane; i < ntk; i += 64) kmax = fmaxf(kmax, kn[i]);
 #pragma unroll
         for (int mm = 32; mm >= 1; mm >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, mm));
         const float mb = sqrtf(qn2) * kmax * (1.0f + 1.0f / 1024);
@@ -179,8 +197,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     // raise m_run when the tile exceeds it by more than kLazyRescale (always on
     // the first tile), rescaling O and l and shifting the tile's x.
     auto row_max_update = [&](int j, f32x16 &s0, f32x16 &s1, bool mask) {
-        const int valid = n - j * kTile;
-        if (mask && valid < kTile) {
+        // a sparse list may hold the sequence's partial last tile at any position
+        const int valid = n - tix(j) * kTile;
+        if ((mask || SPARSE) && valid < kTile) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -357,13 +376,27 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     }
 }
 
+// Explicit instantiations (the host pass emits launch stubs only for these).
+template __global__ void attn_bf16_kernel<64, false>(AttnArgs);
+template __global__ void attn_bf16_kernel<128, false>(AttnArgs);
+template __global__ void attn_bf16_kernel<64, true>(AttnArgs);
+template __global__ void attn_bf16_kernel<128, true>(AttnArgs);
+
 hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_t st)
 {
     if (nitems <= 0) return hipSuccess;
-    if (d == 128)
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)nitems), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)nitems), dim3(256), 0, st, a);
+    const dim3 grid((unsigned)nitems);
+    if (a.tiles) {
+        if (d == 128)
+            hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, dim3(256), 0, st, a);
+    } else {
+        if (d == 128)
+            hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ struct Plan {
     int32_t off[kMaxSeqs + 1];   // padded starts (multiples of kSeqPad)
     size_t qhat, khat, vt, knorm; // byte offsets into the workspace
     size_t q8, k8, v8t, qscale, kscale, ksum, vmax, kmean, vscale;
-    size_t bytes_bf16, bytes_q8;
+    size_t sp_kbar, sp_qsum, sp_cnt; // block-sparse selection scratch (after the bf16 regions)
+    size_t bytes_bf16, bytes_q8, bytes_sparse;
 };
 
 // Which sequence a padded 64-token tile belongs to: tiles of sequence s are
@@ -77,6 +78,36 @@ struct AttnArgs {
     int32_t seq_off[kMaxSeqs];
     int32_t seq_nqb[kMaxSeqs];
     int32_t item_pre[kMaxSeqs + 1];   // prefix sums of H * nqb
+    // block-sparse attention (null tiles: dense): tiles is int32
+    // [items][tpb] in the caller's item order (sequence, head, 128-row query
+    // block); seq_item_base is the caller's first item of each sequence above
+    const int32_t *tiles;
+    int32_t tpb;
+    int32_t seq_item_base[kMaxSeqs];
+};
+
+// Longest tile list (and longest sequence, in 64-key tiles) of the
+// block-sparse path.
+constexpr int kMaxSparseTiles = 2048;
+
+// Block-sparse tile selection (sparse_select.hip).  From the prologue's qhat'
+// and khat in the workspace: per (head, padded 64-token tile) the mean khat row
+// (kbar) and the sum of qhat' rows (qsum), and per tile its valid row count;
+// then per (sequence, head, 128-row query block) the tpb tiles with the
+// largest qbar . kbar, written ascending to tiles [items][tpb] (-1 past
+// min(tpb, tiles of the sequence)).
+struct SparseSelectArgs {
+    const uint16_t *qhat, *khat;     // workspace bf16 [H][Npad][d]
+    float *kbar, *qsum;              // fp32 kbar [H][d][ntiles] (channel-major), qsum [H][ntiles][d]
+    int32_t *cnt;                    // int32 [ntiles]
+    int32_t *tiles;
+    int32_t tpb;
+    int32_t H;
+    int64_t Npad;
+    int32_t ntiles;
+    SeqTable seq;
+    int32_t item_base[kMaxSeqs];     // first item of each sequence (caller order)
+    int32_t group_pre[kMaxSeqs + 1]; // prefix of H * ceil(nqb / 4): select workgroups per sequence
 };
 
 struct Q8Args {
@@ -177,6 +208,7 @@ hipError_t launch_attn_q8(const Q8AttnArgs &a, int d, int64_t nitems, hipStream_
 hipError_t launch_q8_export(const Q8ExportArgs &a, hipStream_t st);
 hipError_t launch_qkv_proj(const ProjArgs &a, int d, hipStream_t st);
 hipError_t launch_out_proj(const OutProjArgs &a, hipStream_t st);
+hipError_t launch_sparse_select(const SparseSelectArgs &a, int d, hipStream_t st);
 
 // Queries per workgroup of the attention kernels (work-item granularity).
 constexpr int kBlockM = 128;

@@ -94,6 +94,10 @@ h3attn_status make_plan(const h3attn_params *p, const int32_t *cu, Plan *pl)
     pl->vt = take(H * Np * d * 2);
     pl->knorm = take(H * T * 4);
     pl->bytes_bf16 = std::max<size_t>(at, 256);   // never 0: 0 reports an error
+    pl->sp_kbar = take(H * T * d * 4);
+    pl->sp_qsum = take(H * T * d * 4);
+    pl->sp_cnt = take(T * 4);
+    pl->bytes_sparse = std::max<size_t>(at, 256);
     at = 0;
     pl->q8 = take(H * Np * d);
     pl->k8 = take(H * Np * d);
@@ -237,12 +241,16 @@ size_t h3attn_workspace_size(const h3attn_params *p, const int32_t *cu_seqlens_h
 {
     Plan pl;
     if (make_plan(p, cu_seqlens_host, &pl) != H3ATTN_OK) return 0;
-    if (quantized && pl.d != 128) {
+    if (quantized == 1 && pl.d != 128) {
         fail(H3ATTN_ERR_UNSUPPORTED, "the quantised path needs head_dim 128");
         return 0;
     }
+    if (quantized < 0 || quantized > 2) {
+        fail(H3ATTN_ERR_INVALID_ARG, "quantized must be 0, 1 or 2 (got %d)", quantized);
+        return 0;
+    }
     ok();
-    return quantized ? pl.bytes_q8 : pl.bytes_bf16;
+    return quantized == 1 ? pl.bytes_q8 : quantized == 2 ? pl.bytes_sparse : pl.bytes_bf16;
 }
 
 h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -514,6 +522,115 @@ h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model
     a.S = num_seqs;
     for (int s = 0; s <= num_seqs; ++s) a.cu[s] = cu[s];
     return hip_status(launch_out_proj(a, static_cast<hipStream_t>(stream)), "output projection launch");
+}
+
+// Caller-order item bases of the block-sparse lists: items run sequence by
+// sequence, then head, then 128-row query block.
+static void sparse_item_base(const Plan &pl, int32_t *base, int64_t *total)
+{
+    int64_t at = 0;
+    for (int s = 0; s < pl.S; ++s) {
+        base[s] = (int32_t)at;
+        at += (int64_t)pl.H * ((pl.cu[s + 1] - pl.cu[s] + 127) / 128);
+    }
+    *total = at;
+}
+
+h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                       const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                                       int32_t tiles_per_block, int32_t *block_tiles, void *out, void *workspace,
+                                       size_t workspace_bytes, void *stream, int stages)
+{
+    Plan pl;
+    h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
+    if (st != H3ATTN_OK) return st;
+    if (stages < 1 || stages > 7) return fail(H3ATTN_ERR_INVALID_ARG, "stages must be in 1..7 (got %d)", stages);
+    if (tiles_per_block < 1 || tiles_per_block > kMaxSparseTiles)
+        return fail(H3ATTN_ERR_INVALID_ARG, "tiles_per_block must be in [1, %d] (got %d)", kMaxSparseTiles,
+                    tiles_per_block);
+    for (int s = 0; s < pl.S; ++s)
+        if ((pl.cu[s + 1] - pl.cu[s] + kTile - 1) / kTile > kMaxSparseTiles)
+            return fail(H3ATTN_ERR_UNSUPPORTED, "sequence %d has %d tokens; the sparse path takes at most %d", s,
+                        pl.cu[s + 1] - pl.cu[s], kMaxSparseTiles * kTile);
+    if (pl.N == 0) return ok();
+    if ((st = check_ptrs(q, k, v, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
+    if (!block_tiles) return fail(H3ATTN_ERR_INVALID_ARG, "block_tiles is NULL");
+    if (!aligned(block_tiles, 4)) return fail(H3ATTN_ERR_INVALID_ARG, "block_tiles is not 4-byte aligned");
+    if (!workspace) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(H3ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    const size_t need = (stages & 2) ? pl.bytes_sparse : pl.bytes_bf16;
+    if (workspace_bytes < need)
+        return fail(H3ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    int32_t base[kMaxSeqs];
+    int64_t nitems_caller;
+    sparse_item_base(pl, base, &nitems_caller);
+
+    PrologueArgs pa = prologue_args(p, pl, q, k, v, norm_w, rope_tables);
+    pa.qhat = reinterpret_cast<uint16_t *>(ws + pl.qhat);
+    pa.khat = reinterpret_cast<uint16_t *>(ws + pl.khat);
+    pa.vt = reinterpret_cast<uint16_t *>(ws + pl.vt);
+    pa.knorm = reinterpret_cast<float *>(ws + pl.knorm);
+    pa.out_hstride = pl.Npad * pl.d;
+    pa.out_tstride = pl.d;
+    pa.natural = 0;
+    pa.q_mult = scale_log2(p);
+    if (stages & 1)
+        if ((st = hip_status(launch_prologue(pa, pl.d, hs), "prologue launch")) != H3ATTN_OK) return st;
+
+    if (stages & 2) {
+        SparseSelectArgs sa;
+        std::memset(&sa, 0, sizeof sa);
+        sa.qhat = pa.qhat;
+        sa.khat = pa.khat;
+        sa.kbar = reinterpret_cast<float *>(ws + pl.sp_kbar);
+        sa.qsum = reinterpret_cast<float *>(ws + pl.sp_qsum);
+        sa.cnt = reinterpret_cast<int32_t *>(ws + pl.sp_cnt);
+        sa.tiles = block_tiles;
+        sa.tpb = tiles_per_block;
+        sa.H = pl.H;
+        sa.Npad = pl.Npad;
+        sa.ntiles = (int32_t)(pl.Npad / kTile);
+        sa.seq = seq_table(pl);
+        int64_t g = 0;
+        for (int s = 0; s < pl.S; ++s) {
+            sa.item_base[s] = base[s];
+            sa.group_pre[s] = (int32_t)g;
+            g += (int64_t)pl.H * (((pl.cu[s + 1] - pl.cu[s] + 127) / 128 + 3) / 4);
+        }
+        sa.group_pre[pl.S] = (int32_t)g;
+        if ((st = hip_status(launch_sparse_select(sa, pl.d, hs), "sparse selection launch")) != H3ATTN_OK)
+            return st;
+    }
+    if (!(stages & 4)) return ok();
+
+    AttnArgs aa;
+    std::memset(&aa, 0, sizeof aa);
+    aa.qhat = pa.qhat;
+    aa.khat = pa.khat;
+    aa.vt = pa.vt;
+    aa.knorm = pa.knorm;
+    aa.out = static_cast<uint16_t *>(out);
+    aa.o_stride = p->o_stride;
+    aa.Npad = pl.Npad;
+    aa.H = pl.H;
+    int32_t seq_idx[kMaxSeqs];
+    const int64_t items = order_work(pl, aa, seq_idx);
+    aa.tiles = block_tiles;
+    aa.tpb = tiles_per_block;
+    for (int i = 0; i < aa.nseq; ++i) aa.seq_item_base[i] = base[seq_idx[i]];
+    return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "sparse attention launch");
+}
+
+h3attn_status h3attn_fwd_sparse(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                                int32_t tiles_per_block, int32_t *block_tiles, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    return h3attn_fwd_sparse_stages(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, tiles_per_block, block_tiles,
+                                    out, workspace, workspace_bytes, stream, 7);
 }
 
 static h3attn_status q8_common(const h3attn_params *p, const void *q, const void *k, const void *v,

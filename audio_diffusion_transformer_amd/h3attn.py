@@ -26,7 +26,7 @@ H3ATTN_MAX_SEQS = 64
 
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
             "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
-            "h3attn_proj_prologue", "h3attn_out_proj",
+            "h3attn_proj_prologue", "h3attn_out_proj", "h3attn_fwd_sparse", "h3attn_fwd_sparse_stages",
             "h3attn_q8_prologue", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
@@ -74,6 +74,11 @@ def lib():
         L.h3attn_proj_prologue.restype = C.c_int
         L.h3attn_proj_prologue.argtypes = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp,
                                            P(C.c_int32), vp, vp, vp, vp]
+        sparse_args = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), C.c_int32, vp, vp, vp, C.c_size_t, vp]
+        L.h3attn_fwd_sparse.restype = C.c_int
+        L.h3attn_fwd_sparse.argtypes = sparse_args
+        L.h3attn_fwd_sparse_stages.restype = C.c_int
+        L.h3attn_fwd_sparse_stages.argtypes = sparse_args + [C.c_int]
         L.h3attn_out_proj.restype = C.c_int
         L.h3attn_out_proj.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, P(C.c_int32), vp, C.c_int64,
                                       vp, vp, vp, C.c_int64, vp, C.c_int64, vp]
@@ -128,9 +133,10 @@ def _cu_ptr(cu: np.ndarray):
     return cu.ctypes.data_as(C.POINTER(C.c_int32))
 
 
-def h3attn_workspace_size(params: h3attn_params, cu_seqlens, quantized: bool = False) -> int:
+def h3attn_workspace_size(params: h3attn_params, cu_seqlens, quantized=False) -> int:
+    """Workspace bytes: quantized False/0 bf16, True/1 quantised, 2 bf16 plus the sparse selection."""
     cu = _cu_array(cu_seqlens)
-    n = int(lib().h3attn_workspace_size(C.byref(params), _cu_ptr(cu), 1 if quantized else 0))
+    n = int(lib().h3attn_workspace_size(C.byref(params), _cu_ptr(cu), int(quantized)))
     if n == 0:
         raise H3AttnError(H3ATTN_ERR_INVALID_ARG, last_error())
     return n
@@ -278,6 +284,47 @@ def h3attn_proj_prologue(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: i
                                       _dev_ptr(norm_w), _dev_ptr(rope_tables), _cu_ptr(cu),
                                       *[_dev_ptr(t) for t in res], _stream_ptr(stream)))
     return tuple(res)
+
+
+def sparse_items(cu_seqlens, num_heads: int) -> int:
+    """Rows of the block-sparse tile lists: sum over sequences of H * ceil(n_s / 128)."""
+    cu = _cu_array(cu_seqlens)
+    return int(sum(num_heads * ((int(cu[s + 1] - cu[s]) + 127) // 128) for s in range(len(cu) - 1)))
+
+
+def sparse_raw(params, q, k, v, norm_w, rope_tables, cu_seqlens, tiles_per_block: int, block_tiles, out,
+               workspace, workspace_bytes, stream, stages: int = 7) -> int:
+    """Direct call of h3attn_fwd_sparse_stages with integer device pointers; returns the status."""
+    cu = _cu_array(cu_seqlens)
+    return int(lib().h3attn_fwd_sparse_stages(C.byref(params), q, k, v, norm_w, rope_tables, _cu_ptr(cu),
+                                              int(tiles_per_block), block_tiles, out, workspace, workspace_bytes,
+                                              stream, int(stages)))
+
+
+def h3attn_fwd_sparse(q, k, v, norm_w, rope_tables, cu_seqlens, tiles_per_block: int, block_tiles=None,
+                      select: bool = True, out=None, workspace=None, eps: float = 1e-6, softmax_scale: float = 0.0,
+                      stream=None):
+    """Block-sparse attention (include/h3attn.h).  With select, the kept tiles
+    are chosen by pooled score and written to block_tiles (allocated when
+    None); otherwise block_tiles [items, tiles_per_block] (int32, device) is
+    the caller's list.  Returns (out, block_tiles)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    cu = _cu_array(cu_seqlens)
+    params = params_for(q, k, v, out, len(cu) - 1, eps, softmax_scale)
+    N, H, d = q.shape
+    if block_tiles is None:
+        if not select:
+            raise ValueError("block_tiles is needed when select is False")
+        block_tiles = torch.empty((sparse_items(cu, H), tiles_per_block), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(h3attn_workspace_size(params, cu, 2 if select else 0), dtype=torch.uint8,
+                                device=q.device)
+    _check(sparse_raw(params, _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w), _dev_ptr(rope_tables), cu,
+                      tiles_per_block, _dev_ptr(block_tiles), _dev_ptr(out), _dev_ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream_ptr(stream), 7 if select else 5))
+    return out, block_tiles
 
 
 def out_proj_raw(num_heads: int, head_dim: int, model_dim: int, cu_seqlens, attn, attn_stride: int, w_o, gate,

@@ -100,9 +100,60 @@ def one_head_problem(w, inputs, head: int):
     return w1, oracle.Problem.from_projection(w1, sub)
 
 
+def cpu_baseline_sparse(w, inputs, seconds: float, threads: int):
+    """Time the fp64 CPU oracle of the block-sparse path on one head: its own
+    tile selection for that head, then sampled query rows over their kept keys."""
+    import oracle
+    rng = np.random.default_rng(w.seed + 99)
+    head = int(rng.integers(w.H))
+    sub = {key: np.ascontiguousarray(inputs[key][:, [head]]) for key in ("q", "k", "v")}
+    sub["norm_w"] = np.ascontiguousarray(inputs["norm_w"][:, [head]])
+    p = oracle.Problem.from_workload(w.replace(H=1), sub)
+    t0 = time.perf_counter()
+    tiles, _ = p.sparse_select(w.keep_tiles)
+    sel_s = time.perf_counter() - t0
+    n = w.seqs[0].n
+    nt = (n + 63) // 64
+    keys_per_block = [int(np.minimum(64, n - 64 * tiles[qb, :min(w.keep_tiles, nt)].astype(np.int64)).sum())
+                      for qb in range(tiles.shape[0])]
+
+    nqb = (n + 127) // 128
+
+    def run(nblocks):
+        # whole query blocks: the kept keys' khat is formed once per block, as in a full run
+        blocks = np.sort(rng.choice(nqb, size=nblocks, replace=False))
+        toks = np.concatenate([np.arange(128 * qb, min(128 * qb + 128, n)) for qb in blocks]).astype(np.int64)
+        t1 = time.perf_counter()
+        p.sparse_attention_rows(toks, tiles, w.keep_tiles, nthreads=threads)
+        return time.perf_counter() - t1, toks
+
+    t_probe, _ = run(1)
+    nb = int(max(1, min(nqb, seconds / max(t_probe, 1e-6))))
+    t, toks = run(nb)
+    nrows = len(toks)
+    flops = sum(4.0 * w.d * keys_per_block[int(tk) // 128] for tk in toks)
+    t += sel_s * nrows / n                 # the head's selection, spread over its rows
+    value = flops / t / 1e12
+    return {
+        "value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "cpu_model": cpu_model(),
+        "extrapolated_full_s": round(sparse_total_flops_estimate(w, keys_per_block) / (value * 1e12), 1),
+        "kind": "oracle",
+        "sample": "%d query rows (%d whole 128-row blocks) of head %d (of %d x %d rows), each over the keys of "
+                  "the %d tiles the oracle keeps for its block; fp64; the head's pooled-score selection (%.1f s) "
+                  "spread over its rows; %.1f s" % (nrows, nb, head, w.N, w.H, w.keep_tiles, sel_s, t),
+    }
+
+
+def sparse_total_flops_estimate(w, keys_per_block) -> float:
+    n = w.seqs[0].n
+    return float(sum(4.0 * w.d * min(128, n - 128 * qb) * k for qb, k in enumerate(keys_per_block))) * w.H
+
+
 def cpu_baseline(w, inputs, seconds: float, threads: int):
     """Time the fp64 CPU oracle on sampled query rows of one head (full key set)."""
     import oracle
+    if w.keep_tiles > 0:
+        return cpu_baseline_sparse(w, inputs, seconds, threads)
     rng = np.random.default_rng(w.seed + 99)
     head = int(rng.integers(w.H))
     n = w.seqs[0].n
@@ -193,6 +244,43 @@ def library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_byte
             "unfused_total_ms": round(g + p, 4)}
 
 
+def sparse_flops(w, tiles) -> float:
+    """4 * d * (query rows) * (kept keys) summed over the (sequence, head, query
+    block) items of the tile lists: the attention work the sparse kernel does."""
+    total, it = 0.0, 0
+    for s in w.seqs:
+        n = s.n
+        nt = (n + 63) // 64
+        L = min(w.keep_tiles, nt)
+        for _ in range(w.H):
+            for qb in range((n + 127) // 128):
+                rows = min(128, n - 128 * qb)
+                kept = tiles[it, :L].astype(np.int64)
+                keys = np.minimum(64, n - 64 * kept).sum()
+                total += 4.0 * w.d * rows * float(keys)
+                it += 1
+    return total
+
+
+def dense_attention_ms(torch, h, w, params, ptrs, cu, out, ws, ws_bytes, stream, reps: int = 3) -> float:
+    """The dense attention kernel on the same inputs (after the timed region),
+    for the speed-up of the block-sparse one."""
+    def run():
+        st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, int(stream.cuda_stream), False, 2)
+        if st != 0:
+            raise RuntimeError(h.last_error())
+    h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, int(stream.cuda_stream), False, 1)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def library_out_proj(torch, w, attn, w_o, gate, resid, stream, reps: int = 5):
     """The unfused output projection, timed after the timed region: torch.mm
     (hipBLASLt) of the attention output by W_o^T, then the gated residual as
@@ -244,6 +332,7 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     proj = w.model_dim > 0
+    sparse = w.keep_tiles > 0
     t0 = time.time()
     inp = synth.generate(w)
     dev = torch.device("cuda:0")
@@ -267,7 +356,9 @@ def main():
         q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
         params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
         ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
-    ws_bytes = h.h3attn_workspace_size(params, cu, w.quantized)
+    ws_bytes = h.h3attn_workspace_size(params, cu, 2 if sparse else int(w.quantized))
+    if sparse:
+        tiles = torch.empty((h.sparse_items(cu, w.H), w.keep_tiles), dtype=torch.int32, device=dev)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
@@ -286,7 +377,11 @@ def main():
         del src, dst
 
     def stage(sid):
-        if proj and sid == 4:
+        if sparse:
+            # 1 prologue, 2 tile selection, 4 attention over the kept tiles
+            st = h.sparse_raw(params, *ptrs, cu, w.keep_tiles, tiles.data_ptr(), out.data_ptr(), ws.data_ptr(),
+                              ws_bytes, sp, sid)
+        elif proj and sid == 4:
             st = h.out_proj_raw(w.H, w.d, w.model_dim, cu, out.data_ptr(), out.stride(0), w_o.data_ptr(),
                                 gate.data_ptr(), resid.data_ptr(), resid.stride(0), y.data_ptr(), y.stride(0), sp)
         elif proj:
@@ -298,12 +393,18 @@ def main():
         if st != 0:
             raise RuntimeError("%s: %s" % (h.status_string(st), h.last_error()))
 
-    nst = 3 if proj else 2                  # launches per step: [projection or prologue,] attention[, output projection]
+    # launches per step: projection or prologue, [tile selection,] attention, [output projection]
+    nst = 3 if (proj or sparse) else 2
+    seq_ids = (1, 2, 4) if sparse else (1, 2, 4) if proj else (1, 2)
+
+    def step_launch(i=None):
+        for k_, sid in enumerate(seq_ids):
+            stage(sid)
+            if i is not None:
+                ev[i][k_ + 1].record(stream)
+
     for _ in range(args.warmup):
-        stage(1)
-        stage(2)
-        if proj:
-            stage(4)
+        step_launch()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -312,22 +413,18 @@ def main():
     wall0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        stage(1)
-        ev[i][1].record(stream)
-        stage(2)
-        ev[i][2].record(stream)
-        if proj:
-            stage(4)
-            ev[i][3].record(stream)
+        step_launch(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = ev[0][0].elapsed_time(ev[K - 1][nst])
     pro_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    att_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ai = 2 if sparse else 1                 # events bracketing the attention launch
+    att_ms = [ev[i][ai].elapsed_time(ev[i][ai + 1]) for i in range(K)]
     ms_step = total_ms / K
     att_avg = float(np.mean(att_ms))
     pro_avg = float(np.mean(pro_ms))
     outp_avg = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])) if proj else 0.0
+    sel_avg = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])) if sparse else 0.0
     step_ms = [ev[i][0].elapsed_time(ev[i][nst]) for i in range(K)]
     copy_gbps = device_copy_rate(torch, dev)        # after the timed region
     print("[bench] %d steps: %.3f ms/step (attention %.3f, %s %.3f), wall %.3f s" % (
@@ -336,11 +433,16 @@ def main():
     if proj:
         unfused.update(library_out_proj(torch, w, out, w_o, gate, resid, stream))
     out_flops = 2.0 * w.N * w.H * w.d * w.model_dim if proj else 0.0
+    attn_flops = w.flops()
+    dense_att = None
+    if sparse:
+        attn_flops = sparse_flops(w, tiles.cpu().numpy())
+        dense_att = dense_attention_ms(torch, h, w, params, ptrs, cu, out, ws, ws_bytes, stream)
 
-    flops = w.flops() + w.proj_flops() + out_flops
+    flops = attn_flops + w.proj_flops() + out_flops
     value = flops / (ms_step * 1e-3) / 1e12
     peak = MI355X_FP8_DENSE_TFLOPS if w.quantized else MI355X_BF16_DENSE_TFLOPS
-    achieved = w.flops() / (att_avg * 1e-3) / 1e12
+    achieved = attn_flops / (att_avg * 1e-3) / 1e12
     kernel_file = "q8.hip" if w.quantized else "attn_bf16.hip"
     summary = ("attn_q8_%s_pmc.md" if w.quantized else "attn_bf16_%s_pmc.md") % w.name
     traffic = measured_traffic(kernel_file, summary)
@@ -361,6 +463,9 @@ def main():
         pro_bytes = 3 * N * H * d * 2 + 3 * N * H * d * 2 + N * (d // 2) * 8
         metric = METRIC if w.name == "joint" else (
             "attention TFLOP/s and %% of bf16 MFMA peak at N=%d packed tokens, H=%d, d=%d" % (N, H, d))
+        if sparse:
+            metric = ("block-sparse attention TFLOP/s of the computed (kept) work, %d of the 64-key tiles kept "
+                      "per 128-row query block, at N=%d packed tokens, H=%d, d=%d" % (w.keep_tiles, N, H, d))
     res = {
         "metric": metric,
         "value": round(value, 3),
@@ -392,6 +497,15 @@ def main():
                     "attention_avg_ms": round(att_avg, 4)},
         "cpu_baseline": None,
     }
+    if sparse:
+        res["kernels"].update({
+            "selection_avg_ms": round(sel_avg, 4),
+            "kept_fraction": round(attn_flops / w.flops(), 4),
+            "dense_attention_ms": round(dense_att, 4),
+            "speedup_vs_dense_step": round((pro_avg + dense_att) / ms_step, 3)})
+        res["roofline"]["kernel"] = "attn_bf16_kernel<128, sparse>"
+        res["roofline"]["traffic"] = None
+        res["config"]["keep_tiles"] = w.keep_tiles
     if proj:
         pf = w.proj_flops() / (pro_avg * 1e-3) / 1e12
         kern = res["kernels"]

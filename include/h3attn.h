@@ -73,8 +73,9 @@ typedef struct h3attn_params {
 } h3attn_params;
 
 /*
- * Bytes of device workspace h3attn_fwd (quantized = 0) or h3attn_fwd_q8
- * (quantized = 1) needs for this shape.  cu_seqlens_host: HOST int32 [S+1],
+ * Bytes of device workspace h3attn_fwd (quantized = 0), h3attn_fwd_q8
+ * (quantized = 1) or h3attn_fwd_sparse with its tile selection (quantized = 2)
+ * needs for this shape.  cu_seqlens_host: HOST int32 [S+1],
  * cu[0] = 0, non-decreasing; N = cu[S] is the packed token count.  Returns 0
  * and sets the last error when the arguments are invalid.
  */
@@ -239,6 +240,45 @@ h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model
                               const int32_t *cu_seqlens_host, const void *attn, int64_t attn_stride,
                               const void *w_o, const float *gate, const void *resid, int64_t resid_stride,
                               void *out, int64_t out_stride, void *stream);
+
+/*
+ * Block-sparse attention: each 128-row query block attends to a kept subset of
+ * its sequence's 64-key tiles, softmax over the kept keys only.  The page
+ * "Open-H3-Regenerate-2K" ("Speed on one B200 (GB200)", per-module table)
+ * credits a sparse attention backend with most of a refine's speed-up over
+ * dense attention and calls it lossy; the pages give no algorithm.  Here:
+ *  - block_tiles: device int32 [items][tiles_per_block], items in the order
+ *    sequence, then head, then 128-row query block (items = sum over sequences
+ *    of H * ceil(n_s / 128)).  Of each row the first
+ *    L = min(tiles_per_block, ceil(n_s / 64)) entries are tile indices within
+ *    the sequence (tile t = its tokens 64t .. 64t+63), distinct; the rest are
+ *    ignored.  Out-of-range entries are clamped to the sequence's tiles.
+ *  - stages (bit mask): 1 the RMSNorm + RoPE prologue into the workspace (as
+ *    h3attn_fwd_stages stage 1); 2 the tile selection, which writes
+ *    block_tiles: for every item the L tiles with the largest dot product of
+ *    the query block's mean stored qhat' row and the tile's mean khat row
+ *    (ties to the lower index), ascending, -1 after them; 4 the attention over
+ *    the listed tiles.  Stage 2 needs workspace_bytes >=
+ *    h3attn_workspace_size(p, cu, 2), the others h3attn_workspace_size(p, cu, 0);
+ *    a later stage reads what an earlier call left in the same workspace and
+ *    stream.  Callers with their own lists use stages 1 | 4.
+ *  - tiles_per_block in [1, 2048]; every sequence at most 2048 tiles (131,072
+ *    tokens), else H3ATTN_ERR_UNSUPPORTED.
+ * Other arguments and conventions as h3attn_fwd.  Keeping every tile
+ * (tiles_per_block >= the longest sequence's tile count) gives dense attention.
+ */
+h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                       const float *norm_w, const float *rope_tables,
+                                       const int32_t *cu_seqlens_host, int32_t tiles_per_block,
+                                       int32_t *block_tiles, void *out, void *workspace, size_t workspace_bytes,
+                                       void *stream, int stages);
+
+/* h3attn_fwd_sparse_stages(..., 7): prologue, tile selection into block_tiles,
+ * sparse attention. */
+h3attn_status h3attn_fwd_sparse(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                                int32_t tiles_per_block, int32_t *block_tiles, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Host helpers that fill RoPE tables (fp32 (cos, sin) pairs) on the host.

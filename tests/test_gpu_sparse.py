@@ -1,0 +1,161 @@
+"""GPU parity of the block-sparse attention (h3attn_fwd_sparse_stages).
+
+- Every tile kept: the sparse kernel visits the same tiles in the same order
+  as the dense one, so its output is bit-identical to h3attn_fwd (and meets
+  the oracle's bf16 gates).
+- Caller lists (the oracle's inputs, from a seeded generator): random subsets
+  of tiles per (sequence, head, query block), in random order, including the
+  sequence's partial last tile, compared on every row with the oracle's
+  softmax over exactly the kept keys.
+- Selection: the tiles the GPU keeps against the oracle's pooled-score top-k.
+  The GPU scores in fp32 and the oracle in fp64 from the same stored bf16
+  values, so a tile may differ only where the oracle's scores of the two
+  tiles involved are within 1e-3 relative of each other (a near tie); the
+  attention over the GPU's selection is then checked on the rows whose lists
+  agree.
+- The 125,242-token joint shape with 25% of the tiles kept, on two heads.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from audio_diffusion_transformer_amd import h3attn as h
+from audio_diffusion_transformer_amd import synth
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+Seq = synth.Seq
+
+SMALL = {
+    "sparse_ragged": synth.Workload("sparse_ragged", H=2, d=128, seqs=(Seq(3, 10, 11, 7), Seq(0, 1, 1), Seq(1, 4, 5, 70)),
+                                    split=(32, 48, 48), k_offset_std=0.5, seed=51),
+    "sparse_long_d64": synth.Workload("sparse_long_d64", H=2, d=64, seqs=(Seq(5, 16, 20, 33),), split=(16, 24, 24),
+                                      seed=52),
+}
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+def _run_sparse(torch, w, t, tpb, tiles=None, select=True, label=""):
+    G.announce("sparse %s N=%d H=%d d=%d tiles_per_block=%d select=%s" % (label, w.N, w.H, w.d, tpb, select))
+    bt = None if tiles is None else torch.from_numpy(np.ascontiguousarray(tiles, dtype=np.int32)).to("cuda:0")
+    out, bt = h.h3attn_fwd_sparse(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], tpb, block_tiles=bt,
+                                  select=select, eps=w.eps)
+    torch.cuda.synchronize()
+    return G.bits(out), bt.cpu().numpy()
+
+
+def _random_lists(w, tpb, seed):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for s in w.seqs:
+        n = s.n
+        nt = (n + 63) // 64
+        for _ in range(w.H):
+            for _ in range((n + 127) // 128):
+                L = min(tpb, nt)
+                pick = rng.choice(nt, L, replace=False)
+                if nt - 1 not in pick and L > 1 and rng.random() < 0.5:
+                    pick[rng.integers(L)] = nt - 1           # often include the partial last tile
+                row = np.full(tpb, -1, dtype=np.int32)
+                row[:L] = pick                                # random order
+                rows.append(row)
+    return np.stack(rows) if rows else np.zeros((0, tpb), np.int32)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_all_tiles_kept_is_dense_attention(torch_dev, name):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    dense = G.bits(G.run(w, t, label=name + " dense"))
+    nt_max = max((s.n + 63) // 64 for s in w.seqs)
+    items = h.sparse_items(inp["cu_seqlens"], w.H)
+    tiles = np.tile(np.arange(nt_max, dtype=np.int32), (items, 1))
+    got, _ = _run_sparse(torch_dev, w, t, nt_max, tiles=tiles, select=False, label=name + " all tiles")
+    assert np.array_equal(got, dense)
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    ref = oracle.Problem.from_workload(w, inp).attention_rows(rows, nthreads=G.oracle_threads())
+    G.check(G.metrics(G.gpu_rows(got, rows, w.H), ref), G.BF16_GATE, name + " all tiles")
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("tpb", [1, 3])
+def test_caller_lists_all_rows(torch_dev, name, tpb):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    tiles = _random_lists(w, tpb, seed=tpb * 100 + len(name))
+    got, _ = _run_sparse(torch_dev, w, t, tpb, tiles=tiles, select=False, label="%s caller lists" % name)
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    ref = oracle.Problem.from_workload(w, inp).sparse_attention_rows(rows, tiles, tpb, nthreads=G.oracle_threads())
+    G.check(G.metrics(G.gpu_rows(got, rows, w.H), ref), G.BF16_GATE, "%s tpb=%d" % (name, tpb))
+
+
+def _compare_selection(gpu, ref, scores, label):
+    """Identical lists except near ties; returns the mask of items whose lists agree."""
+    same = np.all(gpu == ref, axis=1)
+    for i in np.nonzero(~same)[0]:
+        g = set(int(x) for x in gpu[i] if x >= 0)
+        r = set(int(x) for x in ref[i] if x >= 0)
+        assert len(g) == len(r), "%s item %d: %d tiles against %d" % (label, i, len(g), len(r))
+        sc = scores[i]
+        worst_kept = min(sc[t] for t in r)
+        for t in g - r:                       # the GPU kept t, the oracle a tile scoring at least as well
+            assert sc[t] >= worst_kept - 1e-3 * max(abs(worst_kept), 1e-30), \
+                "%s item %d: tile %d (score %.6g) kept, oracle's k-th score %.6g" % (label, i, t, sc[t], worst_kept)
+    assert same.mean() > 0.9, "%s: only %.3f of the lists agree" % (label, same.mean())
+    return same
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_selection_and_attention_over_it(torch_dev, name):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    tpb = 2
+    got, lists = _run_sparse(torch_dev, w, t, tpb, select=True, label=name + " select")
+    p = oracle.Problem.from_workload(w, inp)
+    ref_lists, scores = p.sparse_select(tpb)
+    same = _compare_selection(lists, ref_lists, scores, name)
+    items = p.sparse_items()
+    rows = np.array([tok * w.H + hh for i, (s, hh, qb) in enumerate(items) if same[i]
+                     for tok in range(int(p.cu[s]) + 128 * qb, min(int(p.cu[s]) + 128 * qb + 128, int(p.cu[s + 1])))],
+                    dtype=np.int64)
+    ref = p.sparse_attention_rows(rows, ref_lists, tpb, nthreads=G.oracle_threads())
+    G.check(G.metrics(G.gpu_rows(got, rows, w.H), ref), G.BF16_GATE, name + " selected")
+
+
+def test_full_size_two_heads(torch_dev):
+    w = synth.WORKLOADS["sparse_joint"]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    got, lists = _run_sparse(torch_dev, w, t, w.keep_tiles, select=True, label="sparse_joint")
+    del t
+    heads = [3, 17]
+    sub = {key: np.ascontiguousarray(inp[key][:, heads]) for key in ("q", "k", "v")}
+    sub["norm_w"] = np.ascontiguousarray(inp["norm_w"][:, heads])
+    ws = w.replace(H=len(heads))
+    p = oracle.Problem.from_workload(ws, sub)
+    ref_lists, scores = p.sparse_select(w.keep_tiles)
+    nqb = (w.N + 127) // 128
+    gl = np.concatenate([lists[hh * nqb:(hh + 1) * nqb] for hh in heads])
+    same = _compare_selection(gl, ref_lists, scores, "sparse_joint")
+    rng = np.random.default_rng(12)
+    items = np.nonzero(same)[0]
+    pick = np.sort(rng.choice(items, 64, replace=False))
+    rows = []
+    for i in pick:
+        j, qb = divmod(int(i), nqb)
+        toks = rng.choice(np.arange(128 * qb, min(128 * qb + 128, w.N)), 8, replace=False)
+        rows += [int(tk) * len(heads) + j for tk in toks]
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ref = p.sparse_attention_rows(rows, ref_lists, w.keep_tiles, nthreads=G.oracle_threads())
+    tok, j = rows // len(heads), rows % len(heads)
+    gotr = G.decode(got[tok, np.array(heads)[j]])
+    G.check(G.metrics(gotr, ref), G.BF16_GATE, "sparse_joint sampled")
