@@ -287,3 +287,42 @@ def test_out_proj_empty_input_and_null_gate_residual():
     assert _out_call(cu=(0, 0), ptrs={"attn": 0, "w": 0, "out": 0}) == h.H3ATTN_OK
     if not _gpu_present():
         assert _out_call(ptrs={"gate": 0, "resid": 0}) == h.H3ATTN_ERR_DEVICE   # valid up to the device check
+
+
+def _sparse_call(params=None, cu=(0, 1000), tpb=4, ws_bytes=1 << 40, ptrs=None, stages=7):
+    params = params if params is not None else _params()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, norm_w=FAKE, rope=FAKE, out=FAKE, ws=FAKE * 256, tiles=FAKE * 8)
+    p.update(ptrs or {})
+    return h.sparse_raw(params, p["q"], p["k"], p["v"], p["norm_w"], p["rope"], np.array(cu, np.int32), tpb,
+                        p["tiles"], p["out"], p["ws"], ws_bytes, None, stages)
+
+
+@pytest.mark.parametrize("kw,msg,code", [
+    (dict(tpb=0), "tiles_per_block", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(tpb=2049), "tiles_per_block", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(cu=(0, 131073)), "at most", h.H3ATTN_ERR_UNSUPPORTED),
+    (dict(stages=0), "stages", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(stages=8), "stages", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"tiles": 0}), "block_tiles", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"tiles": FAKE + 2}), "aligned", h.H3ATTN_ERR_INVALID_ARG),
+    (dict(ptrs={"ws": 0}), "workspace", h.H3ATTN_ERR_WORKSPACE),
+    (dict(ptrs={"q": 0}), "NULL", h.H3ATTN_ERR_INVALID_ARG),
+])
+def test_sparse_argument_errors(kw, msg, code):
+    assert _sparse_call(**kw) == code
+    assert msg in h.last_error()
+
+
+def test_sparse_workspace_sizes():
+    p = _params()
+    dense = h.h3attn_workspace_size(p, [0, 1000])
+    with_select = h.h3attn_workspace_size(p, [0, 1000], 2)
+    npad, tiles = 1024, 16
+    assert with_select - dense >= 2 * 24 * tiles * 128 * 4 + tiles * 4     # pooled k means, q sums, counts
+    # the selection stage needs the larger workspace, the others the bf16 one
+    assert _sparse_call(ws_bytes=dense, stages=2) == h.H3ATTN_ERR_WORKSPACE and "needs" in h.last_error()
+    if not _gpu_present():
+        assert _sparse_call(ws_bytes=dense, stages=5) == h.H3ATTN_ERR_DEVICE
+    assert h.sparse_items([0, 1000, 1000, 1129], 24) == 24 * 8 + 24 * 2
+    with pytest.raises(h.H3AttnError):
+        h.h3attn_workspace_size(p, [0, 1000], 3)
