@@ -93,6 +93,23 @@ def _bind(L):
     L.orc_q8_attention_rows.restype = C.c_int
     L.orc_q8_attention_rows.argtypes = [P(_Problem), P(C.c_int64), C.c_int64, P(C.c_double),
                                         P(C.c_double), C.c_int]
+    L.orc_e2m1_encode.restype = C.c_uint8
+    L.orc_e2m1_encode.argtypes = [C.c_double]
+    L.orc_e2m1_decode.restype = C.c_double
+    L.orc_e2m1_decode.argtypes = [C.c_uint8]
+    L.orc_mx_scale_exp.restype = C.c_int
+    L.orc_mx_scale_exp.argtypes = [C.c_double]
+    L.orc_mx_block.restype = C.c_int
+    L.orc_mx_block.argtypes = [P(C.c_double), C.c_int, P(C.c_uint8)]
+    L.orc_mx_qk_quant.restype = C.c_int
+    L.orc_mx_qk_quant.argtypes = [P(_Problem), C.c_int, C.c_int32, C.c_int32, P(C.c_double),
+                                  P(C.c_uint8), P(C.c_int32), C.c_int]
+    L.orc_mx_v_quant.restype = C.c_int
+    L.orc_mx_v_quant.argtypes = [P(_Problem), C.c_int32, C.c_int32, P(C.c_uint8), P(C.c_int32)]
+    L.orc_mx_softmax_pv.argtypes = [P(C.c_double), C.c_int64, P(C.c_double), C.c_int, P(C.c_double)]
+    L.orc_mx_attention_rows.restype = C.c_int
+    L.orc_mx_attention_rows.argtypes = [P(_Problem), P(C.c_int64), C.c_int64, P(C.c_double),
+                                        P(C.c_double), C.c_int]
     L.orc_e4m3_encode.restype = C.c_uint8
     L.orc_e4m3_encode.argtypes = [C.c_double]
     L.orc_e4m3_decode.restype = C.c_double
@@ -323,6 +340,81 @@ class Problem:
         self.L.orc_q8_v_quant(C.byref(self.pr), int(seq), int(head), _ptr(scale, C.c_double),
                               _ptr(ratio, C.c_double), _ptr(codes, C.c_uint8))
         return scale, ratio[:n], codes[:n]
+
+    # -- MXFP4 path stages --------------------------------------------------
+    def mx_qk_quant(self, which: int, seq: int, head: int, kmean=None, nthreads: int = 0):
+        """MXFP4 codes [n, d] (uint8, one code per byte) and scale exponents
+        [n, d/32] of qhat (which 0) or khat - kmean (which 1) of one sequence
+        and head (orc_mx_qk_quant)."""
+        n = int(self.cu[seq + 1] - self.cu[seq])
+        codes = np.zeros((max(n, 1), self.d), dtype=np.uint8)
+        exps = np.zeros((max(n, 1), self.d // 32), dtype=np.int32)
+        km = None
+        if which == 1:
+            km = np.ascontiguousarray(self.q8_kmean(nthreads) if kmean is None else kmean, dtype=np.float64)
+        st = self.L.orc_mx_qk_quant(C.byref(self.pr), int(which), int(seq), int(head),
+                                    _ptr(km, C.c_double) if km is not None else None,
+                                    _ptr(codes, C.c_uint8), _ptr(exps, C.c_int32), int(nthreads))
+        if st < 0:
+            raise ValueError("oracle: bad MXFP4 quantisation request")
+        return codes[:n], exps[:n]
+
+    def mx_v_quant(self, seq: int, head: int):
+        """MXFP4 codes [n, d] and scale exponents [ceil(n/32), d] of raw v of
+        one sequence and head, blocks of 32 tokens (orc_mx_v_quant)."""
+        n = int(self.cu[seq + 1] - self.cu[seq])
+        nb = (n + 31) // 32
+        codes = np.zeros((max(n, 1), self.d), dtype=np.uint8)
+        exps = np.zeros((max(nb, 1), self.d), dtype=np.int32)
+        st = self.L.orc_mx_v_quant(C.byref(self.pr), int(seq), int(head), _ptr(codes, C.c_uint8),
+                                   _ptr(exps, C.c_int32))
+        if st < 0:
+            raise ValueError("oracle: bad MXFP4 quantisation request")
+        return codes[:n], exps[:nb]
+
+    def mx_attention_rows(self, rows, nthreads: int = 0, kmean=None) -> np.ndarray:
+        """Output rows of the FP4 path taken step by step (orc_mx_attention_rows)."""
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        km = np.ascontiguousarray(self.q8_kmean(nthreads) if kmean is None else kmean, dtype=np.float64)
+        out = np.zeros((len(rows), self.d), dtype=np.float64)
+        st = self.L.orc_mx_attention_rows(C.byref(self.pr), _ptr(rows, C.c_int64), len(rows),
+                                          _ptr(km, C.c_double), _ptr(out, C.c_double), int(nthreads))
+        if st != 0:
+            raise ValueError("oracle: row outside every sequence")
+        return out
+
+
+def mx_softmax_pv(x, vdec, library=None) -> np.ndarray:
+    """The FP4 path's softmax and P.V for one row: log2-unit scores x [n],
+    decoded V [n, d] (see orc_mx_softmax_pv)."""
+    L = library or lib()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    vdec = np.ascontiguousarray(vdec, dtype=np.float64)
+    n, d = vdec.shape
+    out = np.zeros(d, dtype=np.float64)
+    L.orc_mx_softmax_pv(_ptr(x, C.c_double), n, _ptr(vdec, C.c_double), d, _ptr(out, C.c_double))
+    return out
+
+
+def e2m1_encode(x: float, library=None) -> int:
+    return int((library or lib()).orc_e2m1_encode(float(x)))
+
+
+def e2m1_decode(c: int, library=None) -> float:
+    return float((library or lib()).orc_e2m1_decode(int(c)))
+
+
+def mx_scale_exp(amax: float, library=None) -> int:
+    return int((library or lib()).orc_mx_scale_exp(float(amax)))
+
+
+def mx_block(x, library=None):
+    """(X, codes) of one MX block of values x (orc_mx_block)."""
+    L = library or lib()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    codes = np.zeros(max(len(x), 1), dtype=np.uint8)
+    X = L.orc_mx_block(_ptr(x, C.c_double), len(x), _ptr(codes, C.c_uint8))
+    return int(X), codes[:len(x)]
 
 
 def q8_softmax_pv(x, vdec, library=None) -> np.ndarray:

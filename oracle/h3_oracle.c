@@ -34,6 +34,20 @@
  * probabilities 224 * 2^(s - m), and a row sum over those quantised
  * probabilities.  Each of these is a reading of the page "H3 Runtime Current
  * State" (the quantised attention it lists), stated where it is used.
+ *
+ * The MXFP4 helpers (orc_e2m1_*, orc_mx_*) state the microscaling FP4 format
+ * of the OCP MX specification by its definition (e2m1 elements, round to
+ * nearest even with saturation at 6, one power-of-two scale per block of 32
+ * elements taken from the block's largest magnitude) and emulate the FP4
+ * attention variant step by step: MXFP4 qhat and khat - mean with blocks along
+ * the channels, MXFP4 v with blocks along the keys, exact dot products of the
+ * decoded values, the same tiles and lazy running maximum as the quantised
+ * path, and the probabilities of every 32-key block quantised as one MX block.
+ * The pages name an FP4 attention without its format: the FastVideo commit
+ * page on docs/getting_started (its note on the FP4 attention switch: faster,
+ * lossy, off by default) and "H3 Runtime Current State" (Sage3 among the
+ * approximate backends, "Implemented And Validated"; keep them quality-gated,
+ * "Quality Work Remaining").  The readings are stated where they are used.
  */
 #include <math.h>
 #include <pthread.h>
@@ -492,6 +506,24 @@ int orc_q8_v_quant(const orc_problem *p, int32_t seq, int32_t head, double *scal
 
 /* --------------------------------- quantised attention, step by step (fp64) */
 
+/* The running maximum of the quantised paths (tiles of 64 keys, base 2): m
+ * starts at the first tile's maximum mx and moves to a later tile's maximum
+ * only when that exceeds m by more than 1.  Returns the factor 2^(m_old - m_new)
+ * by which the sums so far are scaled (1 when m stays). */
+static double lazy_max_step(int first, double mx, double *m)
+{
+    if (first) {
+        *m = mx;
+        return 1.0;
+    }
+    if (mx - *m > 1.0) {
+        double alpha = exp2(*m - mx);
+        *m = mx;
+        return alpha;
+    }
+    return 1.0;
+}
+
 /* The quantised path's softmax and P.V for one query row, in the order the
  * path takes them.  x[j] is key j's score in log2 units (scores of the
  * quantised codes times their scales, softmax scale and log2 e), vdec [n][d]
@@ -509,14 +541,9 @@ void orc_q8_softmax_pv(const double *x, int64_t n, const double *vdec, int d, do
         int64_t t1 = t0 + 64 < n ? t0 + 64 : n;
         double mx = -INFINITY;
         for (int64_t j = t0; j < t1; ++j) if (x[j] > mx) mx = x[j];
-        if (t0 == 0) {
-            m = mx;
-        } else if (mx - m > 1.0) {
-            double alpha = exp2(m - mx);
-            l *= alpha;
-            for (int c = 0; c < d; ++c) out[c] *= alpha;
-            m = mx;
-        }
+        double alpha = lazy_max_step(t0 == 0, mx, &m);
+        l *= alpha;
+        for (int c = 0; c < d; ++c) out[c] *= alpha;
         for (int64_t j = t0; j < t1; ++j) {
             double P = orc_e4m3_decode(orc_e4m3_encode(224.0 * exp2(x[j] - m)));
             l += P;
@@ -613,5 +640,248 @@ int orc_q8_attention_rows(const orc_problem *p, const int64_t *rows, int64_t nro
     }
     free(sel);
     free(pos);
+    return 0;
+}
+
+/* ------------------------------------------------- MXFP4 attention stages */
+
+/* OCP FP4 e2m1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; magnitudes 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN.  Round to nearest, ties to
+ * even, saturating to +-6; a negative value (or -0) that rounds to zero keeps
+ * its sign bit. */
+uint8_t orc_e2m1_encode(double x)
+{
+    uint8_t sign = (x < 0 || (x == 0 && signbit(x))) ? 0x8 : 0x0;
+    double a = fabs(x);
+    if (isnan(x) || a >= 6.0) return sign | 0x7;
+    if (a < 1.0) {                            /* subnormal step 0.5; 2 steps is 1.0, code 2 */
+        double q = nearbyint(a / 0.5);
+        return sign | (uint8_t)q;
+    }
+    int e;
+    double f = frexp(a, &e);                  /* a = f * 2^e, f in [0.5, 1) */
+    int E = e - 1;                            /* a = (2f) * 2^E, E in 0..2 */
+    double mant = nearbyint((2.0 * f - 1.0) * 2.0);   /* 0..2 */
+    if (mant >= 2.0) { mant = 0.0; E += 1; }
+    if (E > 2) return sign | 0x7;
+    return sign | (uint8_t)(((E + 1) << 1) | (int)mant);
+}
+
+double orc_e2m1_decode(uint8_t c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* Scale exponent of one MX block: the OCP rule X = floor(log2 amax) - 2, where
+ * 2 is the exponent of e2m1's largest power of two (4), so that amax / 2^X lies
+ * in [4, 8) and only values above 6 saturate.  Limited to [-126, 127] (E8M0
+ * holds 2^-127..2^127; the lower limit keeps 2^X a normal fp32 number); X = 0
+ * for an all-zero block. */
+int orc_mx_scale_exp(double amax)
+{
+    if (!(amax > 0)) return 0;
+    int e;
+    frexp(amax, &e);                          /* floor(log2 amax) = e - 1 */
+    int X = e - 1 - 2;
+    if (X < -126) X = -126;
+    if (X > 127) X = 127;
+    return X;
+}
+
+/* One MX block of n values: X from their largest magnitude, codes
+ * e2m1(x / 2^X).  Returns X. */
+int orc_mx_block(const double *x, int n, uint8_t *codes)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    int X = orc_mx_scale_exp(amax);
+    for (int i = 0; i < n; ++i) codes[i] = orc_e2m1_encode(ldexp(x[i], -X));
+    return X;
+}
+
+typedef struct {
+    const orc_problem *p;
+    int which;
+    int32_t seq, head;
+    const double *kmean;
+    uint8_t *codes;
+    int32_t *exps;
+} mxqk_ctx;
+
+static void mxqk_body(void *c, int64_t j)
+{
+    mxqk_ctx *x = c;
+    const orc_problem *p = x->p;
+    int d = p->d;
+    double *row = malloc(sizeof(double) * d);
+    prologue_one(p, x->which, p->cu[x->seq] + j, x->head, row);
+    if (x->which == 1)
+        for (int c2 = 0; c2 < d; ++c2) row[c2] -= x->kmean[((int64_t)x->seq * p->H + x->head) * d + c2];
+    for (int b = 0; b < d / 32; ++b)
+        x->exps[j * (d / 32) + b] = orc_mx_block(row + 32 * b, 32, x->codes + j * d + 32 * b);
+    free(row);
+}
+
+/* MXFP4 codes of qhat (which = 0) or khat - kmean (which = 1) for every token
+ * of sequence `seq`, head `head`: blocks of 32 consecutive channels.
+ * codes [n_s][d], exps [n_s][d/32].  kmean is [S][H][d] (orc_q8_kmean; it may
+ * be NULL for which = 0).  Returns n_s, or -1 when d is not a multiple of 32. */
+int orc_mx_qk_quant(const orc_problem *p, int which, int32_t seq, int32_t head, const double *kmean,
+                    uint8_t *codes, int32_t *exps, int nthreads)
+{
+    if (p->d % 32 || seq < 0 || seq >= p->S || head < 0 || head >= p->H) return -1;
+    if (which == 1 && !kmean) return -1;
+    mxqk_ctx c = {p, which, seq, head, kmean, codes, exps};
+    int64_t n = p->cu[seq + 1] - p->cu[seq];
+    parallel_for(n, nthreads, mxqk_body, &c);
+    return (int)n;
+}
+
+/* MXFP4 codes of raw v for one (sequence, head): per channel, blocks of 32
+ * consecutive tokens aligned to the sequence start (a short last block keeps
+ * its own scale).  codes [n_s][d], exps [ceil(n_s / 32)][d].  Returns n_s. */
+int orc_mx_v_quant(const orc_problem *p, int32_t seq, int32_t head, uint8_t *codes, int32_t *exps)
+{
+    int d = p->d;
+    if (p->vf || seq < 0 || seq >= p->S || head < 0 || head >= p->H) return -1;
+    int64_t n = p->cu[seq + 1] - p->cu[seq];
+    double col[32];
+    uint8_t cc[32];
+    for (int64_t b = 0; b * 32 < n; ++b) {
+        int rows = (int)(n - 32 * b < 32 ? n - 32 * b : 32);
+        for (int c = 0; c < d; ++c) {
+            for (int i = 0; i < rows; ++i)
+                col[i] = orc_bf16_to_f64(p->v[(p->cu[seq] + 32 * b + i) * p->v_stride + (int64_t)head * d + c]);
+            exps[b * d + c] = orc_mx_block(col, rows, cc);
+            for (int i = 0; i < rows; ++i) codes[(32 * b + i) * d + c] = cc[i];
+        }
+    }
+    return (int)n;
+}
+
+/* The FP4 path's softmax and P.V for one query row, in the order the path
+ * takes them.  x[j] is key j's score in log2 units, vdec [n][d] the decoded V.
+ * Keys are taken in tiles of 64 with the running maximum of the quantised
+ * path: m starts at the first tile's maximum and moves to a later tile's
+ * maximum only when that exceeds m by more than 1, the sums so far then scaled
+ * by 2^(m_old - m_new).  The probabilities p_j = 2^(x_j - m) of each 32-key
+ * block (aligned to the sequence start, so a tile holds two) are one MX block:
+ * X from the block's largest p, P_j = e2m1(p_j / 2^X) * 2^X.  O += P v and
+ * l += P (the sum of the quantised P); o = O / l. */
+void orc_mx_softmax_pv(const double *x, int64_t n, const double *vdec, int d, double *out)
+{
+    double m = 0.0, l = 0.0, p[32];
+    uint8_t codes[32];
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t t0 = 0; t0 < n; t0 += 64) {
+        int64_t t1 = t0 + 64 < n ? t0 + 64 : n;
+        double mx = -INFINITY;
+        for (int64_t j = t0; j < t1; ++j) if (x[j] > mx) mx = x[j];
+        double alpha = lazy_max_step(t0 == 0, mx, &m);
+        l *= alpha;
+        for (int c = 0; c < d; ++c) out[c] *= alpha;
+        for (int64_t b0 = t0; b0 < t1; b0 += 32) {
+            int nb = (int)(t1 - b0 < 32 ? t1 - b0 : 32);
+            for (int i = 0; i < nb; ++i) p[i] = exp2(x[b0 + i] - m);
+            int X = orc_mx_block(p, nb, codes);
+            for (int i = 0; i < nb; ++i) {
+                double P = ldexp(orc_e2m1_decode(codes[i]), X);
+                l += P;
+                for (int c = 0; c < d; ++c) out[c] += P * vdec[(b0 + i) * d + c];
+            }
+        }
+    }
+    for (int c = 0; c < d; ++c) out[c] = n > 0 ? out[c] / l : 0.0;
+}
+
+typedef struct {
+    const orc_problem *p;
+    int32_t seq;
+    int64_t n;
+    const int64_t *rows;       /* the rows of this (seq, head) */
+    const double *qdec;        /* [rows][d] decoded query codes */
+    const double *kdec;        /* [n][d] */
+    const double *vdec;        /* [n][d] */
+    double *out;               /* [rows][d] */
+} mxrow_ctx;
+
+static void mxrow_body(void *c, int64_t i)
+{
+    mxrow_ctx *x = c;
+    const orc_problem *p = x->p;
+    int d = p->d;
+    const double *q = x->qdec + i * d;
+    double qs = p->scale / log(2.0);
+    double *s = malloc(sizeof(double) * (x->n > 0 ? x->n : 1));
+    for (int64_t j = 0; j < x->n; ++j) {
+        double dot = 0.0;
+        for (int cc = 0; cc < d; ++cc) dot += q[cc] * x->kdec[j * d + cc];
+        s[j] = dot * qs;
+    }
+    orc_mx_softmax_pv(s, x->n, x->vdec, d, x->out + i * d);
+    free(s);
+}
+
+/* Output rows (token * H + head) of the FP4 path, taken step by step: the K
+ * mean (orc_q8_kmean), MXFP4 codes of qhat and of khat - mean along the
+ * channels and of v along the keys (orc_mx_qk_quant, orc_mx_v_quant), the dot
+ * product of the decoded q and k values (code value times 2^X) times the
+ * softmax scale and log2 e, then orc_mx_softmax_pv.  Returns -1 for a row
+ * outside every sequence or d not a multiple of 32. */
+int orc_mx_attention_rows(const orc_problem *p, const int64_t *rows, int64_t nrows, const double *kmean,
+                          double *out, int nthreads)
+{
+    int d = p->d, nb = p->d / 32;
+    if (d % 32) return -1;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t tok = rows[i] / p->H;
+        if (tok < 0 || tok >= p->cu[p->S]) return -1;
+    }
+    int64_t *sel = malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
+    int64_t *pos = malloc(sizeof(int64_t) * (nrows > 0 ? nrows : 1));
+    double *row = malloc(sizeof(double) * d);
+    uint8_t *qc = malloc(d);
+    for (int32_t s = 0; s < p->S; ++s) {
+        int64_t n = p->cu[s + 1] - p->cu[s];
+        if (n == 0) continue;
+        for (int32_t h = 0; h < p->H; ++h) {
+            int64_t m = 0;
+            for (int64_t i = 0; i < nrows; ++i) {
+                int64_t tok = rows[i] / p->H;
+                if (rows[i] % p->H == h && tok >= p->cu[s] && tok < p->cu[s + 1]) {
+                    sel[m] = rows[i];
+                    pos[m] = i;
+                    ++m;
+                }
+            }
+            if (m == 0) continue;
+            uint8_t *kc = malloc((size_t)n * d), *vc = malloc((size_t)n * d);
+            int32_t *kx = malloc(sizeof(int32_t) * n * nb), *vx = malloc(sizeof(int32_t) * ((n + 31) / 32) * d);
+            double *kdec = malloc(sizeof(double) * (size_t)n * d), *vdec = malloc(sizeof(double) * (size_t)n * d);
+            double *qdec = malloc(sizeof(double) * (size_t)m * d);
+            orc_mx_qk_quant(p, 1, s, h, kmean, kc, kx, nthreads);
+            orc_mx_v_quant(p, s, h, vc, vx);
+            for (int64_t j = 0; j < n; ++j)
+                for (int c = 0; c < d; ++c) {
+                    kdec[j * d + c] = ldexp(orc_e2m1_decode(kc[j * d + c]), kx[j * nb + c / 32]);
+                    vdec[j * d + c] = ldexp(orc_e2m1_decode(vc[j * d + c]), vx[(j / 32) * d + c]);
+                }
+            for (int64_t i = 0; i < m; ++i) {
+                prologue_one(p, 0, sel[i] / p->H, h, row);
+                for (int b = 0; b < nb; ++b) {
+                    int X = orc_mx_block(row + 32 * b, 32, qc + 32 * b);
+                    for (int c = 32 * b; c < 32 * b + 32; ++c) qdec[i * d + c] = ldexp(orc_e2m1_decode(qc[c]), X);
+                }
+            }
+            double *o = malloc(sizeof(double) * (size_t)m * d);
+            mxrow_ctx ctx = {p, s, n, sel, qdec, kdec, vdec, o};
+            parallel_for(m, nthreads, mxrow_body, &ctx);
+            for (int64_t i = 0; i < m; ++i) memcpy(out + pos[i] * d, o + i * d, sizeof(double) * d);
+            free(o); free(kc); free(vc); free(kx); free(vx); free(kdec); free(vdec); free(qdec);
+        }
+    }
+    free(sel); free(pos); free(row); free(qc);
     return 0;
 }

@@ -49,13 +49,23 @@ MUTANTS = {
     "e4m3_subnormal_step": ("double q = nearbyint(a / ldexp(1.0, -9));", "double q = nearbyint(a / ldexp(1.0, -10));"),
     "v_scale_fnuz_max": ("scale_out[c] = amax > 0 ? amax / 448.0 : 1.0;",
                          "scale_out[c] = amax > 0 ? amax / 240.0 : 1.0;"),
-    "q8_rescale_on_any_rise": ("} else if (mx - m > 1.0) {", "} else if (mx - m > 0.0) {"),
-    "q8_rowsum_unquantised": ("            l += P;\n", "            l += 224.0 * exp2(x[j] - m);\n"),
+    "lazy_rescale_on_any_rise": ("if (mx - *m > 1.0) {", "if (mx - *m > 0.0) {"),
+    "q8_rowsum_unquantised": ("\n            l += P;\n", "\n            l += 224.0 * exp2(x[j] - m);\n"),
     "q8_p_scale_448": ("orc_e4m3_encode(224.0 * exp2(x[j] - m))", "orc_e4m3_encode(448.0 * exp2(x[j] - m))"),
     "q8_score_natural_log": ("x->qscale[qi / 64] * p->scale / log(2.0)", "x->qscale[qi / 64] * p->scale"),
     "projected_k_from_q": ("const double *xf = which == 0 ? p->qf : p->kf;",
                            "const double *xf = which == 0 ? p->qf : p->qf;"),
     "projected_v_channel": ("p->vf ? p->vf[at + c] :", "p->vf ? p->vf[at + (c ^ 1)] :"),
+    "e2m1_round_half_up": ("double mant = nearbyint((2.0 * f - 1.0) * 2.0);",
+                           "double mant = floor((2.0 * f - 1.0) * 2.0 + 0.5);"),
+    "e2m1_subnormal_half_up": ("double q = nearbyint(a / 0.5);", "double q = floor(a / 0.5 + 0.5);"),
+    "mx_scale_offset": ("int X = e - 1 - 2;", "int X = e - 1 - 1;"),
+    "mx_scale_low_limit": ("if (X < -126) X = -126;", "if (X < -127) X = -127;"),
+    "mx_k_first_block_scale": ("kx[j * nb + c / 32]", "kx[j * nb]"),
+    "mx_v_scale_of_first_block": ("vx[(j / 32) * d + c]", "vx[c]"),
+    "mx_score_natural_log": ("double qs = p->scale / log(2.0);", "double qs = p->scale;"),
+    "mx_rowsum_unquantised": ("                l += P;\n", "                l += exp2(x[b0 + i] - m);\n"),
+    "mx_query_from_k": ("prologue_one(p, 0, sel[i] / p->H, h, row);", "prologue_one(p, 1, sel[i] / p->H, h, row);"),
     "q8_first_block_kscale": ("s[j] = (double)dot * qs * x->kscale[j / 64];",
                               "s[j] = (double)dot * qs * x->kscale[0];"),
 }

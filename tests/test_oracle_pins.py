@@ -613,3 +613,202 @@ def test_sparse_select_closed_form_ranking():
     for i in range(tiles.shape[0]):
         assert list(tiles[i]) == want
         assert np.argmax(scores[i]) == 4
+
+
+# ------------------------------------------------------------ MXFP4 stages
+# OCP Microscaling FP4: e2m1 elements, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6
+# (code = sign << 3 | exponent << 1 | mantissa), one power-of-two scale per
+# 32-element block.  The brute-force helpers below restate the format from
+# its value table, not from the oracle's arithmetic.
+
+E2M1_MAG = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _e2m1_nearest(x):
+    """Code of the nearest e2m1 value to x by search over the table; ties go
+    to the even code (mantissa bit 0); saturates at 6; keeps the sign bit."""
+    a = abs(x)
+    best = min(range(8), key=lambda c: (abs(E2M1_MAG[c] - a), c & 1))
+    return best | (8 if math.copysign(1.0, x) < 0 else 0)
+
+
+def _mx_block_brute(vals):
+    amax = max(abs(v) for v in vals)
+    if amax == 0:
+        X = 0
+    else:
+        X = min(max(math.floor(math.log2(amax)) - 2, -126), 127)
+    return X, [_e2m1_nearest(v / 2.0 ** X) for v in vals]
+
+
+def test_e2m1_decode_is_the_ocp_table():
+    for c in range(16):
+        want = E2M1_MAG[c & 7] * (-1 if c & 8 else 1)
+        got = oracle.e2m1_decode(c, library=L())
+        assert got == want and math.copysign(1, got) == (-1 if c & 8 else 1)
+
+
+def test_e2m1_encode_nearest_ties_even_saturation():
+    rng = np.random.default_rng(30)
+    mids = [(E2M1_MAG[i] + E2M1_MAG[i + 1]) / 2 for i in range(7)]
+    vals = list(rng.uniform(-8, 8, 4000)) + list(rng.uniform(-1, 1, 1000)) + mids + [-m for m in mids] + \
+        [0.0, -0.0, 6.0, 6.5, 7.0, 1e9, -1e9, 1e-30, -1e-30] + E2M1_MAG
+    for x in vals:
+        assert oracle.e2m1_encode(x, library=L()) == _e2m1_nearest(x), x
+    # the seven midpoints go to the even neighbour: 0, 1, 1, 2, 2, 4, 4
+    assert [oracle.e2m1_decode(oracle.e2m1_encode(m, library=L()), library=L()) for m in mids] == \
+        [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+
+
+def test_mx_scale_puts_block_max_in_4_to_8():
+    rng = np.random.default_rng(31)
+    for amax in np.exp(rng.uniform(-60, 60, 2000)):
+        X = oracle.mx_scale_exp(float(amax), library=L())
+        assert 4.0 <= amax / 2.0 ** X < 8.0
+    for k in range(-100, 100, 7):   # exact powers of two: amax / 2^X = 4 exactly
+        assert oracle.mx_scale_exp(2.0 ** k, library=L()) == k - 2
+    assert oracle.mx_scale_exp(0.0, library=L()) == 0
+    assert oracle.mx_scale_exp(2.0 ** -200, library=L()) == -126
+    assert oracle.mx_scale_exp(2.0 ** 300, library=L()) == 127
+
+
+def test_mx_block_matches_brute_force_and_exact_values_round_trip():
+    rng = np.random.default_rng(32)
+    for t in range(200):
+        n = int(rng.integers(1, 33))
+        x = rng.standard_normal(n) * np.exp(rng.uniform(-20, 20))
+        X, codes = oracle.mx_block(x, library=L())
+        Xb, cb = _mx_block_brute(list(x))
+        assert X == Xb and list(codes) == cb
+    # values already on the MX grid come back unchanged
+    for t in range(50):
+        X0 = int(rng.integers(-40, 40))
+        c = rng.integers(0, 16, 32)
+        c[0] = 7                                    # the block max is 6 * 2^X0 -> X = X0
+        x = np.array([oracle.e2m1_decode(int(k), library=L()) * 2.0 ** X0 for k in c])
+        X, codes = oracle.mx_block(x, library=L())
+        dec = np.array([oracle.e2m1_decode(int(k), library=L()) * 2.0 ** X for k in codes])
+        assert X == X0
+        np.testing.assert_array_equal(dec, x)
+
+
+def test_mx_qk_codes_are_blocks_of_32_channels():
+    p = _problem([(2, 4, 5, 3), (1, 2, 3, 0)], H=2, d=64, split=(16, 24, 24), seed=33)
+    km = p.q8_kmean()
+    for which in (0, 1):
+        for s in range(2):
+            toks = np.arange(p.cu[s], p.cu[s + 1])
+            x = p.prologue_rows(which, toks * p.H + 1)
+            if which == 1:
+                x = x - km[s, 1]
+            codes, exps = p.mx_qk_quant(which, s, 1, kmean=km)
+            assert codes.shape == (len(toks), 64) and exps.shape == (len(toks), 2)
+            for t in range(len(toks)):
+                for b in range(2):
+                    Xb, cb = _mx_block_brute(list(x[t, 32 * b:32 * b + 32]))
+                    assert exps[t, b] == Xb and list(codes[t, 32 * b:32 * b + 32]) == cb
+
+
+def test_mx_v_codes_are_blocks_of_32_tokens_from_the_sequence_start():
+    p = _problem([(1, 5, 9, 4), (1, 3, 3, 1)], H=2, d=16, seed=34)   # 49 and 10 tokens
+    for s, n in ((0, 49), (1, 10)):
+        v = _f(p.v[p.cu[s]:p.cu[s + 1], 0])
+        codes, exps = p.mx_v_quant(s, 0)
+        assert codes.shape == (n, 16) and exps.shape == ((n + 31) // 32, 16)
+        for b in range((n + 31) // 32):
+            for c in range(16):
+                Xb, cb = _mx_block_brute(list(v[32 * b:32 * b + 32, c]))
+                assert exps[b, c] == Xb and list(codes[32 * b:32 * b + 32, c]) == cb
+
+
+def test_mx_softmax_pv_golden():
+    with open(os.path.join(GOLDEN, "mx_softmax_pv.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        n = c["n"]
+        x = _expand(c["x"], n)
+        vd = c["v"]["default"]
+        v = np.array([c["v"].get(str(i), vd) for i in range(n)], dtype=np.float64)
+        got = oracle.mx_softmax_pv(x, v, library=L())
+        np.testing.assert_allclose(got, c["expected"], rtol=1e-13, err_msg=c["name"])
+
+
+def test_mx_softmax_pv_is_exact_softmax_when_every_p_is_on_the_grid():
+    """Integer log2 scores within 3 of their 32-key block's maximum give
+    probabilities that are e2m1 values times the block scale, so the FP4
+    softmax equals scipy's exact softmax (when no tile rescales mid-block:
+    scores are kept within 1 of the first tile's maximum)."""
+    rng = np.random.default_rng(35)
+    for t in range(20):
+        n = int(rng.integers(1, 300))
+        x = np.zeros(n)
+        for b0 in range(0, n, 32):
+            top = -float(rng.integers(0, 2)) if b0 else 0.0   # block maxima 0 or -1; the first is 0
+            blk = top - rng.integers(0, 4, min(32, n - b0))
+            blk[0] = top
+            x[b0:b0 + 32] = blk
+        v = rng.standard_normal((n, 3))
+        ref = scipy.special.softmax(x * math.log(2.0)) @ v
+        np.testing.assert_allclose(oracle.mx_softmax_pv(x, v, library=L()), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_mx_rows_with_equal_keys_average_the_quantised_values():
+    """Without RoPE, equal k rows make khat - mean zero, every score 0 and every
+    P 1, so each output row is the mean of the MXFP4-rounded v of its sequence
+    (rounded here by the brute-force quantiser)."""
+    rng = np.random.default_rng(36)
+    seqs = [(1, 5, 8, 7), (1, 2, 3, 0)]
+    N = 47 + 6
+    k = _bf16(np.tile(rng.standard_normal((1, 2, 32)), (N, 1, 1)))
+    p = _problem(seqs, H=2, d=32, split=(8, 12, 12), seed=36, rope=False, k=k)
+    rows = _all_rows(p)
+    got = p.mx_attention_rows(rows)
+    for s in range(2):
+        for h in range(2):
+            v = _f(p.v[p.cu[s]:p.cu[s + 1], h])
+            vq = np.zeros_like(v)
+            for b0 in range(0, len(v), 32):
+                for c in range(32):
+                    X, cb = _mx_block_brute(list(v[b0:b0 + 32, c]))
+                    vq[b0:b0 + 32, c] = [E2M1_MAG[q & 7] * (-1 if q & 8 else 1) * 2.0 ** X for q in cb]
+            want = vq.mean(axis=0)
+            for t in range(p.cu[s], p.cu[s + 1]):
+                np.testing.assert_allclose(got[t * 2 + h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_mx_rows_track_exact_attention():
+    """The FP4 path stays near exact attention (a check of its scaling: a
+    dropped scale or a misplaced block would miss by far more than FP4's own
+    rounding)."""
+    p = _problem([(2, 5, 7, 9), (1, 3, 4, 0)], H=2, d=32, split=(8, 12, 12), seed=8)
+    rows = _all_rows(p)
+    mx = p.mx_attention_rows(rows)
+    ex = p.attention_rows(rows)
+    rel_l2 = np.linalg.norm(mx - ex) / np.linalg.norm(ex)
+    assert rel_l2 < 0.25, rel_l2
+    assert np.corrcoef(mx.ravel(), ex.ravel())[0, 1] > 0.97
+
+
+def test_mx_rows_are_softmax_of_decoded_codes():
+    """The FP4 rows compose their pinned stages: scores from the decoded q and
+    k codes (table value times 2^X of the code's own 32-channel block), times
+    the softmax scale and log2 e, then the pinned FP4 softmax over the decoded
+    v (its own 32-token block's 2^X)."""
+    p = _problem([(1, 6, 8, 5), (1, 3, 4, 0)], H=2, d=64, split=(16, 24, 24), seed=37)
+    km = p.q8_kmean()
+    rows = _all_rows(p)
+    got = p.mx_attention_rows(rows, kmean=km)
+    mag = np.array(E2M1_MAG + [-m for m in E2M1_MAG])
+    for s in range(2):
+        n = int(p.cu[s + 1] - p.cu[s])
+        for h in range(2):
+            qc, qx = p.mx_qk_quant(0, s, h)
+            kc, kx = p.mx_qk_quant(1, s, h, kmean=km)
+            vc, vx = p.mx_v_quant(s, h)
+            qd = mag[qc] * np.repeat(2.0 ** qx, 32, axis=1)
+            kd = mag[kc] * np.repeat(2.0 ** kx, 32, axis=1)
+            vd = mag[vc] * np.repeat(2.0 ** vx, 32, axis=0)[:n]
+            for i in range(n):
+                x = (kd @ qd[i]) * p.scale / math.log(2.0)
+                want = oracle.mx_softmax_pv(x, vd, library=L())
+                np.testing.assert_allclose(got[(p.cu[s] + i) * 2 + h], want, rtol=1e-12, atol=1e-14)
