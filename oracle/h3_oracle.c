@@ -39,8 +39,8 @@
  * of the OCP MX specification by its definition (e2m1 elements, round to
  * nearest even with saturation at 6, one power-of-two scale per block of 32
  * elements taken from the block's largest magnitude) and emulate the FP4
- * attention variant step by step: MXFP4 qhat and khat - mean with blocks along
- * the channels, MXFP4 v with blocks along the keys, exact dot products of the
+ * attention variant step by step: MXFP4 qhat' (qhat times the softmax scale
+ * and log2 e) and khat - mean with blocks along the channels, MXFP4 v with blocks along the keys, exact dot products of the
  * decoded values, the same tiles and lazy running maximum as the quantised
  * path, and the probabilities of every 32-key block quantised as one MX block.
  * The pages name an FP4 attention without its format: the FastVideo commit
@@ -701,6 +701,19 @@ int orc_mx_block(const double *x, int n, uint8_t *codes)
     return X;
 }
 
+/* The query the FP4 path quantises: qhat' = qhat * softmax scale * log2 e (the
+ * pre-scaled query the bf16 path stores as well), so that the scores of its
+ * codes are already in log2 units.  Reading: the pages name no order of
+ * quantisation and scaling; quantising after the (non power-of-two) scale
+ * means the running maximum's own probability is 2^0 = 1 exactly, which the
+ * power-of-two block scale rule, discontinuous at 1, needs for the kernel's
+ * fp32 arithmetic to reach the same codes. */
+static void mx_prescale_q(const orc_problem *p, double *row)
+{
+    double qs = p->scale / log(2.0);
+    for (int c = 0; c < p->d; ++c) row[c] *= qs;
+}
+
 typedef struct {
     const orc_problem *p;
     int which;
@@ -717,6 +730,7 @@ static void mxqk_body(void *c, int64_t j)
     int d = p->d;
     double *row = malloc(sizeof(double) * d);
     prologue_one(p, x->which, p->cu[x->seq] + j, x->head, row);
+    if (x->which == 0) mx_prescale_q(p, row);
     if (x->which == 1)
         for (int c2 = 0; c2 < d; ++c2) row[c2] -= x->kmean[((int64_t)x->seq * p->H + x->head) * d + c2];
     for (int b = 0; b < d / 32; ++b)
@@ -724,8 +738,9 @@ static void mxqk_body(void *c, int64_t j)
     free(row);
 }
 
-/* MXFP4 codes of qhat (which = 0) or khat - kmean (which = 1) for every token
- * of sequence `seq`, head `head`: blocks of 32 consecutive channels.
+/* MXFP4 codes of qhat' (which = 0, see mx_prescale_q) or khat - kmean
+ * (which = 1) for every token of sequence `seq`, head `head`: blocks of 32
+ * consecutive channels.
  * codes [n_s][d], exps [n_s][d/32].  kmean is [S][H][d] (orc_q8_kmean; it may
  * be NULL for which = 0).  Returns n_s, or -1 when d is not a multiple of 32. */
 int orc_mx_qk_quant(const orc_problem *p, int which, int32_t seq, int32_t head, const double *kmean,
@@ -813,22 +828,22 @@ static void mxrow_body(void *c, int64_t i)
     const orc_problem *p = x->p;
     int d = p->d;
     const double *q = x->qdec + i * d;
-    double qs = p->scale / log(2.0);
     double *s = malloc(sizeof(double) * (x->n > 0 ? x->n : 1));
     for (int64_t j = 0; j < x->n; ++j) {
         double dot = 0.0;
         for (int cc = 0; cc < d; ++cc) dot += q[cc] * x->kdec[j * d + cc];
-        s[j] = dot * qs;
+        s[j] = dot;
     }
     orc_mx_softmax_pv(s, x->n, x->vdec, d, x->out + i * d);
     free(s);
 }
 
 /* Output rows (token * H + head) of the FP4 path, taken step by step: the K
- * mean (orc_q8_kmean), MXFP4 codes of qhat and of khat - mean along the
- * channels and of v along the keys (orc_mx_qk_quant, orc_mx_v_quant), the dot
- * product of the decoded q and k values (code value times 2^X) times the
- * softmax scale and log2 e, then orc_mx_softmax_pv.  Returns -1 for a row
+ * mean (orc_q8_kmean), MXFP4 codes of qhat' (qhat times the softmax scale and
+ * log2 e) and of khat - mean along the channels and of v along the keys
+ * (orc_mx_qk_quant, orc_mx_v_quant), the dot product of the decoded q and k
+ * values (code value times 2^X), which is the score in log2 units, then
+ * orc_mx_softmax_pv.  Returns -1 for a row
  * outside every sequence or d not a multiple of 32. */
 int orc_mx_attention_rows(const orc_problem *p, const int64_t *rows, int64_t nrows, const double *kmean,
                           double *out, int nthreads)
@@ -870,6 +885,7 @@ int orc_mx_attention_rows(const orc_problem *p, const int64_t *rows, int64_t nro
                 }
             for (int64_t i = 0; i < m; ++i) {
                 prologue_one(p, 0, sel[i] / p->H, h, row);
+                mx_prescale_q(p, row);
                 for (int b = 0; b < nb; ++b) {
                     int X = orc_mx_block(row + 32 * b, 32, qc + 32 * b);
                     for (int c = 32 * b; c < 32 * b + 32; ++c) qdec[i * d + c] = ldexp(orc_e2m1_decode(qc[c]), X);

@@ -63,7 +63,8 @@ MUTANTS = {
     "mx_scale_low_limit": ("if (X < -126) X = -126;", "if (X < -127) X = -127;"),
     "mx_k_first_block_scale": ("kx[j * nb + c / 32]", "kx[j * nb]"),
     "mx_v_scale_of_first_block": ("vx[(j / 32) * d + c]", "vx[c]"),
-    "mx_score_natural_log": ("double qs = p->scale / log(2.0);", "double qs = p->scale;"),
+    "mx_score_natural_log": ("double qs = p->scale / log(2.0);\n    for (int c = 0; c < p->d; ++c) row[c] *= qs;",
+                             "double qs = p->scale;\n    for (int c = 0; c < p->d; ++c) row[c] *= qs;"),
     "mx_rowsum_unquantised": ("                l += P;\n", "                l += exp2(x[b0 + i] - m);\n"),
     "mx_query_from_k": ("prologue_one(p, 0, sel[i] / p->H, h, row);", "prologue_one(p, 1, sel[i] / p->H, h, row);"),
     "q8_first_block_kscale": ("s[j] = (double)dot * qs * x->kscale[j / 64];",

@@ -699,6 +699,8 @@ def test_mx_qk_codes_are_blocks_of_32_channels():
         for s in range(2):
             toks = np.arange(p.cu[s], p.cu[s + 1])
             x = p.prologue_rows(which, toks * p.H + 1)
+            if which == 0:
+                x = x * (p.scale / math.log(2.0))        # the FP4 path quantises the pre-scaled query
             if which == 1:
                 x = x - km[s, 1]
             codes, exps = p.mx_qk_quant(which, s, 1, kmean=km)
@@ -790,10 +792,10 @@ def test_mx_rows_track_exact_attention():
 
 
 def test_mx_rows_are_softmax_of_decoded_codes():
-    """The FP4 rows compose their pinned stages: scores from the decoded q and
-    k codes (table value times 2^X of the code's own 32-channel block), times
-    the softmax scale and log2 e, then the pinned FP4 softmax over the decoded
-    v (its own 32-token block's 2^X)."""
+    """The FP4 rows compose their pinned stages: scores from the decoded
+    codes of the pre-scaled query and of k (table value times 2^X of the
+    code's own 32-channel block), already in log2 units, then the pinned FP4
+    softmax over the decoded v (its own 32-token block's 2^X)."""
     p = _problem([(1, 6, 8, 5), (1, 3, 4, 0)], H=2, d=64, split=(16, 24, 24), seed=37)
     km = p.q8_kmean()
     rows = _all_rows(p)
@@ -809,6 +811,6 @@ def test_mx_rows_are_softmax_of_decoded_codes():
             kd = mag[kc] * np.repeat(2.0 ** kx, 32, axis=1)
             vd = mag[vc] * np.repeat(2.0 ** vx, 32, axis=0)[:n]
             for i in range(n):
-                x = (kd @ qd[i]) * p.scale / math.log(2.0)
+                x = kd @ qd[i]
                 want = oracle.mx_softmax_pv(x, vd, library=L())
                 np.testing.assert_allclose(got[(p.cu[s] + i) * 2 + h], want, rtol=1e-12, atol=1e-14)
