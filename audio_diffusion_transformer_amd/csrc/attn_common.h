@@ -27,12 +27,13 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
 
 // 16-byte chunk swizzle of an LDS row: rows of 256 bytes (16 chunks) XOR the
 // chunk index with row % 16, rows of 128 bytes (8 chunks) with (row / 2) % 8,
-// rows of 64 bytes (4 chunks) with (row / 4) % 4, so that 16 consecutive rows
-// read at one logical chunk cover all 64 banks.
+// rows of 64 bytes (4 chunks) with (row / 4) % 4, rows of 32 bytes (2 chunks)
+// with (row / 8) % 2, so that 16 consecutive rows read at one logical chunk
+// cover all 64 banks.
 template <int CPR>
 __device__ __forceinline__ int swz(int row)
 {
-    return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+    return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : CPR == 4 ? ((row >> 2) & 3) : ((row >> 3) & 1);
 }
 
 // Direct-to-LDS tile fill (buffer_load_dwordx4 ... lds): a tile of ROWS x CPR

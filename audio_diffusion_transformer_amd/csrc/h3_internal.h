@@ -32,7 +32,8 @@ struct Plan {
     size_t qhat, khat, vt, knorm; // byte offsets into the workspace
     size_t q8, k8, v8t, qscale, kscale, ksum, vmax, kmean, vscale;
     size_t sp_kbar, sp_qsum, sp_cnt; // block-sparse selection scratch (after the bf16 regions)
-    size_t bytes_bf16, bytes_q8, bytes_sparse;
+    size_t qx, qxs, kx, kxs, vxt, vxs, mx_ksum, mx_kmean;   // MXFP4 path (mx.hip)
+    size_t bytes_bf16, bytes_q8, bytes_sparse, bytes_mx;
 };
 
 // Which sequence a padded 64-token tile belongs to: tiles of sequence s are
@@ -156,6 +157,61 @@ struct Q8ExportArgs {
     SeqTable seq;
 };
 
+// MXFP4 attention (mx.hip): OCP microscaling FP4, e2m1 codes with one E8M0
+// scale byte (2^(byte - 127)) per 32 elements.  Workspace:
+//   qx, kx : fp4 [H][Npad][d/2], two codes per byte (even channel in the low
+//            nibble), of qhat' = qhat * q_mult and of khat - mean; the 64 rows of every K tile are stored in the key order
+//            of the FP4 score operand (mx_key_row)
+//   qxs    : E8M0 [H][Npad][d/32]
+//   kxs    : E8M0 [H][ntiles][256], each tile's bytes in the order the
+//            attention kernel reads them (mx_kscale_pos)
+//   vxt    : fp4 [H][ntiles][d][32], V transposed per tile (a channel row of
+//            64 keys, key 2i in the low nibble of byte i)
+//   vxs    : E8M0 [H][ntiles][256] (mx_vscale_pos)
+//   ksum   : fp32 [H][ntiles][d] per-tile partial sums of khat
+//   kmean  : fp32 [S][H][d]
+struct MxArgs {
+    const uint16_t *q, *k, *v;
+    int64_t q_stride, k_stride, v_stride;
+    const float *norm_w, *rope;
+    uint8_t *qx, *qxs, *kx, *kxs, *vxt, *vxs;
+    float *ksum, *kmean;
+    int32_t H;
+    int64_t Npad;
+    float eps;
+    float q_mult;                // qhat is quantised times this (softmax scale * log2 e)
+    int32_t ntiles;
+    SeqTable seq;
+};
+
+struct MxAttnArgs {
+    const uint8_t *qx, *qxs, *kx, *kxs, *vxt, *vxs;
+    uint16_t *out;
+    int64_t o_stride;
+    int64_t Npad;
+    int32_t H;
+    int32_t nseq;
+    int32_t seq_n[kMaxSeqs];
+    int32_t seq_cu[kMaxSeqs];
+    int32_t seq_off[kMaxSeqs];
+    int32_t seq_nqb[kMaxSeqs];
+    int32_t item_pre[kMaxSeqs + 1];
+};
+
+// Natural-layout copy of the MXFP4 workspace (diagnostic export), one code
+// per byte: q_codes, k_codes, v_codes [N][H][d]; q_exp, k_exp [N][H][d/32]
+// and v_exp [NB][H][d] scale bytes, NB = sum over sequences of ceil(n / 32)
+// (32-token blocks in sequence order).
+struct MxExportArgs {
+    const uint8_t *qx, *qxs, *kx, *kxs, *vxt, *vxs;
+    uint8_t *q_codes, *q_exp, *k_codes, *k_exp, *v_codes, *v_exp;
+    int32_t H;
+    int64_t Npad;
+    int32_t ntiles;
+    SeqTable seq;
+    int32_t vblk_pre[kMaxSeqs + 1];   // prefix of ceil(n_s / 32)
+};
+
 // Fused QKV projection + RMSNorm + RoPE + layout (qkv_proj.hip).  x is bf16
 // [N][D] (token stride x_stride), w is bf16 [3*H*d][D] with the q, k and v
 // output features in that order, each head-major.  The outputs are those of
@@ -209,6 +265,9 @@ hipError_t launch_q8_export(const Q8ExportArgs &a, hipStream_t st);
 hipError_t launch_qkv_proj(const ProjArgs &a, int d, hipStream_t st);
 hipError_t launch_out_proj(const OutProjArgs &a, hipStream_t st);
 hipError_t launch_sparse_select(const SparseSelectArgs &a, int d, hipStream_t st);
+hipError_t launch_mx_prep(const MxArgs &a, int d, hipStream_t st);
+hipError_t launch_attn_mx(const MxAttnArgs &a, int d, int64_t nitems, hipStream_t st);
+hipError_t launch_mx_export(const MxExportArgs &a, hipStream_t st);
 
 // Queries per workgroup of the attention kernels (work-item granularity).
 constexpr int kBlockM = 128;

@@ -109,6 +109,16 @@ h3attn_status make_plan(const h3attn_params *p, const int32_t *cu, Plan *pl)
     pl->kmean = take(S * H * d * 4);
     pl->vscale = take(S * H * d * 4);
     pl->bytes_q8 = std::max<size_t>(at, 256);
+    at = 0;
+    pl->qx = take(H * Np * d / 2);
+    pl->qxs = take(H * Np * d / 32);
+    pl->kx = take(H * Np * d / 2);
+    pl->kxs = take(H * T * 256);
+    pl->vxt = take(H * Np * d / 2);
+    pl->vxs = take(H * T * 256);
+    pl->mx_ksum = take(H * T * d * 4);
+    pl->mx_kmean = take(S * H * d * 4);
+    pl->bytes_mx = std::max<size_t>(at, 256);
     return H3ATTN_OK;
 }
 
@@ -241,16 +251,17 @@ size_t h3attn_workspace_size(const h3attn_params *p, const int32_t *cu_seqlens_h
 {
     Plan pl;
     if (make_plan(p, cu_seqlens_host, &pl) != H3ATTN_OK) return 0;
-    if (quantized == 1 && pl.d != 128) {
-        fail(H3ATTN_ERR_UNSUPPORTED, "the quantised path needs head_dim 128");
+    if ((quantized == 1 || quantized == 3) && pl.d != 128) {
+        fail(H3ATTN_ERR_UNSUPPORTED, "the quantised paths need head_dim 128");
         return 0;
     }
-    if (quantized < 0 || quantized > 2) {
-        fail(H3ATTN_ERR_INVALID_ARG, "quantized must be 0, 1 or 2 (got %d)", quantized);
+    if (quantized < 0 || quantized > 3) {
+        fail(H3ATTN_ERR_INVALID_ARG, "quantized must be 0, 1, 2 or 3 (got %d)", quantized);
         return 0;
     }
     ok();
-    return quantized == 1 ? pl.bytes_q8 : quantized == 2 ? pl.bytes_sparse : pl.bytes_bf16;
+    return quantized == 1 ? pl.bytes_q8 : quantized == 2 ? pl.bytes_sparse : quantized == 3 ? pl.bytes_mx
+                                                                                            : pl.bytes_bf16;
 }
 
 h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -753,6 +764,127 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
     if ((st = hip_status(hipMemcpyAsync(k_mean, qa.kmean, sb, hipMemcpyDeviceToDevice, hs), "k_mean copy")) != H3ATTN_OK)
         return st;
     return hip_status(hipMemcpyAsync(v_scale, qa.vscale, sb, hipMemcpyDeviceToDevice, hs), "v_scale copy");
+}
+
+static h3attn_status mx_common(const h3attn_params *p, const void *q, const void *k, const void *v,
+                               const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                               const void *out, void *workspace, size_t workspace_bytes, Plan &pl, MxArgs &ma)
+{
+    h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
+    if (st != H3ATTN_OK) return st;
+    if (pl.d != 128) return fail(H3ATTN_ERR_UNSUPPORTED, "the FP4 path needs head_dim 128 (got %d)", pl.d);
+    if (pl.N == 0) return H3ATTN_OK;
+    if ((st = check_ptrs(q, k, v, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
+    if (!workspace) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(H3ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < pl.bytes_mx)
+        return fail(H3ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes_mx);
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    char *ws = static_cast<char *>(workspace);
+    std::memset(&ma, 0, sizeof ma);
+    ma.q = static_cast<const uint16_t *>(q);
+    ma.k = static_cast<const uint16_t *>(k);
+    ma.v = static_cast<const uint16_t *>(v);
+    ma.q_stride = p->q_stride;
+    ma.k_stride = p->k_stride;
+    ma.v_stride = p->v_stride;
+    ma.norm_w = norm_w;
+    ma.rope = rope_tables;
+    ma.qx = reinterpret_cast<uint8_t *>(ws + pl.qx);
+    ma.qxs = reinterpret_cast<uint8_t *>(ws + pl.qxs);
+    ma.kx = reinterpret_cast<uint8_t *>(ws + pl.kx);
+    ma.kxs = reinterpret_cast<uint8_t *>(ws + pl.kxs);
+    ma.vxt = reinterpret_cast<uint8_t *>(ws + pl.vxt);
+    ma.vxs = reinterpret_cast<uint8_t *>(ws + pl.vxs);
+    ma.ksum = reinterpret_cast<float *>(ws + pl.mx_ksum);
+    ma.kmean = reinterpret_cast<float *>(ws + pl.mx_kmean);
+    ma.H = pl.H;
+    ma.Npad = pl.Npad;
+    ma.eps = p->eps;
+    ma.q_mult = scale_log2(p);
+    ma.ntiles = (int32_t)(pl.Npad / kTile);
+    ma.seq = seq_table(pl);
+    return H3ATTN_OK;
+}
+
+h3attn_status h3attn_fwd_mx_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                   const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                                   void *out, void *workspace, size_t workspace_bytes, void *stream, int stages)
+{
+    if (stages < 1 || stages > 3) return fail(H3ATTN_ERR_INVALID_ARG, "stages must be 1, 2 or 3 (got %d)", stages);
+    Plan pl;
+    MxArgs ma;
+    h3attn_status st = mx_common(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, out, workspace,
+                                 workspace_bytes, pl, ma);
+    if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (stages & 1)
+        if ((st = hip_status(launch_mx_prep(ma, pl.d, hs), "FP4 prologue launch")) != H3ATTN_OK) return st;
+    if (!(stages & 2)) return ok();
+    MxAttnArgs aa;
+    std::memset(&aa, 0, sizeof aa);
+    aa.qx = ma.qx;
+    aa.qxs = ma.qxs;
+    aa.kx = ma.kx;
+    aa.kxs = ma.kxs;
+    aa.vxt = ma.vxt;
+    aa.vxs = ma.vxs;
+    aa.out = static_cast<uint16_t *>(out);
+    aa.o_stride = p->o_stride;
+    aa.Npad = pl.Npad;
+    aa.H = pl.H;
+    const int64_t items = order_work(pl, aa, nullptr);
+    return hip_status(launch_attn_mx(aa, pl.d, items, hs), "FP4 attention launch");
+}
+
+h3attn_status h3attn_fwd_mx(const h3attn_params *p, const void *q, const void *k, const void *v,
+                            const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                            void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return h3attn_fwd_mx_stages(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, out, workspace,
+                                workspace_bytes, stream, 3);
+}
+
+h3attn_status h3attn_mx_prologue(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                 const float *norm_w, const float *rope_tables,
+                                 const int32_t *cu_seqlens_host, void *workspace, size_t workspace_bytes,
+                                 uint8_t *q_codes, uint8_t *q_exp, uint8_t *k_codes, uint8_t *k_exp,
+                                 float *k_mean, uint8_t *v_codes, uint8_t *v_exp, void *stream)
+{
+    Plan pl;
+    MxArgs ma;
+    h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
+    if (st != H3ATTN_OK) return st;
+    const void *outs[7] = {q_codes, q_exp, k_codes, k_exp, k_mean, v_codes, v_exp};
+    const char *names[7] = {"q_codes", "q_exp", "k_codes", "k_exp", "k_mean", "v_codes", "v_exp"};
+    for (int i = 0; i < 7 && pl.N > 0; ++i)
+        if (!outs[i]) return fail(H3ATTN_ERR_INVALID_ARG, "%s is NULL", names[i]);
+    st = mx_common(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, q_codes, workspace, workspace_bytes, pl, ma);
+    if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = hip_status(launch_mx_prep(ma, pl.d, hs), "FP4 prologue launch")) != H3ATTN_OK) return st;
+    MxExportArgs ea;
+    std::memset(&ea, 0, sizeof ea);
+    ea.qx = ma.qx;
+    ea.qxs = ma.qxs;
+    ea.kx = ma.kx;
+    ea.kxs = ma.kxs;
+    ea.vxt = ma.vxt;
+    ea.vxs = ma.vxs;
+    ea.q_codes = q_codes;
+    ea.q_exp = q_exp;
+    ea.k_codes = k_codes;
+    ea.k_exp = k_exp;
+    ea.v_codes = v_codes;
+    ea.v_exp = v_exp;
+    ea.H = pl.H;
+    ea.Npad = pl.Npad;
+    ea.ntiles = ma.ntiles;
+    ea.seq = ma.seq;
+    for (int s = 0; s < pl.S; ++s) ea.vblk_pre[s + 1] = ea.vblk_pre[s] + (pl.cu[s + 1] - pl.cu[s] + 31) / 32;
+    if ((st = hip_status(launch_mx_export(ea, hs), "FP4 export launch")) != H3ATTN_OK) return st;
+    const size_t sb = (size_t)pl.S * pl.H * pl.d * sizeof(float);
+    return hip_status(hipMemcpyAsync(k_mean, ma.kmean, sb, hipMemcpyDeviceToDevice, hs), "k_mean copy");
 }
 
 h3attn_status h3attn_rope_fill_video(int32_t T, int32_t Hg, int32_t Wg, int32_t dt, int32_t dh, int32_t dw,

@@ -27,7 +27,8 @@ H3ATTN_MAX_SEQS = 64
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
             "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
             "h3attn_proj_prologue", "h3attn_out_proj", "h3attn_fwd_sparse", "h3attn_fwd_sparse_stages",
-            "h3attn_q8_prologue", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
+            "h3attn_q8_prologue", "h3attn_fwd_mx", "h3attn_fwd_mx_stages", "h3attn_mx_prologue",
+            "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
 
@@ -59,10 +60,10 @@ def lib():
         L.h3attn_workspace_size.restype = C.c_size_t
         L.h3attn_workspace_size.argtypes = [P(h3attn_params), P(C.c_int32), C.c_int]
         fwd_args = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp, vp, C.c_size_t, vp]
-        for name in ("h3attn_fwd", "h3attn_fwd_q8"):
+        for name in ("h3attn_fwd", "h3attn_fwd_q8", "h3attn_fwd_mx"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = fwd_args
-        for name in ("h3attn_fwd_stages", "h3attn_fwd_q8_stages"):
+        for name in ("h3attn_fwd_stages", "h3attn_fwd_q8_stages", "h3attn_fwd_mx_stages"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = fwd_args + [C.c_int]
         proj_args = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp, P(C.c_int32), vp, vp,
@@ -86,6 +87,9 @@ def lib():
         L.h3attn_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, P(C.c_int32), vp, vp, vp]
         L.h3attn_q8_prologue.restype = C.c_int
         L.h3attn_q8_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp,
+                                         C.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.h3attn_mx_prologue.restype = C.c_int
+        L.h3attn_mx_prologue.argtypes = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp,
                                          C.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
         L.h3attn_rope_fill_video.restype = C.c_int
         L.h3attn_rope_fill_video.argtypes = [C.c_int32] * 6 + [C.c_double, P(C.c_float)]
@@ -133,10 +137,20 @@ def _cu_ptr(cu: np.ndarray):
     return cu.ctypes.data_as(C.POINTER(C.c_int32))
 
 
+def _mode(quantized) -> int:
+    """False/0: bf16; True/1: INT8/FP8; 2: bf16 plus the sparse selection; "mx"/3: MXFP4."""
+    if isinstance(quantized, str):
+        if quantized != "mx":
+            raise ValueError("quantized must be a bool, 0..3 or 'mx' (got %r)" % quantized)
+        return 3
+    return int(quantized)
+
+
 def h3attn_workspace_size(params: h3attn_params, cu_seqlens, quantized=False) -> int:
-    """Workspace bytes: quantized False/0 bf16, True/1 quantised, 2 bf16 plus the sparse selection."""
+    """Workspace bytes: quantized False/0 bf16, True/1 INT8/FP8, 2 bf16 plus the
+    sparse selection, "mx"/3 MXFP4."""
     cu = _cu_array(cu_seqlens)
-    n = int(lib().h3attn_workspace_size(C.byref(params), _cu_ptr(cu), int(quantized)))
+    n = int(lib().h3attn_workspace_size(C.byref(params), _cu_ptr(cu), _mode(quantized)))
     if n == 0:
         raise H3AttnError(H3ATTN_ERR_INVALID_ARG, last_error())
     return n
@@ -145,18 +159,20 @@ def h3attn_workspace_size(params: h3attn_params, cu_seqlens, quantized=False) ->
 # ---------------------------------------------------------------- raw calls
 
 def fwd_raw(params, q, k, v, norm_w, rope_tables, cu_seqlens, out, workspace, workspace_bytes,
-            stream, quantized: bool = False, stages: int = 3) -> int:
+            stream, quantized=False, stages: int = 3) -> int:
     """Direct call with integer device pointers; returns the status code.
-    ``stages`` (1 prologue, 2 attention, 3 both) selects h3attn_fwd_stages /
-    h3attn_fwd_q8_stages when it is not 3."""
+    ``quantized`` picks h3attn_fwd (False), h3attn_fwd_q8 (True) or
+    h3attn_fwd_mx ("mx"); ``stages`` (1 prologue, 2 attention, 3 both) selects
+    the matching *_stages entry point when it is not 3."""
     cu = _cu_array(cu_seqlens)
     args = (C.byref(params), q, k, v, norm_w, rope_tables, _cu_ptr(cu), out, workspace,
             workspace_bytes, stream)
+    name = {0: "h3attn_fwd", 1: "h3attn_fwd_q8", 3: "h3attn_fwd_mx"}.get(_mode(quantized))
+    if name is None:
+        raise ValueError("quantized must be False, True or 'mx'")
     if stages != 3:
-        f = lib().h3attn_fwd_q8_stages if quantized else lib().h3attn_fwd_stages
-        return int(f(*args, int(stages)))
-    f = lib().h3attn_fwd_q8 if quantized else lib().h3attn_fwd
-    return int(f(*args))
+        return int(getattr(lib(), name + "_stages")(*args, int(stages)))
+    return int(getattr(lib(), name)(*args))
 
 
 # ------------------------------------------------------------ torch helpers
@@ -216,6 +232,12 @@ def h3attn_fwd_q8(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=
                   eps: float = 1e-6, softmax_scale: float = 0.0, stream=None):
     return h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out, workspace, eps,
                       softmax_scale, stream, quantized=True)
+
+
+def h3attn_fwd_mx(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=None,
+                  eps: float = 1e-6, softmax_scale: float = 0.0, stream=None, stages: int = 3):
+    return h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out, workspace, eps,
+                      softmax_scale, stream, quantized="mx", stages=stages)
 
 
 def h3attn_prologue(q, k, norm_w, rope_tables, cu_seqlens, q_hat=None, k_hat=None,
@@ -389,6 +411,37 @@ def h3attn_q8_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,
         _dev_ptr(rope_tables), _cu_ptr(cu), _dev_ptr(workspace),
         workspace.numel() * workspace.element_size(),
         *[_dev_ptr(res[n]) for n in ("q8", "k8", "q_scale", "k_scale", "k_mean", "v8", "v_scale")],
+        _stream_ptr(stream)))
+    return res
+
+
+def h3attn_mx_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,
+                       eps: float = 1e-6, stream=None):
+    """FP4 prologue exported in natural layouts, one code per byte (see include/h3attn.h)."""
+    import torch
+    N, H, d = q.shape
+    cu = _cu_array(cu_seqlens)
+    S = len(cu) - 1
+    nvb = int(sum((int(cu[s + 1] - cu[s]) + 31) // 32 for s in range(S)))
+    params = params_for(q, k, v, q, S, eps)
+    if workspace is None:
+        workspace = torch.empty(h3attn_workspace_size(params, cu, "mx"), dtype=torch.uint8,
+                                device=q.device)
+    dev = q.device
+    res = {
+        "q_codes": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
+        "q_exp": torch.empty((N, H, d // 32), dtype=torch.uint8, device=dev),
+        "k_codes": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
+        "k_exp": torch.empty((N, H, d // 32), dtype=torch.uint8, device=dev),
+        "k_mean": torch.empty((S, H, d), dtype=torch.float32, device=dev),
+        "v_codes": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
+        "v_exp": torch.empty((nvb, H, d), dtype=torch.uint8, device=dev),
+    }
+    _check(lib().h3attn_mx_prologue(
+        C.byref(params), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w),
+        _dev_ptr(rope_tables), _cu_ptr(cu), _dev_ptr(workspace),
+        workspace.numel() * workspace.element_size(),
+        *[_dev_ptr(res[n]) for n in ("q_codes", "q_exp", "k_codes", "k_exp", "k_mean", "v_codes", "v_exp")],
         _stream_ptr(stream)))
     return res
 

@@ -61,6 +61,7 @@ class Workload:
     k_offset_std: float = 0.0            # per-(head, channel) offset on raw K
     seed: int = 0
     quantized: bool = False
+    fp4: bool = False                    # MXFP4 path (h3attn_fwd_mx)
     sharp: bool = False                  # diagnostic: per-token scale + larger weights
     model_dim: int = 0                   # D > 0: inputs are hidden states x [N, D] and W_qkv
     keep_tiles: int = 0                  # > 0: block-sparse attention keeping this many 64-key tiles per 128-row block
@@ -122,6 +123,9 @@ WORKLOADS: Dict[str, Workload] = {
         "q8", H=24, d=128, seqs=(Seq(36, 30, 54),), split=_SPLIT128, seed=1005,
         quantized=True,
         description="INT8-QK / FP8-PV path at the 58,320-token video shape"),
+    "mx": Workload(
+        "mx", H=24, d=128, seqs=(Seq(36, 30, 54),), split=_SPLIT128, seed=1007, fp4=True,
+        description="MXFP4 path at the 58,320-token video shape"),
     "sparse_joint": Workload(
         "sparse_joint", H=24, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128,
         k_offset_std=0.5, seed=1003, keep_tiles=490,

@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 MI355X_BF16_DENSE_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense, no sparsity)
 MI355X_FP8_DENSE_TFLOPS = 5033.2
+MI355X_FP4_DENSE_TFLOPS = 10066.4     # FP4 (and FP6) dense MFMA
 MI355X_HBM_GBPS = 8000.0
 METRIC = "attention TFLOP/s and % of bf16 MFMA peak at N=125k packed tokens, H=24, d=128"
 
@@ -170,11 +171,13 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
         p = oracle.Problem.from_workload(w, inputs)
         H_rows, head_row = w.H, head
 
+    rows_fn = p.mx_attention_rows if w.fp4 else p.attention_rows
+
     def run(nrows):
         toks = np.sort(rng.choice(n, size=nrows, replace=False)).astype(np.int64)
         rows = toks * H_rows + head_row
         t0 = time.perf_counter()
-        p.attention_rows(rows, nthreads=threads)
+        rows_fn(rows, nthreads=threads)
         return time.perf_counter() - t0
 
     # fixed cost (the keys' prologue) + per-row cost, from two probes
@@ -191,6 +194,8 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
     value = nrows * flops_per_row / t / 1e12
     sample = ("%d query rows of head %d (of %d x %d rows), each over all %d keys; fp64; "
               "the keys' RMSNorm+RoPE included; %.1f s" % (nrows, head, w.N, w.H, n, t))
+    if w.fp4:
+        sample += "; the step-by-step MXFP4 emulation (codes of q, k, v, FP4 probabilities)"
     if w.model_dim > 0:
         sample += ("; plus the head's fp64 QKV projection of all tokens (%.1f s, %.0f%% of it "
                    "charged to the sampled rows)" % (proj_s, 100.0 * nrows / n))
@@ -356,7 +361,8 @@ def main():
         q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
         params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
         ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
-    ws_bytes = h.h3attn_workspace_size(params, cu, 2 if sparse else int(w.quantized))
+    mode = "mx" if w.fp4 else w.quantized
+    ws_bytes = h.h3attn_workspace_size(params, cu, 2 if sparse else mode)
     if sparse:
         tiles = torch.empty((h.sparse_items(cu, w.H), w.keep_tiles), dtype=torch.int32, device=dev)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -388,8 +394,7 @@ def main():
             st = h.proj_raw(params, w.model_dim, x.data_ptr(), x.stride(0), wq.data_ptr(), norm_w.data_ptr(),
                             rope.data_ptr(), cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp, sid)
         else:
-            st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp,
-                           w.quantized, sid)
+            st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp, mode, sid)
         if st != 0:
             raise RuntimeError("%s: %s" % (h.status_string(st), h.last_error()))
 
@@ -441,13 +446,21 @@ def main():
 
     flops = attn_flops + w.proj_flops() + out_flops
     value = flops / (ms_step * 1e-3) / 1e12
-    peak = MI355X_FP8_DENSE_TFLOPS if w.quantized else MI355X_BF16_DENSE_TFLOPS
+    peak = (MI355X_FP4_DENSE_TFLOPS if w.fp4 else MI355X_FP8_DENSE_TFLOPS if w.quantized
+            else MI355X_BF16_DENSE_TFLOPS)
     achieved = attn_flops / (att_avg * 1e-3) / 1e12
-    kernel_file = "q8.hip" if w.quantized else "attn_bf16.hip"
-    summary = ("attn_q8_%s_pmc.md" if w.quantized else "attn_bf16_%s_pmc.md") % w.name
+    kname = "mx" if w.fp4 else "q8" if w.quantized else "bf16"
+    kernel_file = {"mx": "mx.hip", "q8": "q8.hip", "bf16": "attn_bf16.hip"}[kname]
+    summary = "attn_%s_%s_pmc.md" % (kname, w.name)
     traffic = measured_traffic(kernel_file, summary)
     N, H, d = w.N, w.H, w.d
-    if w.quantized:
+    if w.fp4:
+        # pass 1 reads q, k and the table and writes FP4 q; pass 3 re-reads k, v and
+        # the table and writes FP4 k and v; one scale byte per 32 values
+        pro_bytes = 4 * N * H * d * 2 + 2 * N * (d // 2) * 8 + 3 * N * H * d // 2 + 3 * N * H * d // 32
+        metric = ("attention TFLOP/s (MXFP4 QK and PV) and %% of fp4 MFMA peak at N=%d packed tokens, "
+                  "H=%d, d=%d" % (N, H, d))
+    elif w.quantized:
         # pass 1 reads q, k, v and the table and writes q8; pass 3 re-reads k, v and the
         # table and writes k8 and v8 (per-tile scales and sums are negligible)
         pro_bytes = 5 * N * H * d * 2 + 3 * N * H * d + 2 * N * (d // 2) * 8
@@ -477,14 +490,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8/fp8" if w.quantized else "bf16",
+        "dtype": {"mx": "mxfp4", "q8": "int8/fp8", "bf16": "bf16"}[kname],
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "tokens": N, "heads": H,
                    "head_dim": d, "seq_lens": [s.n for s in w.seqs], "parallelism": "none"},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "attn_q8_kernel" if w.quantized else "attn_bf16_kernel<128>",
+                     "kernel": {"mx": "attn_mx_kernel", "q8": "attn_q8_kernel",
+                                "bf16": "attn_bf16_kernel<128>"}[kname],
                      "avg_ms": round(att_avg, 4)},
         "step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 4),
                     "p50": round(float(np.percentile(step_ms, 50)), 4),

@@ -74,8 +74,8 @@ typedef struct h3attn_params {
 
 /*
  * Bytes of device workspace h3attn_fwd (quantized = 0), h3attn_fwd_q8
- * (quantized = 1) or h3attn_fwd_sparse with its tile selection (quantized = 2)
- * needs for this shape.  cu_seqlens_host: HOST int32 [S+1],
+ * (quantized = 1), h3attn_fwd_sparse with its tile selection (quantized = 2)
+ * or h3attn_fwd_mx (quantized = 3) needs for this shape.  cu_seqlens_host: HOST int32 [S+1],
  * cu[0] = 0, non-decreasing; N = cu[S] is the packed token count.  Returns 0
  * and sets the last error when the arguments are invalid.
  */
@@ -137,6 +137,58 @@ h3attn_status h3attn_fwd_q8_stages(const h3attn_params *p, const void *q, const 
                                    const void *v, const float *norm_w, const float *rope_tables,
                                    const int32_t *cu_seqlens_host, void *out, void *workspace,
                                    size_t workspace_bytes, void *stream, int stages);
+
+/*
+ * MXFP4 variant with the same arguments and result layout (head_dim 128;
+ * workspace >= h3attn_workspace_size(p, cu, 3)).  The FastVideo commit page
+ * for docs/getting_started notes an FP4 attention switch (faster, changes the
+ * output, off by default) and "H3 Runtime Current State" keeps the approximate
+ * backends quality-gated; the pages give no format, so this is OCP MXFP4, the
+ * format the CDNA4 FP4 matrix cores take: e2m1 codes (round to nearest even,
+ * saturating at 6) with one power-of-two scale 2^X per block of 32 values,
+ * X = floor(log2 amax) - 2 limited to [-126, 127] (0 for an all-zero block).
+ * After the same RMSNorm + RoPE and the per-sequence K mean of
+ * h3attn_fwd_q8: qhat' = qhat * softmax scale * log2 e (so that scores are
+ * in log2 units) and khat - mean in blocks of 32 channels, v in blocks
+ * of 32 tokens per channel (aligned to the sequence start), scores on the
+ * scaled FP4 MFMA with fp32 accumulation, the lazy base-2 running maximum of
+ * h3attn_fwd_q8, and each query row's probabilities of every 32-key block
+ * (aligned to the sequence start) as one MX block; the row sum is the sum of
+ * those quantised probabilities.  Lossy: the result approximates h3attn_fwd
+ * more loosely than h3attn_fwd_q8.
+ */
+h3attn_status h3attn_fwd_mx(const h3attn_params *p, const void *q, const void *k,
+                            const void *v, const float *norm_w, const float *rope_tables,
+                            const int32_t *cu_seqlens_host, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* The two stages of h3attn_fwd_mx (1: FP4 prologue, 2: attention, 3: both);
+ * same contract as h3attn_fwd_stages. */
+h3attn_status h3attn_fwd_mx_stages(const h3attn_params *p, const void *q, const void *k,
+                                   const void *v, const float *norm_w, const float *rope_tables,
+                                   const int32_t *cu_seqlens_host, void *out, void *workspace,
+                                   size_t workspace_bytes, void *stream, int stages);
+
+/*
+ * Diagnostic: the FP4 prologue of h3attn_fwd_mx, exported in natural layouts,
+ * one e2m1 code (0..15: sign bit 8, then exponent and mantissa) per byte and
+ * one E8M0 scale byte (X + 127) per block.  Runs the same kernels as
+ * h3attn_fwd_mx into `workspace`, then copies out:
+ *   q_codes, k_codes  device uint8 [N][H][d]     codes of qhat' (qhat * softmax scale
+ *                                                * log2 e) and of khat - mean
+ *   q_exp, k_exp      device uint8 [N][H][d/32]  block scale bytes (32 channels)
+ *   k_mean            device fp32 [S][H][d]      per-sequence mean of khat
+ *   v_codes           device uint8 [N][H][d]     codes of v
+ *   v_exp             device uint8 [NB][H][d]    block scale bytes of v: NB = sum
+ *                     over sequences of ceil(n_s / 32); block b of sequence s is
+ *                     entry (sum_{s'<s} ceil(n_s'/32)) + b
+ */
+h3attn_status h3attn_mx_prologue(const h3attn_params *p, const void *q, const void *k,
+                                 const void *v, const float *norm_w, const float *rope_tables,
+                                 const int32_t *cu_seqlens_host, void *workspace,
+                                 size_t workspace_bytes, uint8_t *q_codes, uint8_t *q_exp,
+                                 uint8_t *k_codes, uint8_t *k_exp, float *k_mean,
+                                 uint8_t *v_codes, uint8_t *v_exp, void *stream);
 
 /*
  * Diagnostic: the fused RMSNorm + RoPE prologue alone, written as bf16 qhat and

@@ -213,6 +213,47 @@ def test_quantised_path_argument_errors():
     assert _call(ptrs={"v": 0}, quantized=True) == h.H3ATTN_ERR_INVALID_ARG
 
 
+def test_fp4_path_argument_errors():
+    small = _params(num_heads=2, head_dim=64, q_stride=128, k_stride=128, v_stride=128, o_stride=128)
+    assert _call(small, quantized="mx") == h.H3ATTN_ERR_UNSUPPORTED
+    assert "head_dim 128" in h.last_error()
+    with pytest.raises(h.H3AttnError):
+        h.h3attn_workspace_size(small, [0, 1000], quantized="mx")
+    need = h.h3attn_workspace_size(_params(), [0, 1000], quantized="mx")
+    # FP4 codes (d/2 bytes per row of q, k and v) and scale bytes are smaller than the INT8/FP8 copies
+    assert need < h.h3attn_workspace_size(_params(), [0, 1000], quantized=True)
+    assert need == h.h3attn_workspace_size(_params(), [0, 1000], quantized=3)
+    assert _call(ws_bytes=need - 1, quantized="mx") == h.H3ATTN_ERR_WORKSPACE
+    assert _call(ptrs={"ws": FAKE * 256 + 16}, quantized="mx") == h.H3ATTN_ERR_WORKSPACE
+    assert _call(quantized="mx", stages=0) == h.H3ATTN_ERR_INVALID_ARG
+    assert _call(quantized="mx", stages=4) == h.H3ATTN_ERR_INVALID_ARG
+    assert _call(ptrs={"k": 0}, quantized="mx") == h.H3ATTN_ERR_INVALID_ARG
+    assert _call(ptrs={"out": FAKE + 2}, quantized="mx") == h.H3ATTN_ERR_INVALID_ARG
+    # empty input: nothing read, written or launched
+    assert _call(cu=(0, 0), ptrs={"q": 0, "k": 0, "v": 0, "out": 0, "ws": 0}, quantized="mx") == h.H3ATTN_OK
+    # a valid call reaches the device check (only where no GPU is present)
+    if not _gpu_present():
+        assert _call(quantized="mx") == h.H3ATTN_ERR_DEVICE
+    with pytest.raises(ValueError):
+        h.fwd_raw(_params(), FAKE, FAKE, FAKE, FAKE, FAKE, np.array([0, 10], np.int32), FAKE, FAKE * 256,
+                  1 << 40, None, "fp4")
+
+
+def test_fp4_prologue_export_errors():
+    import ctypes as C
+    L = h.lib()
+    cu = np.array([0, 1000], np.int32)
+    outs = [FAKE] * 7
+    args = lambda o: (C.byref(_params()), FAKE, FAKE, FAKE, FAKE, FAKE, cu.ctypes.data_as(C.POINTER(C.c_int32)),
+                      FAKE * 256, 1 << 40, *o, None)
+    names = ("q_codes", "q_exp", "k_codes", "k_exp", "k_mean", "v_codes", "v_exp")
+    for i in range(7):      # every output is checked before any device call
+        o = list(outs)
+        o[i] = 0
+        assert L.h3attn_mx_prologue(*args(o)) == h.H3ATTN_ERR_INVALID_ARG
+        assert names[i] in h.last_error() and "NULL" in h.last_error()
+
+
 def _proj_call(params=None, model_dim=3072, x_stride=3072, cu=(0, 1000), ws_bytes=1 << 40, ptrs=None,
                stages=3):
     params = params if params is not None else _params()
@@ -325,4 +366,4 @@ def test_sparse_workspace_sizes():
         assert _sparse_call(ws_bytes=dense, stages=5) == h.H3ATTN_ERR_DEVICE
     assert h.sparse_items([0, 1000, 1000, 1129], 24) == 24 * 8 + 24 * 2
     with pytest.raises(h.H3AttnError):
-        h.h3attn_workspace_size(p, [0, 1000], 3)
+        h.h3attn_workspace_size(p, [0, 1000], 4)

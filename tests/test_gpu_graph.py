@@ -45,15 +45,15 @@ def _replays(torch, fn, out, label, n=4):
         del junk
 
 
-@pytest.mark.parametrize("path", ["bf16", "q8", "sparse"])
+@pytest.mark.parametrize("path", ["bf16", "q8", "mx", "sparse"])
 def test_attention_entry_points_replay(torch_dev, path):
     torch = torch_dev
     inp = synth.generate(W)
     t = G.to_device(inp, W)
     out = torch.empty_like(t["q"])
-    quant = path == "q8"
+    quant = {"q8": True, "mx": "mx"}.get(path, False)
     ws = torch.empty(h.h3attn_workspace_size(h.params_for(t["q"], t["k"], t["v"], out, W.S), inp["cu_seqlens"],
-                                             2 if path == "sparse" else int(quant)), dtype=torch.uint8,
+                                             2 if path == "sparse" else quant), dtype=torch.uint8,
                      device="cuda:0")
     tiles = torch.empty((h.sparse_items(inp["cu_seqlens"], W.H), 3), dtype=torch.int32, device="cuda:0")
 

@@ -1,0 +1,186 @@
+"""GPU parity of the MXFP4 path (h3attn_fwd_mx, h3attn_mx_prologue).
+
+Stage parity: the e2m1 codes and E8M0 scale bytes of qhat' (qhat times the
+softmax scale and log2 e) and of khat - mean (blocks of 32 channels), of v (blocks of 32 tokens) and the per-sequence K
+mean are compared with the oracle's MX quantisers.  The GPU computes the
+values being rounded in fp32 and the oracle in fp64, so a code may differ
+only where the oracle's value x / 2^X lies within 1e-5 (relative) of an e2m1
+rounding midpoint, and a block's scale only where its largest magnitude lies
+within 1e-5 of a power of two; both must be rare, every other code and scale
+equal.
+
+End to end: against the oracle's step-by-step emulation of the FP4 path (same
+codes, scales, tiles, lazy maximum and FP4 probabilities) at a tight gate, and
+against exact attention at the FP4 quality guards (MX_GATE at full size,
+MX_SMALL_GATE on the small cases).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from audio_diffusion_transformer_amd import h3attn as h
+from audio_diffusion_transformer_amd import synth
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+Seq = synth.Seq
+
+SMALL = {
+    "mx_ragged_337": synth.Workload("mx_ragged_337", H=3, d=128, seqs=(Seq(3, 10, 11, 7),),
+                                    split=(32, 48, 48), seed=31, fp4=True),
+    # lengths 144+0, 0, 90, 33, 1: empty sequences, a one-token sequence, one
+    # shorter than a 32-key block and a short last block
+    "mx_multi_seq_offset": synth.Workload(
+        "mx_multi_seq_offset", H=2, d=128,
+        seqs=(Seq(2, 8, 9), Seq(0, 1, 1), Seq(1, 4, 5, 70), Seq(0, 1, 1, 33), Seq(1, 1, 1)),
+        split=(32, 48, 48), k_offset_std=0.5, seed=32, fp4=True),
+    "mx_long_2100_offset": synth.Workload("mx_long_2100_offset", H=2, d=128,
+                                          seqs=(Seq(6, 15, 20, 300),), split=(32, 48, 48),
+                                          k_offset_std=0.5, seed=33, fp4=True),
+    # 128 and 192 tokens: two and three whole tiles (the kernel's even/odd tails)
+    "mx_whole_tiles": synth.Workload("mx_whole_tiles", H=2, d=128, seqs=(Seq(2, 8, 8), Seq(3, 8, 8)),
+                                     split=(32, 48, 48), seed=34, fp4=True),
+}
+MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+def _near_midpoint(ratio):
+    a = np.abs(ratio)[..., None]
+    return (np.abs(a - MIDPOINTS) <= 1e-5 * np.maximum(a, 1e-30)).any(axis=-1)
+
+
+def _near_pow2(amax):
+    with np.errstate(divide="ignore"):
+        l2 = np.log2(np.maximum(amax, 1e-300))
+    return np.abs(l2 - np.round(l2)) <= 1e-5 / np.log(2)
+
+
+def _compare_blocks(gc, gx, oc, ox, vals, label):
+    """Codes gc/oc [..., 32] and scale exponents (GPU byte gx, oracle X ox) of
+    blocks of 32 values `vals`; returns (codes that differ, blocks whose scale
+    differs)."""
+    amax = np.abs(vals).max(axis=-1)
+    xdiff = gx.astype(np.int32) - 127 != ox
+    assert not (xdiff & ~_near_pow2(amax)).any(), "%s: scale bytes differ away from a power of two" % label
+    same = ~xdiff
+    ratio = vals / np.ldexp(1.0, ox)[..., None]
+    cdiff = (gc != oc) & same[..., None]
+    bad = cdiff & ~_near_midpoint(ratio)
+    assert not bad.any(), "%s: %d codes differ away from a rounding midpoint" % (label, int(bad.sum()))
+    return int(cdiff.sum()), int(xdiff.sum())
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_mx_prologue_stage(torch_dev, name):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    G.announce("mx prologue %s" % name)
+    res = h.h3attn_mx_prologue(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], eps=w.eps)
+    torch_dev.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in res.items()}
+    p = oracle.Problem.from_workload(w, inp)
+    km = p.q8_kmean()
+    np.testing.assert_allclose(g["k_mean"], km, rtol=0, atol=2e-5)
+    cu = inp["cu_seqlens"]
+    nvb = [(int(cu[s + 1] - cu[s]) + 31) // 32 for s in range(w.S)]
+    vpre = np.concatenate([[0], np.cumsum(nvb)]).astype(int)
+    codes_off = scales_off = blocks = 0
+    for s in range(w.S):
+        n = int(cu[s + 1] - cu[s])
+        if n == 0:
+            continue
+        toks = np.arange(cu[s], cu[s + 1])
+        for hd in range(w.H):
+            for which, key in ((0, "q"), (1, "k")):
+                oc, ox = p.mx_qk_quant(which, s, hd, kmean=km)
+                vals = p.prologue_rows(which, toks * w.H + hd)
+                if which == 0:
+                    vals = vals * (p.scale / np.log(2.0))
+                if which == 1:
+                    vals = vals - km[s, hd]
+                c, x = _compare_blocks(g[key + "_codes"][toks, hd].reshape(n, 4, 32), g[key + "_exp"][toks, hd],
+                                       oc.reshape(n, 4, 32), ox, vals.reshape(n, 4, 32),
+                                       "%s %s s%d h%d" % (name, key, s, hd))
+                codes_off += c
+                scales_off += x
+                blocks += n * 4
+            oc, ox = p.mx_v_quant(s, hd)
+            v = G.decode(inp["v"][cu[s]:cu[s + 1], hd])
+            pad = nvb[s] * 32 - n
+            vb = np.concatenate([v, np.zeros((pad, 128))]).reshape(nvb[s], 32, 128).transpose(0, 2, 1)
+            gcv = np.concatenate([g["v_codes"][toks, hd], np.zeros((pad, 128), np.uint8)])
+            ocv = np.concatenate([oc, np.zeros((pad, 128), np.uint8)])
+            c, x = _compare_blocks(gcv.reshape(nvb[s], 32, 128).transpose(0, 2, 1), g["v_exp"][vpre[s]:vpre[s + 1], hd],
+                                   ocv.reshape(nvb[s], 32, 128).transpose(0, 2, 1), ox, vb,
+                                   "%s v s%d h%d" % (name, s, hd))
+            codes_off += c
+            scales_off += x
+            blocks += nvb[s] * 128
+    G.announce("%s: %d codes and %d of %d block scales differ at rounding boundaries" % (
+        name, codes_off, scales_off, blocks))
+    assert scales_off <= max(2, blocks // 1000), name
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_mx_attention_tracks_exact_all_rows(torch_dev, name):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized="mx", label=name))
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    ref = G.oracle_rows(w, inp, rows)
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.MX_SMALL_GATE, name)
+
+
+def _emulation_metrics(got, ref):
+    m = G.metrics(got, ref)
+    m["max_rel_row"] = float((np.linalg.norm(got - ref, axis=1) /
+                              np.maximum(np.linalg.norm(ref, axis=1), 1e-30)).max())
+    return m
+
+
+@pytest.mark.parametrize("name", sorted(SMALL) + ["mx"])
+def test_mx_attention_matches_stepwise_emulation(torch_dev, name):
+    """Against the oracle's step-by-step emulation of the FP4 path: the GPU
+    reaches the same values up to fp32 arithmetic, the bf16 output rounding and
+    the rare code that fp32 rounds across a boundary."""
+    w = SMALL[name] if name in SMALL else synth.WORKLOADS["mx"]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized="mx", label=name + "_vs_emulation"))
+    del t
+    rows = (np.arange(w.N * w.H, dtype=np.int64) if name in SMALL else synth.sample_rows(w, 512, seed=12))
+    p = oracle.Problem.from_workload(w, inp)
+    ref = p.mx_attention_rows(rows, nthreads=G.oracle_threads())
+    m = _emulation_metrics(G.gpu_rows(out, rows, w.H), ref)
+    print(name, m)
+    G.check(m, G.MX_EMULATION_GATE, name + " vs emulation")
+
+
+@pytest.mark.parametrize("name", ["mx", "joint_mx"])
+def test_mx_attention_full_size_sampled(torch_dev, name):
+    w = synth.WORKLOADS["mx"] if name == "mx" else synth.WORKLOADS["joint"].replace(name="joint_mx", fp4=True)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized="mx", label=name))
+    del t
+    rows = synth.sample_rows(w, 2048)
+    ref = G.oracle_rows(w, inp, rows)
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.MX_GATE, name)
+
+
+def test_mx_repeat_calls_bit_identical(torch_dev):
+    w = SMALL["mx_long_2100_offset"]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    a = G.bits(G.run(w, t, quantized="mx", label="mx determinism-1"))
+    b = G.bits(G.run(w, t, quantized="mx", label="mx determinism-2"))
+    np.testing.assert_array_equal(a, b)
