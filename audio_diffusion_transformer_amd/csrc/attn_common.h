@@ -18,6 +18,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kWaitVmcnt0 = 0x0F70;
 // Word 3 of a raw (unformatted, stride 0) buffer descriptor on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
+// s_waitcnt immediate (gfx9 encoding): vmcnt = n < 64, lgkmcnt = 0, expcnt at its maximum.
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would wait for every direct-to-LDS fill in flight, including those of
+// stages that are not read yet.  The caller has already waited for what the
+// barrier hands over; the clobber keeps memory accesses on their side of it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {

@@ -26,14 +26,6 @@ constexpr int kGemmBK = 32;      // K elements per slab
 constexpr int kGemmStages = 4;
 constexpr int kGemmWaves = 8;
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt = n < 64, lgkmcnt = 0, expcnt at its maximum.
-constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
-
-// Workgroup barrier without the memory fence of __syncthreads(): the fence
-// would wait for every direct-to-LDS fill in flight, including those of
-// stages that are not read yet.  The caller has already waited for what the
-// barrier hands over; the clobber keeps memory accesses on their side of it.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 // Direct-to-LDS fill of a slab of ROWS rows x 4 16-byte chunks (32 bf16), the
 // rows `row_bytes` apart in global memory, shared by the workgroup's waves.
