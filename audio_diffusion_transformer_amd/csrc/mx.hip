@@ -450,19 +450,24 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(MxAttnArgs a)
         step(j + 2, lk2, lv2, lks2, lvs2, true, lk1, lv1, lks1, lvs1, false, min(j + 4, nt - 1));
         wait_next(one_pending());
     }
-    // the last one to three tiles (buffers 0, 1, 2 in turn), the last one masked
-    if (j + 1 == nt) {
-        step(j, lk0, lv0, lks0, lvs0, false, nullptr, nullptr, nullptr, nullptr, true, 0);
-    } else if (j + 2 == nt) {
-        step(j, lk0, lv0, lks0, lvs0, false, nullptr, nullptr, nullptr, nullptr, false, 0);
-        wait_next(none_pending());
-        step(j + 1, lk1, lv1, lks1, lvs1, false, nullptr, nullptr, nullptr, nullptr, true, 0);
-    } else {
-        step(j, lk0, lv0, lks0, lvs0, true, lk2, lv2, lks2, lvs2, false, j + 2);
-        wait_next(one_pending());
-        step(j + 1, lk1, lv1, lks1, lvs1, false, nullptr, nullptr, nullptr, nullptr, false, 0);
-        wait_next(none_pending());
-        step(j + 2, lk2, lv2, lks2, lvs2, false, nullptr, nullptr, nullptr, nullptr, true, 0);
+    // The last one to three tiles (buffers 0, 1, 2 in turn; the last tile
+    // masked), with the buffer picked at run time: the compiler then waits
+    // for every fill before reading LDS, which only costs these few steps,
+    // and one copy of the step keeps the code small.
+    auto kb = [&](int r) -> uint8_t * { return r == 0 ? lk0 : r == 1 ? lk1 : lk2; };
+    auto vb = [&](int r) -> uint8_t * { return r == 0 ? lv0 : r == 1 ? lv1 : lv2; };
+    auto ksb = [&](int r) -> uint32_t * { return r == 0 ? lks0 : r == 1 ? lks1 : lks2; };
+    auto vsb = [&](int r) -> uint32_t * { return r == 0 ? lvs0 : r == 1 ? lvs1 : lvs2; };
+    for (int r = 0; j < nt; ++j, ++r) {
+        const bool last = j + 1 == nt;
+        // a fill only where tile j+2 exists and is not in flight yet (the loop
+        // above issued tiles up to j+1)
+        const bool more = r == 0 && j + 2 < nt;
+        step(j, kb(r), vb(r), ksb(r), vsb(r), more, kb(2), vb(2), ksb(2), vsb(2), last, j + 2);
+        if (!last) {
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+            barrier_only();
+        }
     }
     // no fill may still be writing LDS when the workgroup ends
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));

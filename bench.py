@@ -180,11 +180,13 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
         rows_fn(rows, nthreads=threads)
         return time.perf_counter() - t0
 
-    # fixed cost (the keys' prologue) + per-row cost, from two probes
+    # fixed cost (the keys' prologue, and for the FP4 emulation their
+    # quantisation) + per-row cost, from two probes far enough apart that the
+    # per-row part stands out of the fixed part
     probe = 2 * threads
     t1 = run(probe)
-    t2 = run(2 * probe)
-    per_row = max((t2 - t1) / probe, 1e-6)
+    t2 = run(5 * probe)
+    per_row = max((t2 - t1) / (4 * probe), 1e-6)
     fixed = max(t1 - per_row * probe, 0.0)
     nrows = int(max(probe, min(n, (seconds - fixed) / per_row)))
     t = run(nrows)
