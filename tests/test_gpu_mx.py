@@ -184,3 +184,71 @@ def test_mx_repeat_calls_bit_identical(torch_dev):
     a = G.bits(G.run(w, t, quantized="mx", label="mx determinism-1"))
     b = G.bits(G.run(w, t, quantized="mx", label="mx determinism-2"))
     np.testing.assert_array_equal(a, b)
+
+
+def _emulation_all_rows(w, inp, out_bits, label, scale=None):
+    p = oracle.Problem.from_workload(w, inp, scale=scale)
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    ref = p.mx_attention_rows(rows, nthreads=G.oracle_threads())
+    m = _emulation_metrics(G.gpu_rows(out_bits, rows, w.H), ref)
+    G.check(m, G.MX_EMULATION_GATE, label + " vs emulation")
+
+
+def test_mx_largest_batch_of_sequences(torch_dev):
+    """64 sequences with ragged lengths (empty, 1, 63, 64, 65, 255, 256, 257 tokens,
+    audio-only ones, short last V blocks), every row against the emulation."""
+    from tests.test_gpu_edges import _max_batch
+    w = _max_batch().replace(name="max_batch_64_mx", fp4=True)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized="mx", label=w.name))
+    _emulation_all_rows(w, inp, out, w.name)
+
+
+def test_mx_single_token_sequences(torch_dev):
+    """One key per sequence: its p is exactly 1 (scale 2^-2, code 4.0), so each
+    output row is that token's v rounded to MXFP4 on its own (a one-token V
+    block), then to bf16."""
+    w = synth.Workload("single_tokens_mx", H=3, d=128, seqs=tuple(Seq(1, 1, 1) for _ in range(17)),
+                       split=(32, 48, 48), seed=35, fp4=True)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized="mx", label=w.name))
+    p = oracle.Problem.from_workload(w, inp)
+    got = G.decode(out)
+    for s in range(w.S):
+        for hd in range(w.H):
+            codes, exps = p.mx_v_quant(s, hd)
+            want = np.array([oracle.e2m1_decode(int(c)) for c in codes[0]]) * np.ldexp(1.0, exps[0])
+            np.testing.assert_allclose(got[s, hd], want, rtol=2.0 ** -8, atol=0)
+    _emulation_all_rows(w, inp, out, w.name)
+
+
+def test_mx_strided_views_scale_and_eps(torch_dev):
+    """q, k, v as strided views of one fused [N, 3, H, d] buffer, a non-default
+    softmax scale and RMSNorm epsilon: every row against the emulation."""
+    torch = torch_dev
+    w = synth.Workload("strided_mx", H=2, d=128, seqs=(Seq(3, 9, 10, 30), Seq(2, 5, 7)), split=(32, 48, 48),
+                       eps=1e-3, seed=36, fp4=True)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    fused = torch.empty((w.N, 3, w.H, w.d), dtype=torch.bfloat16, device="cuda:0")
+    fused[:, 0], fused[:, 1], fused[:, 2] = t["q"], t["k"], t["v"]
+    q, k, v = fused[:, 0], fused[:, 1], fused[:, 2]
+    assert q.stride(0) == 3 * w.H * w.d
+    scale = 0.05
+    G.announce("strided_mx workload=%s N=%d scale=%g eps=%g" % (w.name, w.N, scale, w.eps))
+    o = h.h3attn_fwd_mx(q, k, v, t["norm_w"], t["rope"], t["cu"], eps=w.eps, softmax_scale=scale)
+    torch.cuda.synchronize()
+    _emulation_all_rows(w, inp, G.bits(o), w.name, scale=scale)
+
+
+def test_mx_empty_input_is_a_no_op(torch_dev):
+    torch = torch_dev
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda:0")
+    nw = torch.ones((2, 2, 128), dtype=torch.float32, device="cuda:0")
+    rope = torch.empty((0, 64, 2), dtype=torch.float32, device="cuda:0")
+    G.announce("mx empty input")
+    o = h.h3attn_fwd_mx(z, z, z, nw, rope, np.array([0, 0], np.int32))
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 128)
