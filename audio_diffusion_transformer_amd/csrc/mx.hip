@@ -349,6 +349,11 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(MxAttnArgs a)
     const i32x8 ones = {one4, one4, one4, one4, 0, 0, 0, 0};
     float m_run = 0.f;              // running max of the scores (log2 units)
     bool first = true;
+    // Every score chain starts from the splat -m_run, so the MFMAs give s - m_run
+    // and p = 2^(s - m_run) needs no subtraction.  Rebuilt only when m_run moves;
+    // the empty asm keeps the 16 registers live instead of re-materialised.
+    f32x16 ninit = {};
+    asm volatile("" : "+v"(ninit));
 
     auto wide = [](i32x4 x) -> i32x8 { return (i32x8){x[0], x[1], x[2], x[3], 0, 0, 0, 0}; };
     // A fragment of the score MFMA for key block kb, channel step st
@@ -372,9 +377,8 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(MxAttnArgs a)
         const uint32_t vsw = vsl[2 * m + hh];
         if (more) fill(jfill, kn, vn, ksn, vsn);
 
-        f32x16 s0 = {}, s1 = {};
-        s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k00), wide(qf0), s0, 4, 4, 0, ksw, 0, qsc);
-        s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k10), wide(qf0), s1, 4, 4, 2, ksw, 0, qsc);
+        f32x16 s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k00), wide(qf0), ninit, 4, 4, 0, ksw, 0, qsc);
+        f32x16 s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k10), wide(qf0), ninit, 4, 4, 2, ksw, 0, qsc);
         s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k01), wide(qf1), s0, 4, 4, 1, ksw, 2, qsc);
         s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k11), wide(qf1), s1, 4, 4, 3, ksw, 2, qsc);
         if (mask) {
@@ -385,35 +389,45 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(MxAttnArgs a)
                 if (32 * hh + 16 + r >= valid) s1[r] = -INFINITY;
             }
         }
-        const float lmax = lane_max32(s0, s1);    // the largest score of this lane's P block
-        const float rmax = row_max2(lmax);
-        const float x = rmax - m_run;
+        // s0, s1 hold s - m_run.  The lane's largest (of its P block) and the row's:
+        float lmax = lane_max32(s0, s1);
+        const float x = row_max2(lmax);
         const bool need = first || x > kMxLazy;
         // Rare after the first tiles: kept a real branch (the empty asm stops
         // the compiler from if-converting it into 65 multiplies per tile).
+        // m_run moves to the tile maximum, m_run + x: the scores lie on the
+        // grid of their codes' scales, so x and this sum are exact and the
+        // maximum's own p is 2^0 = 1 exactly, which the power-of-two block
+        // scale rule needs (it jumps at 1).
         if (__builtin_expect(__any(need), 0)) {
             asm volatile("" ::: "memory");
+            const float delta = need ? x : 0.f;
             if (!first) {
-                const float alpha = __builtin_amdgcn_exp2f(need ? -x : 0.f);
+                const float alpha = __builtin_amdgcn_exp2f(-delta);
                 ol[0] *= alpha;     // rows 1..31 of the row-sum block are zero
                 o0 *= alpha;
                 o1 *= alpha;
                 o2 *= alpha;
                 o3 *= alpha;
             }
-            m_run = need ? rmax : m_run;
+            m_run += delta;
+            s0 -= delta;
+            s1 -= delta;
+            lmax -= delta;
+            ninit = (f32x16){} - m_run;
+            asm volatile("" : "+v"(ninit));
             first = false;
         }
         float p[32];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(s0[r] - m_run);
-            p[16 + r] = __builtin_amdgcn_exp2f(s1[r] - m_run);
+            p[r] = __builtin_amdgcn_exp2f(s0[r]);
+            p[16 + r] = __builtin_amdgcn_exp2f(s1[r]);
         }
         // The block's largest p: v_exp_f32 is non-decreasing (checked on every
         // fp32 input in [-150, 2]; arguments here are <= 1, and below -150 any
         // value gives the same limited scale), so it is exp2 of the largest score.
-        const uint32_t pbyte = mx_scale_byte(__builtin_amdgcn_exp2f(lmax - m_run));
+        const uint32_t pbyte = mx_scale_byte(__builtin_amdgcn_exp2f(lmax));
         const float psc = mx_scale_value(pbyte);
         const i32x8 pf = {(int)fp4x8(p, psc), (int)fp4x8(p + 8, psc), (int)fp4x8(p + 16, psc),
                           (int)fp4x8(p + 24, psc), 0, 0, 0, 0};

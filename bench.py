@@ -182,11 +182,12 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
 
     # fixed cost (the keys' prologue, and for the FP4 emulation their
     # quantisation) + per-row cost, from two probes far enough apart that the
-    # per-row part stands out of the fixed part
+    # per-row part stands out of the fixed part, the larger one big enough to
+    # see the memory-bound rate of many rows streaming the keys at once
     probe = 2 * threads
     t1 = run(probe)
-    t2 = run(5 * probe)
-    per_row = max((t2 - t1) / (4 * probe), 1e-6)
+    t2 = run(20 * probe)
+    per_row = max((t2 - t1) / (19 * probe), 1e-6)
     fixed = max(t1 - per_row * probe, 0.0)
     nrows = int(max(probe, min(n, (seconds - fixed) / per_row)))
     t = run(nrows)
