@@ -109,6 +109,10 @@ Q8_EMULATION_GATE = dict(max_abs=4e-2, mean_abs=1e-3, rel_l2=5e-3, cosine=0.9999
 # (rel-L2 ~1) or a misplaced block fails them.
 MX_GATE = dict(mean_abs=2e-2, rel_l2=0.30, cosine=0.96)
 MX_SMALL_GATE = dict(rel_l2=0.30, cosine=0.96)
+# Sharp diagnostic inputs (a few dominant keys per row) magnify the rounding of
+# the largest probabilities: the FP4 emulation itself is at rel-L2 0.38, cosine
+# 0.927 from exact attention there; the guard sits just outside.
+MX_SHARP_GATE = dict(rel_l2=0.45, cosine=0.90)
 # FP4 path against the oracle's step-by-step emulation of it (same codes,
 # scales, tiles, lazy maximum and FP4 probabilities): what is left is the bf16
 # output rounding (unit roundoff 2^-8, rel-L2 ~ 2^-8 / sqrt(3) ~ 0.0017 on
