@@ -284,13 +284,17 @@ __global__ __launch_bounds__(256) void mx_export_kernel(MxExportArgs a)
 }
 
 // --------------------------------------------------------------- attention
-// One workgroup = 4 waves x 32 query rows of one (sequence, head).  The FP4
-// K tile (64 rows x 64 bytes), the FP4 V^T tile (128 channel rows x 32 bytes)
-// and their 256 scale bytes each are filled straight into a ring of three LDS
-// buffers by buffer_load ... lds, two tiles ahead: each step reads its tile's
-// fragments, then issues the fill of the tile after next, and at its end waits
-// only for the next tile's fill (three loads per wave stay in flight).
-__global__ __launch_bounds__(256, 2) void attn_mx_kernel(MxAttnArgs a)
+// One workgroup = 4 waves x 32 query rows of one (sequence, head), three
+// workgroups per CU (168 VGPRs): the step's vector work (exp2, FP4 packing) and
+// matrix work alternate inside a wave, and the third wave per SIMD fills more of
+// the gaps.  The FP4 K tile (64 rows x 64 bytes), the FP4 V^T tile (128 channel
+// rows x 32 bytes) and their 256 scale bytes each are filled straight into a
+// ring of three LDS buffers by buffer_load ... lds, two tiles ahead: each step
+// reads its K fragments, computes the scores and P, then reads its V fragments
+// (late, to keep them out of the register peak), issues the fill of the tile
+// after next, and at its end waits only for the next tile's fill (three loads
+// per wave stay in flight).
+__global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lk0[kTileBytes], lk1[kTileBytes], lk2[kTileBytes];
     __shared__ __attribute__((aligned(16))) uint8_t lv0[kTileBytes], lv1[kTileBytes], lv2[kTileBytes];
@@ -373,9 +377,6 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(MxAttnArgs a)
                     bool more, void *kn, void *vn, uint32_t *ksn, uint32_t *vsn, bool mask, int jfill) {
         const i32x4 k00 = kfrag(kl, 0, 0), k10 = kfrag(kl, 1, 0), k01 = kfrag(kl, 0, 1), k11 = kfrag(kl, 1, 1);
         const uint32_t ksw = ksl[2 * m + hh];
-        const i32x4 v0 = vfrag(vl, 0), v1 = vfrag(vl, 1), v2 = vfrag(vl, 2), v3 = vfrag(vl, 3);
-        const uint32_t vsw = vsl[2 * m + hh];
-        if (more) fill(jfill, kn, vn, ksn, vsn);
 
         f32x16 s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k00), wide(qf0), ninit, 4, 4, 0, ksw, 0, qsc);
         f32x16 s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k10), wide(qf0), ninit, 4, 4, 2, ksw, 0, qsc);
@@ -431,6 +432,9 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(MxAttnArgs a)
         const float psc = mx_scale_value(pbyte);
         const i32x8 pf = {(int)fp4x8(p, psc), (int)fp4x8(p + 8, psc), (int)fp4x8(p + 16, psc),
                           (int)fp4x8(p + 24, psc), 0, 0, 0, 0};
+        const uint32_t vsw = vsl[2 * m + hh];
+        const i32x4 v0 = vfrag(vl, 0), v1 = vfrag(vl, 1), v2 = vfrag(vl, 2), v3 = vfrag(vl, 3);
+        if (more) fill(jfill, kn, vn, ksn, vsn);
         o0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(v0), pf, o0, 4, 4, 0, vsw, 0, pbyte);
         o1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(v1), pf, o1, 4, 4, 1, vsw, 0, pbyte);
         o2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(v2), pf, o2, 4, 4, 2, vsw, 0, pbyte);
