@@ -455,7 +455,6 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
         __builtin_amdgcn_sched_barrier(0);
     };
     using one_pending = std::integral_constant<int, 1>;
-    using none_pending = std::integral_constant<int, 0>;
     fill(0, lk0, lv0, lks0, lvs0);
     fill(min(1, nt - 1), lk1, lv1, lks1, lvs1);
     wait_next(one_pending());
