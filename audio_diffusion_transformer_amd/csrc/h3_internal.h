@@ -77,7 +77,7 @@ struct AttnArgs {
     int32_t seq_n[kMaxSeqs];
     int32_t seq_cu[kMaxSeqs];
     int32_t seq_off[kMaxSeqs];
-    int32_t seq_nqb[kMaxSeqs];
+    int32_t seq_nqb[kMaxSeqs];        // query blocks of the kernel's block size
     int32_t item_pre[kMaxSeqs + 1];   // prefix sums of H * nqb
     // block-sparse attention (null tiles: dense): tiles is int32
     // [items][tpb] in the caller's item order (sequence, head, 128-row query
@@ -271,5 +271,12 @@ hipError_t launch_mx_export(const MxExportArgs &a, hipStream_t st);
 
 // Queries per workgroup of the attention kernels (work-item granularity).
 constexpr int kBlockM = 128;
+// Queries per workgroup of the dense bf16 kernel at head_dim 128 (two groups
+// of four waves, 32 rows each); every sequence is padded to kSeqPad rows, a
+// multiple of it, so its query blocks stay inside the sequence's rows.
+constexpr int kBlockM2 = 256;
+static_assert(kSeqPad % kBlockM2 == 0, "query blocks stay within a padded sequence");
+// Rows per work item launch_attn_bf16 expects for (head_dim, block-sparse).
+inline int attn_bf16_block_m(int d, bool sparse) { return d == 128 && !sparse ? kBlockM2 : kBlockM; }
 
 }  // namespace h3

@@ -190,9 +190,10 @@ float scale_log2(const h3attn_params *p)
     return (float)(s * 1.4426950408889634);
 }
 
-// Sequences with work, longest first (stable), and the work-item prefix.
+// Sequences with work, longest first (stable), and the work-item prefix for
+// query blocks of block_m rows.
 template <class Args>
-int64_t order_work(const Plan &pl, Args &a, int32_t *seq_idx)
+int64_t order_work(const Plan &pl, Args &a, int32_t *seq_idx, int block_m = kBlockM)
 {
     int order[kMaxSeqs];
     std::iota(order, order + pl.S, 0);
@@ -209,7 +210,7 @@ int64_t order_work(const Plan &pl, Args &a, int32_t *seq_idx)
         a.seq_n[k] = n;
         a.seq_cu[k] = pl.cu[s];
         a.seq_off[k] = pl.off[s];
-        a.seq_nqb[k] = (n + kBlockM - 1) / kBlockM;
+        a.seq_nqb[k] = (n + block_m - 1) / block_m;
         if (seq_idx) seq_idx[k] = s;
         items += (int64_t)pl.H * a.seq_nqb[k];
         a.item_pre[k + 1] = (int32_t)items;
@@ -306,7 +307,7 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     aa.o_stride = p->o_stride;
     aa.Npad = pl.Npad;
     aa.H = pl.H;
-    const int64_t items = order_work(pl, aa, nullptr);
+    const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d, false));
     return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "attention launch");
 }
 
@@ -427,7 +428,7 @@ h3attn_status h3attn_fwd_proj_stages(const h3attn_params *p, int32_t model_dim, 
     aa.o_stride = p->o_stride;
     aa.Npad = pl.Npad;
     aa.H = pl.H;
-    const int64_t items = order_work(pl, aa, nullptr);
+    const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d, false));
     return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "attention launch");
 }
 
@@ -628,7 +629,7 @@ h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, co
     aa.Npad = pl.Npad;
     aa.H = pl.H;
     int32_t seq_idx[kMaxSeqs];
-    const int64_t items = order_work(pl, aa, seq_idx);
+    const int64_t items = order_work(pl, aa, seq_idx, attn_bf16_block_m(pl.d, true));
     aa.tiles = block_tiles;
     aa.tpb = tiles_per_block;
     for (int i = 0; i < aa.nseq; ++i) aa.seq_item_base[i] = base[seq_idx[i]];

@@ -501,7 +501,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": {"mx": "attn_mx_kernel", "q8": "attn_q8_kernel",
-                                "bf16": "attn_bf16_kernel<128>"}[kname],
+                                "bf16": "attn_bf16_pp_kernel<128>"}[kname],
                      "avg_ms": round(att_avg, 4)},
         "step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 4),
                     "p50": round(float(np.percentile(step_ms, 50)), 4),

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 Seq = synth.Seq
 
 # Small cases: several key tiles, ragged tails, empty and audio-only sequences,
-# exact tile multiples, d = 64 and d = 128.
+# exact tile multiples, every tile count up to 13, d = 64 and d = 128.
 SMALL = {
     "tiny": synth.WORKLOADS["tiny"],
     "ragged_tail_337": synth.Workload("ragged_tail_337", H=3, d=128, seqs=(Seq(3, 10, 11, 7),),
@@ -34,6 +34,12 @@ SMALL = {
                                     split=(16, 24, 24), seed=14),
     "sharp_700": synth.Workload("sharp_700", H=4, d=128, seqs=(Seq(4, 10, 15, 100),),
                                 split=(32, 48, 48), seed=15, sharp=True),
+    # 1 .. 13 key tiles (every exit of the six-tile loop of the dense kernel,
+    # whole and ragged 256-row query blocks)
+    "tile_counts_1_to_13": synth.Workload(
+        "tile_counts_1_to_13", H=2, d=128,
+        seqs=tuple(Seq(1, 1, n) for n in (1, 65, 130, 250, 257, 384, 385, 449, 530, 600, 700, 768, 777)),
+        split=(32, 48, 48), k_offset_std=0.5, seed=16),
 }
 
 
