@@ -406,9 +406,12 @@ template __global__ void attn_bf16_kernel<128, true>(AttnArgs);
 //                  beside the first half, which reads keys 0..31 only.
 // Group 1 waits one barrier before its first phase and group 0 one after its
 // last, so on every SIMD one wave runs its softmax phase while the other runs
-// its P.V phase.  Both phases carry 16 MFMAs and 16 exp2, and the vector work
-// of each wave runs beside the matrix work of the other; the barrier keeps the
-// two waves half a tile apart, which free-running waves do not stay.
+// its P.V phase.  Both phases carry 16 MFMAs and 16 exp2.  The mid-tile
+// barrier is what keeps the two waves half a tile apart: with one barrier per
+// tile they drift back into step and the kernel is slower.  Against two 4-wave
+// workgroups per CU, one 256-row workgroup reads each K/V tile from L2 once
+// instead of twice; measured, that takes the same cycles per launch at a
+// higher engine clock on this power-limited part.
 //
 // K and V^T tiles rotate through three LDS buffers per operand (96 KB, one
 // workgroup per CU).  In its softmax phase of tile j a wave issues its quarter
