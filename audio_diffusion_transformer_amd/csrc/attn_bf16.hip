@@ -2,8 +2,8 @@
 //
 // This is the attention share of a MiniMax-H3 block (about 58% of block time
 // on the page "Buyer Questions: Current Evidence Status", question 4), and the
-// "H3-specific attention backend" the page "H3 Runtime Current State" lists
-// under "Owned Performance Kernels".  It consumes the prologue's head-major
+// attention backend tuned to H3's own shapes that the page "H3 Runtime Current
+// State" counts as owed ("Owned Performance Kernels").  It consumes the prologue's head-major
 // qhat / khat and per-tile transposed V, and computes, for each query row,
 // the softmax over the keys of its own sequence tile by tile (an online
 // softmax), never materialising the N x N score matrix.

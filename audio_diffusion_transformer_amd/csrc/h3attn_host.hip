@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 #include <string>
@@ -69,6 +70,15 @@ h3attn_status make_plan(const h3attn_params *p, const int32_t *cu, Plan *pl)
     for (int s = 0; s < p->num_seqs; ++s)
         if (cu[s + 1] < cu[s])
             return fail(H3ATTN_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", s, cu[s], cu[s + 1]);
+    // The attention kernels address one (sequence, head) slice of the K and V
+    // copies through a buffer descriptor whose size and offsets are 32-bit
+    // signed values: its bf16 slice (whole 64-token tiles) must stay below 2 GiB.
+    const int64_t max_seq = (((int64_t)1 << 31) / (2 * (int64_t)p->head_dim)) / kTile * kTile - kTile;
+    for (int s = 0; s < p->num_seqs; ++s)
+        if ((int64_t)cu[s + 1] - cu[s] > max_seq)
+            return fail(H3ATTN_ERR_UNSUPPORTED, "sequence %d has %lld tokens; at head_dim %d at most %lld fit the "
+                        "kernels' 2 GiB per-(sequence, head) K/V buffer range", s,
+                        (long long)cu[s + 1] - cu[s], p->head_dim, (long long)max_seq);
     std::memset(pl, 0, sizeof *pl);
     pl->S = p->num_seqs;
     pl->H = p->num_heads;
@@ -122,8 +132,11 @@ h3attn_status make_plan(const h3attn_params *p, const int32_t *cu, Plan *pl)
     return H3ATTN_OK;
 }
 
+bool fault_injected();
+
 h3attn_status check_device()
 {
+    if (fault_injected()) return H3ATTN_OK;   // nothing will be launched
     static std::atomic<int> checked[64];
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
@@ -221,9 +234,35 @@ int64_t order_work(const Plan &pl, Args &a, int32_t *seq_idx, int block_m = kBlo
     return items;
 }
 
-h3attn_status hip_status(hipError_t e, const char *what)
+bool env_is(const char *name, const char *value)
 {
+    const char *e = std::getenv(name);
+    return e && std::strcmp(e, value) == 0;
+}
+
+// Host-side fault injection for tests of the error path: with the environment
+// variable H3ATTN_FAULT=launch, a call that passes every argument check makes no
+// HIP call at all (no device check, no launch) and reports its first launch as
+// failed.  Read on every call, so a test can switch it in-process.
+bool fault_injected() { return env_is("H3ATTN_FAULT", "launch"); }
+
+// Issues one launch (or device copy) and turns its hipError_t into a status.
+// With H3ATTN_DEBUG=1 it then waits for the stream and reports an execution
+// error as well, naming the launch (this synchronises, so it is not for graph
+// capture or timing).
+template <class Launch>
+h3attn_status launch_status(hipStream_t stream, const char *what, Launch &&launch)
+{
+    if (fault_injected())
+        return fail(H3ATTN_ERR_HIP, "%s: injected failure (H3ATTN_FAULT=launch), nothing was launched", what);
+    hipError_t e = launch();
     if (e != hipSuccess) return fail(H3ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    if (env_is("H3ATTN_DEBUG", "1")) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return fail(H3ATTN_ERR_HIP, "%s (checked by H3ATTN_DEBUG=1 after the stream drained): %s", what,
+                        hipGetErrorString(e));
+    }
     return ok();
 }
 
@@ -294,7 +333,8 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     pa.natural = 0;
     pa.q_mult = scale_log2(p);
     if (stages & 1)
-        if ((st = hip_status(launch_prologue(pa, pl.d, hs), "prologue launch")) != H3ATTN_OK) return st;
+        if ((st = launch_status(hs, "prologue launch",
+                [&] { return launch_prologue(pa, pl.d, hs); })) != H3ATTN_OK) return st;
     if (!(stages & 2)) return ok();
 
     AttnArgs aa;
@@ -308,7 +348,7 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     aa.Npad = pl.Npad;
     aa.H = pl.H;
     const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d, false));
-    return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "attention launch");
+    return launch_status(hs, "attention launch", [&] { return launch_attn_bf16(aa, pl.d, items, hs); });
 }
 
 h3attn_status h3attn_fwd(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -339,7 +379,8 @@ h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void 
     pa.out_hstride = pl.d;
     pa.out_tstride = (int64_t)pl.H * pl.d;
     pa.natural = 1;
-    return hip_status(launch_prologue(pa, pl.d, static_cast<hipStream_t>(stream)), "prologue launch");
+    return launch_status(static_cast<hipStream_t>(stream), "prologue launch",
+            [&] { return launch_prologue(pa, pl.d, static_cast<hipStream_t>(stream)); });
 }
 
 // Checks of the projection entry points' own arguments; fills the plan.  The
@@ -415,7 +456,8 @@ h3attn_status h3attn_fwd_proj_stages(const h3attn_params *p, int32_t model_dim, 
     pa.natural = 0;
     pa.q_mult = scale_log2(p);
     if (stages & 1)
-        if ((st = hip_status(launch_qkv_proj(pa, pl.d, hs), "projection launch")) != H3ATTN_OK) return st;
+        if ((st = launch_status(hs, "projection launch",
+                [&] { return launch_qkv_proj(pa, pl.d, hs); })) != H3ATTN_OK) return st;
     if (!(stages & 2)) return ok();
 
     AttnArgs aa;
@@ -429,7 +471,7 @@ h3attn_status h3attn_fwd_proj_stages(const h3attn_params *p, int32_t model_dim, 
     aa.Npad = pl.Npad;
     aa.H = pl.H;
     const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d, false));
-    return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "attention launch");
+    return launch_status(hs, "attention launch", [&] { return launch_attn_bf16(aa, pl.d, items, hs); });
 }
 
 h3attn_status h3attn_fwd_proj(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
@@ -461,7 +503,8 @@ h3attn_status h3attn_proj_prologue(const h3attn_params *p, int32_t model_dim, co
     pa.out_hstride = pl.d;
     pa.out_tstride = (int64_t)pl.H * pl.d;
     pa.natural = 1;
-    return hip_status(launch_qkv_proj(pa, pl.d, static_cast<hipStream_t>(stream)), "projection launch");
+    return launch_status(static_cast<hipStream_t>(stream), "projection launch",
+            [&] { return launch_qkv_proj(pa, pl.d, static_cast<hipStream_t>(stream)); });
 }
 
 h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model_dim, int32_t num_seqs,
@@ -533,7 +576,8 @@ h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model
     a.nblk = (int32_t)((N + 255) / 256);
     a.S = num_seqs;
     for (int s = 0; s <= num_seqs; ++s) a.cu[s] = cu[s];
-    return hip_status(launch_out_proj(a, static_cast<hipStream_t>(stream)), "output projection launch");
+    return launch_status(static_cast<hipStream_t>(stream), "output projection launch",
+            [&] { return launch_out_proj(a, static_cast<hipStream_t>(stream)); });
 }
 
 // Caller-order item bases of the block-sparse lists: items run sequence by
@@ -590,7 +634,8 @@ h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, co
     pa.natural = 0;
     pa.q_mult = scale_log2(p);
     if (stages & 1)
-        if ((st = hip_status(launch_prologue(pa, pl.d, hs), "prologue launch")) != H3ATTN_OK) return st;
+        if ((st = launch_status(hs, "prologue launch",
+                [&] { return launch_prologue(pa, pl.d, hs); })) != H3ATTN_OK) return st;
 
     if (stages & 2) {
         SparseSelectArgs sa;
@@ -613,7 +658,8 @@ h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, co
             g += (int64_t)pl.H * (((pl.cu[s + 1] - pl.cu[s] + 127) / 128 + 3) / 4);
         }
         sa.group_pre[pl.S] = (int32_t)g;
-        if ((st = hip_status(launch_sparse_select(sa, pl.d, hs), "sparse selection launch")) != H3ATTN_OK)
+        if ((st = launch_status(hs, "sparse selection launch",
+                [&] { return launch_sparse_select(sa, pl.d, hs); })) != H3ATTN_OK)
             return st;
     }
     if (!(stages & 4)) return ok();
@@ -633,7 +679,7 @@ h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, co
     aa.tiles = block_tiles;
     aa.tpb = tiles_per_block;
     for (int i = 0; i < aa.nseq; ++i) aa.seq_item_base[i] = base[seq_idx[i]];
-    return hip_status(launch_attn_bf16(aa, pl.d, items, hs), "sparse attention launch");
+    return launch_status(hs, "sparse attention launch", [&] { return launch_attn_bf16(aa, pl.d, items, hs); });
 }
 
 h3attn_status h3attn_fwd_sparse(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -698,7 +744,8 @@ h3attn_status h3attn_fwd_q8_stages(const h3attn_params *p, const void *q, const 
     if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (stages & 1)
-        if ((st = hip_status(launch_q8_prep(qa, pl.d, hs), "quantised prologue launch")) != H3ATTN_OK) return st;
+        if ((st = launch_status(hs, "quantised prologue launch",
+                [&] { return launch_q8_prep(qa, pl.d, hs); })) != H3ATTN_OK) return st;
     if (!(stages & 2)) return ok();
     Q8AttnArgs aa;
     std::memset(&aa, 0, sizeof aa);
@@ -714,7 +761,7 @@ h3attn_status h3attn_fwd_q8_stages(const h3attn_params *p, const void *q, const 
     aa.H = pl.H;
     aa.scale_log2 = scale_log2(p);
     const int64_t items = order_work(pl, aa, aa.seq_idx);
-    return hip_status(launch_attn_q8(aa, pl.d, items, hs), "quantised attention launch");
+    return launch_status(hs, "quantised attention launch", [&] { return launch_attn_q8(aa, pl.d, items, hs); });
 }
 
 h3attn_status h3attn_fwd_q8(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -741,7 +788,8 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
     for (int i = 0; i < 6; ++i)
         if (!outs[i]) return fail(H3ATTN_ERR_INVALID_ARG, "%s is NULL", names[i]);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if ((st = hip_status(launch_q8_prep(qa, pl.d, hs), "quantised prologue launch")) != H3ATTN_OK) return st;
+    if ((st = launch_status(hs, "quantised prologue launch",
+            [&] { return launch_q8_prep(qa, pl.d, hs); })) != H3ATTN_OK) return st;
     Q8ExportArgs ea;
     std::memset(&ea, 0, sizeof ea);
     ea.q8 = qa.q8;
@@ -760,11 +808,14 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
     ea.ntiles = qa.ntiles;
     for (int s = 0; s < pl.S; ++s) ea.nblocks += (pl.cu[s + 1] - pl.cu[s] + kTile - 1) / kTile;
     ea.seq = qa.seq;
-    if ((st = hip_status(launch_q8_export(ea, hs), "quantised export launch")) != H3ATTN_OK) return st;
+    if ((st = launch_status(hs, "quantised export launch",
+            [&] { return launch_q8_export(ea, hs); })) != H3ATTN_OK) return st;
     const size_t sb = (size_t)pl.S * pl.H * pl.d * sizeof(float);
-    if ((st = hip_status(hipMemcpyAsync(k_mean, qa.kmean, sb, hipMemcpyDeviceToDevice, hs), "k_mean copy")) != H3ATTN_OK)
+    if ((st = launch_status(hs, "k_mean copy",
+            [&] { return hipMemcpyAsync(k_mean, qa.kmean, sb, hipMemcpyDeviceToDevice, hs); })) != H3ATTN_OK)
         return st;
-    return hip_status(hipMemcpyAsync(v_scale, qa.vscale, sb, hipMemcpyDeviceToDevice, hs), "v_scale copy");
+    return launch_status(hs, "v_scale copy",
+            [&] { return hipMemcpyAsync(v_scale, qa.vscale, sb, hipMemcpyDeviceToDevice, hs); });
 }
 
 static h3attn_status mx_common(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -820,7 +871,8 @@ h3attn_status h3attn_fwd_mx_stages(const h3attn_params *p, const void *q, const 
     if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (stages & 1)
-        if ((st = hip_status(launch_mx_prep(ma, pl.d, hs), "FP4 prologue launch")) != H3ATTN_OK) return st;
+        if ((st = launch_status(hs, "FP4 prologue launch",
+                [&] { return launch_mx_prep(ma, pl.d, hs); })) != H3ATTN_OK) return st;
     if (!(stages & 2)) return ok();
     MxAttnArgs aa;
     std::memset(&aa, 0, sizeof aa);
@@ -835,7 +887,7 @@ h3attn_status h3attn_fwd_mx_stages(const h3attn_params *p, const void *q, const 
     aa.Npad = pl.Npad;
     aa.H = pl.H;
     const int64_t items = order_work(pl, aa, nullptr);
-    return hip_status(launch_attn_mx(aa, pl.d, items, hs), "FP4 attention launch");
+    return launch_status(hs, "FP4 attention launch", [&] { return launch_attn_mx(aa, pl.d, items, hs); });
 }
 
 h3attn_status h3attn_fwd_mx(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -863,7 +915,8 @@ h3attn_status h3attn_mx_prologue(const h3attn_params *p, const void *q, const vo
     st = mx_common(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, q_codes, workspace, workspace_bytes, pl, ma);
     if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if ((st = hip_status(launch_mx_prep(ma, pl.d, hs), "FP4 prologue launch")) != H3ATTN_OK) return st;
+    if ((st = launch_status(hs, "FP4 prologue launch",
+            [&] { return launch_mx_prep(ma, pl.d, hs); })) != H3ATTN_OK) return st;
     MxExportArgs ea;
     std::memset(&ea, 0, sizeof ea);
     ea.qx = ma.qx;
@@ -883,9 +936,11 @@ h3attn_status h3attn_mx_prologue(const h3attn_params *p, const void *q, const vo
     ea.ntiles = ma.ntiles;
     ea.seq = ma.seq;
     for (int s = 0; s < pl.S; ++s) ea.vblk_pre[s + 1] = ea.vblk_pre[s] + (pl.cu[s + 1] - pl.cu[s] + 31) / 32;
-    if ((st = hip_status(launch_mx_export(ea, hs), "FP4 export launch")) != H3ATTN_OK) return st;
+    if ((st = launch_status(hs, "FP4 export launch",
+            [&] { return launch_mx_export(ea, hs); })) != H3ATTN_OK) return st;
     const size_t sb = (size_t)pl.S * pl.H * pl.d * sizeof(float);
-    return hip_status(hipMemcpyAsync(k_mean, ma.kmean, sb, hipMemcpyDeviceToDevice, hs), "k_mean copy");
+    return launch_status(hs, "k_mean copy",
+            [&] { return hipMemcpyAsync(k_mean, ma.kmean, sb, hipMemcpyDeviceToDevice, hs); });
 }
 
 h3attn_status h3attn_rope_fill_video(int32_t T, int32_t Hg, int32_t Wg, int32_t dt, int32_t dh, int32_t dw,

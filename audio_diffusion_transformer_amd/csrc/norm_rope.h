@@ -3,9 +3,10 @@
 //
 // A row of d channels is spread over d/8 consecutive lanes, 8 channels
 // (16 bytes of bf16) per lane; the sum of squares is a butterfly over those
-// lanes, and each RoPE pair (2j, 2j+1) lives inside one lane.  The RMSNorm and
-// rotation follow the "Fused Q/K RMSNorm, RoPE, and layout work" named under
-// "Owned Performance Kernels" on the page "H3 Runtime Current State":
+// lanes, and each RoPE pair (2j, 2j+1) lives inside one lane.  These are the
+// norm and rotation of the fused norm/RoPE/relayout kernel that the page "H3
+// Runtime Current State" counts among the owed kernels ("Owned Performance
+// Kernels"):
 //   y_c = x_c / sqrt(mean_c x_c^2 + eps) * w_c, then pair (y_2j, y_2j+1) turned
 //   by the token's angle for pair j (cos, sin taken from the RoPE table).
 #pragma once

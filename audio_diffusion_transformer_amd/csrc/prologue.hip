@@ -1,7 +1,7 @@
 // Fused Q/K RMSNorm + RoPE + layout prologue for gfx950.
 //
-// The page "H3 Runtime Current State" lists "Fused Q/K RMSNorm, RoPE, and
-// layout work" under "Owned Performance Kernels"; "Buyer Questions: Current
+// The page "H3 Runtime Current State" counts a fused Q/K norm, RoPE and
+// relayout kernel among the owed ones ("Owned Performance Kernels"); "Buyer Questions: Current
 // Evidence Status" (question 4) measures norm/RoPE as about 4% of a block and
 // the strided-NHD QKV copy as about 3.6%.  This kernel does all of it in one
 // HBM pass: it reads q, k and v once through their token strides, normalises

@@ -2,9 +2,9 @@
 //
 // The GEMMs are the second-largest share of a MiniMax-H3 block after
 // attention (about 27% on the page "Buyer Questions: Current Evidence
-// Status", question 4), and the page "H3 Runtime Current State" lists the
-// attention QKV projection among its tensor-parallel GEMMs and "Fused Q/K
-// RMSNorm, RoPE, and layout work" among its owned kernels.  This kernel is
+// Status", question 4), and the page "H3 Runtime Current State" counts the
+// attention QKV projection among its tensor-parallel GEMMs and a fused
+// norm/RoPE/relayout kernel among the owed ones.  This kernel is
 // the projection with that prologue in its epilogue: y = x . W^T on the
 // matrix cores, then, still in registers, RMSNorm over each head's d
 // features, the norm weight, the RoPE rotation and the head-major store that

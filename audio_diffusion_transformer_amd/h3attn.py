@@ -14,7 +14,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libh3attn.so")
+# H3ATTN_LIB points the binding at another build of the same sources (the
+# tests use it for a build with host-side sanitizers).
+LIB_PATH = os.environ.get("H3ATTN_LIB") or os.path.join(_HERE, "libh3attn.so")
 
 H3ATTN_OK = 0
 H3ATTN_ERR_INVALID_ARG = 1
@@ -187,6 +189,18 @@ def _stream_ptr(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _empty(stream, shape, dtype, device):
+    """torch.empty on the launch stream: memory allocated while a stream is
+    current belongs to that stream in torch's caching allocator, so a buffer
+    the kernels on ``stream`` use is not handed to other streams' work before
+    those kernels are done with it."""
+    import torch
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def params_for(q, k, v, out, num_seqs: int, eps: float = 1e-6, softmax_scale: float = 0.0):
     """Params from [N, H, d] bf16 tensors (any token stride, unit channel stride)."""
     N, H, d = q.shape
@@ -215,12 +229,11 @@ def h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=Non
     device; cu_seqlens: int32 [S+1] (host array or CPU tensor)."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(stream, q.shape, q.dtype, q.device)
     cu = _cu_array(cu_seqlens)
     params = params_for(q, k, v, out, len(cu) - 1, eps, softmax_scale)
     if workspace is None:
-        workspace = torch.empty(h3attn_workspace_size(params, cu, quantized), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _empty(stream, (h3attn_workspace_size(params, cu, quantized),), torch.uint8, q.device)
     _check(fwd_raw(params, _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w),
                    _dev_ptr(rope_tables), cu, _dev_ptr(out), _dev_ptr(workspace),
                    workspace.numel() * workspace.element_size(), _stream_ptr(stream), quantized,
@@ -243,8 +256,8 @@ def h3attn_fwd_mx(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=
 def h3attn_prologue(q, k, norm_w, rope_tables, cu_seqlens, q_hat=None, k_hat=None,
                     eps: float = 1e-6, stream=None):
     import torch
-    q_hat = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if q_hat is None else q_hat
-    k_hat = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if k_hat is None else k_hat
+    q_hat = _empty(stream, q.shape, torch.bfloat16, q.device) if q_hat is None else q_hat
+    k_hat = _empty(stream, q.shape, torch.bfloat16, q.device) if k_hat is None else k_hat
     cu = _cu_array(cu_seqlens)
     params = params_for(q, k, q, q_hat, len(cu) - 1, eps)
     _check(lib().h3attn_prologue(C.byref(params), _dev_ptr(q), _dev_ptr(k), _dev_ptr(norm_w),
@@ -283,11 +296,11 @@ def h3attn_fwd_proj(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: int, h
     import torch
     N, D = x.shape
     if out is None:
-        out = torch.empty((N, num_heads, head_dim), dtype=torch.bfloat16, device=x.device)
+        out = _empty(stream, (N, num_heads, head_dim), torch.bfloat16, x.device)
     cu = _cu_array(cu_seqlens)
     params = _proj_params(x, w_qkv, num_heads, head_dim, len(cu) - 1, out.stride(0), eps, softmax_scale)
     if workspace is None:
-        workspace = torch.empty(h3attn_workspace_size(params, cu), dtype=torch.uint8, device=x.device)
+        workspace = _empty(stream, (h3attn_workspace_size(params, cu),), torch.uint8, x.device)
     _check(proj_raw(params, D, _dev_ptr(x), x.stride(0), _dev_ptr(w_qkv), _dev_ptr(norm_w),
                     _dev_ptr(rope_tables), cu, _dev_ptr(out), _dev_ptr(workspace),
                     workspace.numel() * workspace.element_size(), _stream_ptr(stream), stages))
@@ -300,7 +313,7 @@ def h3attn_proj_prologue(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: i
     import torch
     N, D = x.shape
     cu = _cu_array(cu_seqlens)
-    res = [torch.empty((N, num_heads, head_dim), dtype=torch.bfloat16, device=x.device) for _ in range(3)]
+    res = [_empty(stream, (N, num_heads, head_dim), torch.bfloat16, x.device) for _ in range(3)]
     params = _proj_params(x, w_qkv, num_heads, head_dim, len(cu) - 1, num_heads * head_dim, eps, 0.0)
     _check(lib().h3attn_proj_prologue(C.byref(params), D, _dev_ptr(x), x.stride(0), _dev_ptr(w_qkv),
                                       _dev_ptr(norm_w), _dev_ptr(rope_tables), _cu_ptr(cu),
@@ -332,17 +345,16 @@ def h3attn_fwd_sparse(q, k, v, norm_w, rope_tables, cu_seqlens, tiles_per_block:
     the caller's list.  Returns (out, block_tiles)."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(stream, q.shape, q.dtype, q.device)
     cu = _cu_array(cu_seqlens)
     params = params_for(q, k, v, out, len(cu) - 1, eps, softmax_scale)
     N, H, d = q.shape
     if block_tiles is None:
         if not select:
             raise ValueError("block_tiles is needed when select is False")
-        block_tiles = torch.empty((sparse_items(cu, H), tiles_per_block), dtype=torch.int32, device=q.device)
+        block_tiles = _empty(stream, (sparse_items(cu, H), tiles_per_block), torch.int32, q.device)
     if workspace is None:
-        workspace = torch.empty(h3attn_workspace_size(params, cu, 2 if select else 0), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _empty(stream, (h3attn_workspace_size(params, cu, 2 if select else 0),), torch.uint8, q.device)
     _check(sparse_raw(params, _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w), _dev_ptr(rope_tables), cu,
                       tiles_per_block, _dev_ptr(block_tiles), _dev_ptr(out), _dev_ptr(workspace),
                       workspace.numel() * workspace.element_size(), _stream_ptr(stream), 7 if select else 5))
@@ -373,7 +385,7 @@ def h3attn_out_proj(attn, w_o, cu_seqlens, gate=None, resid=None, out=None, stre
     if not w_o.is_contiguous() or w_o.shape[1] != H * d:
         raise ValueError("w_o must be a contiguous [D, H*d] tensor")
     if out is None:
-        out = torch.empty((N, D), dtype=torch.bfloat16, device=attn.device)
+        out = _empty(stream, (N, D), torch.bfloat16, attn.device)
     for t in (out, resid):
         if t is not None and (t.dim() != 2 or t.shape[1] != D or t.stride(1) != 1):
             raise ValueError("out / resid must be [N, D] with contiguous channels")
@@ -394,17 +406,16 @@ def h3attn_q8_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,
     nblocks = int(sum((int(cu[s + 1] - cu[s]) + 63) // 64 for s in range(S)))
     params = params_for(q, k, v, q, S, eps)
     if workspace is None:
-        workspace = torch.empty(h3attn_workspace_size(params, cu, True), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _empty(stream, (h3attn_workspace_size(params, cu, True),), torch.uint8, q.device)
     dev = q.device
     res = {
-        "q8": torch.empty((N, H, d), dtype=torch.int8, device=dev),
-        "k8": torch.empty((N, H, d), dtype=torch.int8, device=dev),
-        "q_scale": torch.empty((H, nblocks), dtype=torch.float32, device=dev),
-        "k_scale": torch.empty((H, nblocks), dtype=torch.float32, device=dev),
-        "k_mean": torch.empty((S, H, d), dtype=torch.float32, device=dev),
-        "v8": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
-        "v_scale": torch.empty((S, H, d), dtype=torch.float32, device=dev),
+        "q8": _empty(stream, (N, H, d), torch.int8, dev),
+        "k8": _empty(stream, (N, H, d), torch.int8, dev),
+        "q_scale": _empty(stream, (H, nblocks), torch.float32, dev),
+        "k_scale": _empty(stream, (H, nblocks), torch.float32, dev),
+        "k_mean": _empty(stream, (S, H, d), torch.float32, dev),
+        "v8": _empty(stream, (N, H, d), torch.uint8, dev),
+        "v_scale": _empty(stream, (S, H, d), torch.float32, dev),
     }
     _check(lib().h3attn_q8_prologue(
         C.byref(params), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w),
@@ -425,17 +436,16 @@ def h3attn_mx_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,
     nvb = int(sum((int(cu[s + 1] - cu[s]) + 31) // 32 for s in range(S)))
     params = params_for(q, k, v, q, S, eps)
     if workspace is None:
-        workspace = torch.empty(h3attn_workspace_size(params, cu, "mx"), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _empty(stream, (h3attn_workspace_size(params, cu, "mx"),), torch.uint8, q.device)
     dev = q.device
     res = {
-        "q_codes": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
-        "q_exp": torch.empty((N, H, d // 32), dtype=torch.uint8, device=dev),
-        "k_codes": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
-        "k_exp": torch.empty((N, H, d // 32), dtype=torch.uint8, device=dev),
-        "k_mean": torch.empty((S, H, d), dtype=torch.float32, device=dev),
-        "v_codes": torch.empty((N, H, d), dtype=torch.uint8, device=dev),
-        "v_exp": torch.empty((nvb, H, d), dtype=torch.uint8, device=dev),
+        "q_codes": _empty(stream, (N, H, d), torch.uint8, dev),
+        "q_exp": _empty(stream, (N, H, d // 32), torch.uint8, dev),
+        "k_codes": _empty(stream, (N, H, d), torch.uint8, dev),
+        "k_exp": _empty(stream, (N, H, d // 32), torch.uint8, dev),
+        "k_mean": _empty(stream, (S, H, d), torch.float32, dev),
+        "v_codes": _empty(stream, (N, H, d), torch.uint8, dev),
+        "v_exp": _empty(stream, (nvb, H, d), torch.uint8, dev),
     }
     _check(lib().h3attn_mx_prologue(
         C.byref(params), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w),

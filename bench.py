@@ -71,6 +71,23 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def oracle_threads():
+    """Threads for the CPU oracle: every CPU this process may run on, limited
+    to the job's CPU share when OMP_NUM_THREADS states one (a one-GPU job on a
+    shared host gets a slice of its cores).  Returns (threads, host facts)."""
+    host_cpus = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = host_cpus
+    share = os.environ.get("OMP_NUM_THREADS", "").strip()
+    threads = affinity
+    if share.isdigit() and int(share) > 0:
+        threads = min(affinity, int(share))
+    return max(1, threads), {"host_cpus": host_cpus, "affinity_cpus": affinity,
+                             "job_cpu_share": int(share) if share.isdigit() else None}
+
+
 def device_copy_rate(torch, dev, mib: int = 1024, reps: int = 5) -> float:
     """GB/s (read + write bytes) of a plain device-to-device copy, the practical
     rate of mixed HBM traffic the prologue is compared with."""
@@ -537,9 +554,10 @@ def main():
         kern.update(unfused)
         res["config"]["model_dim"] = w.model_dim
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        print("[bench] timing the CPU oracle on %d threads" % threads, file=sys.stderr, flush=True)
+        threads, host = oracle_threads()
+        print("[bench] timing the CPU oracle on %d threads (%s)" % (threads, host), file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, threads)
+        res["cpu_baseline"].update(host)
     print(json.dumps(res), flush=True)
     return 0
 

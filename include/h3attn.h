@@ -4,9 +4,9 @@
  *
  * The operation is the self-attention of a joint video+audio diffusion
  * transformer block (MiniMax-H3) over its packed token sequence, with the Q/K
- * RMSNorm and RoPE that the page "H3 Runtime Current State" lists, under
- * "Owned Performance Kernels", as fused "Q/K RMSNorm, RoPE, and layout work"
- * still owed beside an H3-specific attention backend.  The page "Buyer
+ * RMSNorm and RoPE in front of it: the page "H3 Runtime Current State", section
+ * "Owned Performance Kernels", counts a fused norm/RoPE/relayout kernel and an
+ * attention backend tuned for H3's shapes among the work still owed.  The page "Buyer
  * Questions: Current Evidence Status", question 4 ("Current answer"), puts
  * attention at about 58% and norm/RoPE at about 4% of a block and credits the
  * removal of the strided-NHD QKV copy with about 3.6%: here q, k and v are
@@ -31,6 +31,13 @@
  *    nothing was enqueued (except H3ATTN_ERR_HIP after a failed launch) and
  *    h3attn_last_error() gives a message (thread-local).  Argument checks run
  *    on the host before any HIP call.  No C++ exception crosses the ABI.
+ *  - Environment switches, read on every call: H3ATTN_DEBUG=1 waits for the
+ *    stream after each launch and reports an execution error as
+ *    H3ATTN_ERR_HIP naming that launch (it synchronises: not for graph
+ *    capture or timing).  H3ATTN_FAULT=launch is for tests of the error path:
+ *    a call that passes its argument checks then makes no HIP call at all
+ *    (no device check, no launch) and returns H3ATTN_ERR_HIP for its first
+ *    launch.
  *  - Device: the current HIP device must be a gfx950 (MI355X); otherwise
  *    H3ATTN_ERR_DEVICE.
  *  - Aliasing: q, k and v may alias one another (e.g. views of a fused

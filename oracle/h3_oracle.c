@@ -8,9 +8,9 @@
  * the HIP library.
  *
  * What it follows.  The operation is the attention step of a MiniMax-H3
- * denoiser block together with the "Fused Q/K RMSNorm, RoPE, and layout work"
- * that the page "H3 Runtime Current State" lists under "Owned Performance
- * Kernels", and that the page "Buyer Questions: Current Evidence Status"
+ * denoiser block together with the Q/K norm, RoPE and relayout that the
+ * page "H3 Runtime Current State" counts as an owed fused kernel ("Owned
+ * Performance Kernels"), and that the page "Buyer Questions: Current Evidence Status"
  * (question 4, "Current answer") measures as the norm/RoPE share beside the
  * attention share of a block.  The pages print no formula, so this file
  * implements the plain textbook definitions, each reading stated where it is

@@ -80,14 +80,13 @@ def metrics(got: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
 # bf16 path gates: the max/mean absolute bounds of the target, plus relative
 # guards (rel-L2, cosine) that an all-zero or norm-skipping output would fail.
 BF16_GATE = dict(max_abs=2e-2, mean_abs=2e-3, rel_l2=1e-2, cosine=0.9999)
-# Sharp diagnostic inputs (RMSNorm weights ~2, per-token scales): qhat . khat /
-# sqrt(d) reaches ~45 and storing qhat/khat in bf16 (unit roundoff u = 2^-8,
-# 8-bit significand) perturbs a score by up to about u * |qhat| |khat| / sqrt(d)
-# ~ 0.04 (less in practice: the roundings of the d products partly cancel),
-# i.e. a few % relative on the dominant softmax weights of outputs of size ~0.4.
-# The gate is 1.5 times that worst case (measured max-abs 0.026); BF16_GATE
-# applies to every standard workload.
-SHARP_GATE = dict(max_abs=6e-2, mean_abs=6e-3, rel_l2=1.5e-2, cosine=0.9999)
+# Sharp diagnostic inputs (RMSNorm weights ~2, per-token scales): scores reach
+# ~45, and storing qhat' and khat in bf16 alone (the oracle evaluated on the
+# rounded values, tests/test_tolerance_floors.py) already gives max-abs 0.031,
+# mean-abs 0.0020 and rel-L2 0.0070 on these inputs, above the target's max-abs.
+# The gate is twice that floor (measured on the GPU: 0.026 / 0.0014 / 0.0072);
+# BF16_GATE applies to every standard workload.
+SHARP_GATE = dict(max_abs=6e-2, mean_abs=4e-3, rel_l2=1.4e-2, cosine=0.9999)
 # Quantised path: mean-abs bound of the target plus relative guards set at the
 # measured error (rel-L2 0.034-0.039, cosine >= 0.9992 on every case) plus margin;
 # an all-zero output (rel-L2 1) or a dropped V scale would fail them.

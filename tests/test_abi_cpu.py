@@ -127,6 +127,24 @@ def test_workspace_size_layout():
                                         v_stride=128, o_stride=128), [0, 10], quantized=True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_sequence_longer_than_the_descriptor_range(d):
+    """One (sequence, head) slice of the bf16 K/V copies must stay below 2 GiB:
+    the kernels' buffer descriptors take 32-bit sizes and offsets."""
+    hd = 24 * d
+    p = _params(head_dim=d, q_stride=hd, k_stride=hd, v_stride=hd, o_stride=hd)
+    limit = (2 ** 31 // (2 * d)) // 64 * 64 - 64
+    assert (limit + 64) * d * 2 <= 2 ** 31
+    p2 = _params(head_dim=d, num_seqs=2, q_stride=hd, k_stride=hd, v_stride=hd, o_stride=hd)
+    for cu in ([0, limit + 1], [0, 5, limit + 6]):
+        prm = p if len(cu) == 2 else p2
+        assert _call(prm, cu=cu) == h.H3ATTN_ERR_UNSUPPORTED
+        assert "at most %d" % limit in h.last_error()
+        with pytest.raises(h.H3AttnError):
+            h.h3attn_workspace_size(prm, cu)
+    assert h.h3attn_workspace_size(p, [0, limit]) > 3 * 24 * limit * d * 2
+
+
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device error path; a GPU is present")
 def test_valid_call_without_gpu_reports_device_error():
     assert _call() == h.H3ATTN_ERR_DEVICE
@@ -367,3 +385,34 @@ def test_sparse_workspace_sizes():
     assert h.sparse_items([0, 1000, 1000, 1129], 24) == 24 * 8 + 24 * 2
     with pytest.raises(h.H3AttnError):
         h.h3attn_workspace_size(p, [0, 1000], 4)
+
+
+def test_injected_launch_failure_reports_hip_error(monkeypatch):
+    """H3ATTN_FAULT=launch: a call that passes its argument checks makes no
+    HIP call and reports its first launch as failed, with a message naming
+    it; argument errors still come first, and the binding raises."""
+    monkeypatch.setenv("H3ATTN_FAULT", "launch")
+    cases = [
+        (lambda: _call(), "prologue launch"),
+        (lambda: _call(stages=2), "attention launch"),
+        (lambda: _call(quantized=True), "quantised prologue launch"),
+        (lambda: _call(quantized=True, stages=2), "quantised attention launch"),
+        (lambda: _call(quantized="mx"), "FP4 prologue launch"),
+        (lambda: _call(quantized="mx", stages=2), "FP4 attention launch"),
+        (lambda: _proj_call(), "projection launch"),
+        (lambda: _out_call(), "output projection launch"),
+        (lambda: _sparse_call(), "prologue launch"),
+        (lambda: _sparse_call(stages=4), "sparse attention launch"),
+    ]
+    for fn, what in cases:
+        assert fn() == h.H3ATTN_ERR_HIP, what
+        msg = h.last_error()
+        assert msg.startswith(what) and "injected" in msg, msg
+    assert _call(_params(num_heads=0)) == h.H3ATTN_ERR_INVALID_ARG
+    assert _call(cu=(0, 0), ptrs={"q": 0, "k": 0, "v": 0, "out": 0, "ws": 0}) == h.H3ATTN_OK   # nothing to launch
+    with pytest.raises(h.H3AttnError, match="injected") as err:
+        h._check(_call())
+    assert err.value.status == h.H3ATTN_ERR_HIP
+    monkeypatch.setenv("H3ATTN_FAULT", "")
+    if not _gpu_present():
+        assert _call() == h.H3ATTN_ERR_DEVICE     # switched off again: back to the device check

@@ -82,3 +82,31 @@ def test_softmax_scale_and_eps(torch_dev):
     o = h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], eps=w.eps, softmax_scale=scale)
     torch_dev.cuda.synchronize()
     _all_rows(w, inp, G.bits(o), G.BF16_GATE, "scale_eps", scale=scale)
+
+
+@pytest.mark.parametrize("quantized", [False, True, "mx"])
+def test_side_stream_without_workspace(torch_dev, quantized):
+    """A call on a side stream with no workspace given: the binding allocates
+    the workspace and the output on that stream, so memory that the current
+    stream allocates and overwrites right after the call (while the side
+    stream's kernels may still run) is never the workspace.  The result must
+    equal the same call on the current stream bit for bit."""
+    torch = torch_dev
+    w = synth.Workload("side_stream", H=4, d=128, seqs=(Seq(4, 16, 24), Seq(1, 8, 8, 50)), split=(32, 48, 48),
+                       k_offset_std=0.5, seed=24, quantized=quantized is True, fp4=quantized == "mx")
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    want = G.bits(G.run(w, t, quantized=quantized, label="side_stream_current"))
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda:0")
+    G.announce("side_stream quantized=%s N=%d H=%d" % (quantized, w.N, w.H))
+    for _ in range(3):
+        big = big @ big.t() * 1e-3                         # keeps the current stream busy
+    side.wait_stream(cur)                                 # the call starts after that work
+    o = h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], eps=w.eps, stream=side,
+                     quantized=quantized)
+    junk = [torch.full((1 << 24,), 0x7F, dtype=torch.uint8, device="cuda:0") for _ in range(8)]
+    torch.cuda.synchronize()
+    del junk
+    assert np.array_equal(G.bits(o), want)

@@ -67,6 +67,14 @@ MUTANTS = {
                              "double qs = p->scale;\n    for (int c = 0; c < p->d; ++c) row[c] *= qs;"),
     "mx_rowsum_unquantised": ("                l += P;\n", "                l += exp2(x[b0 + i] - m);\n"),
     "mx_query_from_k": ("prologue_one(p, 0, sel[i] / p->H, h, row);", "prologue_one(p, 1, sel[i] / p->H, h, row);"),
+    "q8_first_block_qscale": ("double qs = x->qscale[qi / 64] * p->scale / log(2.0);",
+                              "double qs = x->qscale[0] * p->scale / log(2.0);"),
+    "q8_qscale_of_next_block": ("double qs = x->qscale[qi / 64] * p->scale / log(2.0);",
+                                "double qs = x->qscale[(qi + 1) / 64] * p->scale / log(2.0);"),
+    "q8_v_scale_of_first_channel": ("vdec[j * d + c] = orc_e4m3_decode(vc[j * d + c]) * vsc[c];",
+                                    "vdec[j * d + c] = orc_e4m3_decode(vc[j * d + c]) * vsc[0];"),
+    "q8_v_scale_channel_reversed": ("vdec[j * d + c] = orc_e4m3_decode(vc[j * d + c]) * vsc[c];",
+                                    "vdec[j * d + c] = orc_e4m3_decode(vc[j * d + c]) * vsc[d - 1 - c];"),
     "q8_first_block_kscale": ("s[j] = (double)dot * qs * x->kscale[j / 64];",
                               "s[j] = (double)dot * qs * x->kscale[0];"),
 }

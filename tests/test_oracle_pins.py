@@ -448,6 +448,34 @@ def test_q8_rows_track_exact_attention():
     assert np.corrcoef(q8.ravel(), ex.ravel())[0, 1] > 0.998
 
 
+def test_q8_rows_are_softmax_of_decoded_codes():
+    """The quantised rows compose their pinned stages: the exact integer dot
+    product of the INT8 codes of qhat and of khat - mean, times the query's
+    own 64-token block scale, the key's own block scale, the softmax scale
+    and log2 e, fed to the pinned step-by-step softmax over the decoded v
+    (e4m3 value times its channel's scale).  Sequences of 79 and 130 tokens
+    give two and three blocks per head, with short last blocks."""
+    p = _problem([(2, 5, 7, 9), (2, 5, 13, 0)], H=2, d=32, split=(8, 12, 12), seed=38)
+    km = p.q8_kmean()
+    rows = _all_rows(p)
+    got = p.q8_attention_rows(rows, kmean=km)
+    e4m3 = np.array([oracle.e4m3_decode(c, library=L()) for c in range(256)])
+    for s in range(2):
+        n = int(p.cu[s + 1] - p.cu[s])
+        nb = (n + 63) // 64
+        for h in range(2):
+            blocks = [[p.q8_block_quant(which, s, h, b, kmean=km) for b in range(nb)] for which in (0, 1)]
+            qs, ks = (np.repeat([blk[0] for blk in blocks[w]], 64)[:n] for w in (0, 1))
+            qc, kc = (np.concatenate([blk[2] for blk in blocks[w]]).astype(np.int64) for w in (0, 1))
+            assert qc.shape == (n, p.d) and len(set(np.round(qs, 12))) == nb
+            vsc, _, vc = p.q8_v_quant(s, h)
+            vd = e4m3[vc] * vsc[None, :]
+            for i in range(n):
+                x = (kc @ qc[i]).astype(np.float64) * qs[i] * ks * p.scale / math.log(2.0)
+                want = oracle.q8_softmax_pv(x, vd, library=L())
+                np.testing.assert_allclose(got[(p.cu[s] + i) * 2 + h], want, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------- QKV projection
 
 def test_projection_matches_exact_sums():
