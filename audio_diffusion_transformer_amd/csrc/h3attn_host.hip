@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <string>
 
@@ -357,6 +358,67 @@ h3attn_status h3attn_fwd(const h3attn_params *p, const void *q, const void *k, c
 {
     return h3attn_fwd_stages(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, out, workspace,
                              workspace_bytes, stream, 3);
+}
+
+}  // extern "C"
+
+// ---- the static workspace of h3attn_fwd_static (callers that cannot allocate)
+//
+// A file-scope device array: each device that runs h3attn_fwd_static holds its
+// own copy, at its own address, until the process ends.  In host code the name
+// `scratch` only identifies the variable for the address lookup; it is not a
+// device address and is never passed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[H3ATTN_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_dev[64];      // device address of `scratch` per device, looked up once
+
+// This device's address of `scratch`, looked up on the first call with the
+// device current and kept per device.
+h3attn_status scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(H3ATTN_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(H3ATTN_ERR_DEVICE, "device index %d is outside 0..63", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(H3ATTN_ERR_HIP, "hipGetSymbolAddress of the static workspace on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return H3ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+h3attn_status h3attn_fwd_static(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                const float *norm_w, const float *rope_tables, const int32_t *cu_seqlens_host,
+                                void *out, void *stream)
+{
+    Plan pl;
+    h3attn_status st = make_plan(p, cu_seqlens_host, &pl);
+    if (st != H3ATTN_OK) return st;
+    if (pl.N == 0) return ok();
+    if ((st = check_ptrs(q, k, v, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
+    if (pl.bytes_bf16 > H3ATTN_STATIC_WORKSPACE_BYTES)
+        return fail(H3ATTN_ERR_WORKSPACE, "this shape needs %zu bytes of workspace; the static workspace holds %zu",
+                    pl.bytes_bf16, (size_t)H3ATTN_STATIC_WORKSPACE_BYTES);
+    if (fault_injected())
+        return launch_status(static_cast<hipStream_t>(stream), "prologue launch", [] { return hipSuccess; });
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != H3ATTN_OK) return st;
+    return h3attn_fwd_stages(p, q, k, v, norm_w, rope_tables, cu_seqlens_host, out, ws,
+                             H3ATTN_STATIC_WORKSPACE_BYTES, stream, 3);
 }
 
 h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void *k, const float *norm_w,

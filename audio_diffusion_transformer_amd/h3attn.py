@@ -25,12 +25,13 @@ H3ATTN_ERR_WORKSPACE = 3
 H3ATTN_ERR_DEVICE = 4
 H3ATTN_ERR_HIP = 5
 H3ATTN_MAX_SEQS = 64
+H3ATTN_STATIC_WORKSPACE_BYTES = 128 << 20
 
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
             "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
             "h3attn_proj_prologue", "h3attn_out_proj", "h3attn_fwd_sparse", "h3attn_fwd_sparse_stages",
             "h3attn_q8_prologue", "h3attn_fwd_mx", "h3attn_fwd_mx_stages", "h3attn_mx_prologue",
-            "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
+            "h3attn_fwd_static", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
 
@@ -68,6 +69,8 @@ def lib():
         for name in ("h3attn_fwd_stages", "h3attn_fwd_q8_stages", "h3attn_fwd_mx_stages"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = fwd_args + [C.c_int]
+        L.h3attn_fwd_static.restype = C.c_int
+        L.h3attn_fwd_static.argtypes = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp, vp]
         proj_args = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp, P(C.c_int32), vp, vp,
                      C.c_size_t, vp]
         L.h3attn_fwd_proj.restype = C.c_int
@@ -238,6 +241,23 @@ def h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=Non
                    _dev_ptr(rope_tables), cu, _dev_ptr(out), _dev_ptr(workspace),
                    workspace.numel() * workspace.element_size(), _stream_ptr(stream), quantized,
                    stages))
+    return out
+
+
+def static_raw(params, q, k, v, norm_w, rope_tables, cu_seqlens, out, stream) -> int:
+    """Direct call of h3attn_fwd_static with integer device pointers; returns the status."""
+    cu = _cu_array(cu_seqlens)
+    return int(lib().h3attn_fwd_static(C.byref(params), q, k, v, norm_w, rope_tables, _cu_ptr(cu), out, stream))
+
+
+def h3attn_fwd_static(q, k, v, norm_w, rope_tables, cu_seqlens, out, eps: float = 1e-6,
+                      softmax_scale: float = 0.0, stream=None):
+    """h3attn_fwd with the library's static device workspace (include/h3attn.h):
+    allocates nothing, so ``out`` must be given."""
+    cu = _cu_array(cu_seqlens)
+    params = params_for(q, k, v, out, len(cu) - 1, eps, softmax_scale)
+    _check(static_raw(params, _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w), _dev_ptr(rope_tables),
+                      cu, _dev_ptr(out), _stream_ptr(stream)))
     return out
 
 

@@ -121,6 +121,28 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
                                 size_t workspace_bytes, void *stream, int stages);
 
 /*
+ * h3attn_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace is a static device array of the library, H3ATTN_STATIC_WORKSPACE_BYTES
+ * (128 MiB) per device, which each device holds from the first call on it until
+ * the process ends.  The other arguments, the result and the errors are those
+ * of h3attn_fwd; a shape whose h3attn_workspace_size(p, cu, 0) exceeds the
+ * array returns H3ATTN_ERR_WORKSPACE before any HIP call (the limit is
+ * H * padded tokens <= about 174,000 at d = 128: e.g. 7,168 tokens at H = 24,
+ * 58,112 at H = 3).  No allocation, memset or copy is made: the prologue writes
+ * every workspace byte the attention then reads, so nothing carries over from
+ * the previous call.  Every call on one device shares the one array: calls
+ * that overlap in time on one device (two streams, two threads) race and must
+ * be ordered by the caller.  The first call on a device looks up the array's
+ * device address (it may load the library's device code), so it should not be
+ * the one made under stream capture.
+ */
+#define H3ATTN_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+h3attn_status h3attn_fwd_static(const h3attn_params *p, const void *q, const void *k, const void *v,
+                                const float *norm_w, const float *rope_tables,
+                                const int32_t *cu_seqlens_host, void *out, void *stream);
+
+/*
  * Block-quantised variant with the same arguments and result layout
  * (workspace >= h3attn_workspace_size(p, cu, 1)).  After the same RMSNorm +
  * RoPE: the per-sequence mean of khat over tokens is subtracted (which leaves

@@ -416,3 +416,35 @@ def test_injected_launch_failure_reports_hip_error(monkeypatch):
     monkeypatch.setenv("H3ATTN_FAULT", "")
     if not _gpu_present():
         assert _call() == h.H3ATTN_ERR_DEVICE     # switched off again: back to the device check
+
+
+def _static_call(params=None, cu=(0, 1000), ptrs=None):
+    params = params if params is not None else _params()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, norm_w=FAKE, rope=FAKE, out=FAKE)
+    p.update(ptrs or {})
+    return h.static_raw(params, p["q"], p["k"], p["v"], p["norm_w"], p["rope"], np.array(cu, np.int32), p["out"],
+                        None)
+
+
+def test_static_workspace_entry_point_limits():
+    """h3attn_fwd_static takes shapes whose bf16 workspace fits the static
+    array and rejects larger ones, before any HIP call; argument errors are
+    those of h3attn_fwd."""
+    cap = h.H3ATTN_STATIC_WORKSPACE_BYTES
+    assert h.h3attn_workspace_size(_params(), [0, 7168]) <= cap < h.h3attn_workspace_size(_params(), [0, 7169])
+    assert _static_call(cu=(0, 7169)) == h.H3ATTN_ERR_WORKSPACE
+    assert "static workspace holds %d" % cap in h.last_error()
+    p3 = _params(num_heads=3, q_stride=384, k_stride=384, v_stride=384, o_stride=384)
+    assert _static_call(p3, cu=(0, 58113)) == h.H3ATTN_ERR_WORKSPACE
+    assert _static_call(_params(num_heads=0)) == h.H3ATTN_ERR_INVALID_ARG
+    assert _static_call(ptrs={"out": 0}) == h.H3ATTN_ERR_INVALID_ARG and "out" in h.last_error()
+    assert _static_call(cu=(0, 0), ptrs={"q": 0, "k": 0, "v": 0, "out": 0}) == h.H3ATTN_OK
+    if not _gpu_present():
+        assert _static_call(cu=(0, 7168)) == h.H3ATTN_ERR_DEVICE
+        assert _static_call(p3, cu=(0, 58112)) == h.H3ATTN_ERR_DEVICE
+
+
+def test_static_workspace_entry_point_injected_failure(monkeypatch):
+    monkeypatch.setenv("H3ATTN_FAULT", "launch")
+    assert _static_call() == h.H3ATTN_ERR_HIP and "injected" in h.last_error()
+    assert _static_call(cu=(0, 7169)) == h.H3ATTN_ERR_WORKSPACE       # the size check comes first
