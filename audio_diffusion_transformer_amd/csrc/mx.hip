@@ -45,6 +45,7 @@ namespace h3 {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int MD = 128;                      // head dim of the FP4 path
 constexpr int kRowBytes = MD / 2;            // FP4 bytes of one token row
@@ -59,6 +60,16 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax)
     return amax > 0.f ? (uint32_t)max(e - 2, 1) : 127u;
 }
 __device__ __forceinline__ float mx_scale_value(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// This lane's index (0..63) from the hardware lane counter, opaque to the
+// compiler so that it is computed where it is used rather than kept live (and
+// spilled) from the kernel start.
+__device__ __forceinline__ int lane_here()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 
 // Eight values -> eight e2m1 codes of x / scale (value i in nibble i).
 __device__ __forceinline__ uint32_t fp4x8(const float *y, float scale)
@@ -79,19 +90,20 @@ __device__ __forceinline__ int mx_key_row(int r)
 {
     return (((r >> 4) & 1) << 5) | (((r >> 2) & 3) << 3) | (((r >> 5) & 1) << 2) | (r & 3);
 }
-// Byte of a K tile's scales for tile row P and channel block cb: lane (m, h)
-// reads the word 2m + h, whose byte 2 kb + st is its A scale in score MFMA
-// (key block kb, channel step st).
+// Byte of a K tile's scales for tile row P and channel block cb: lane
+// L = 32 h + m reads word L (consecutive lanes, consecutive words: 4-byte LDS
+// reads of a word per lane are conflict-free only that way), whose byte
+// 2 kb + st is its A scale in score MFMA (key block kb, channel step st).
 __device__ __forceinline__ int mx_kscale_pos(int P, int cb)
 {
-    return 8 * (P & 31) + 4 * (cb & 1) + 2 * (P >> 5) + (cb >> 1);
+    return 4 * ((P & 31) + 32 * (cb & 1)) + 2 * (P >> 5) + (cb >> 1);
 }
-// Byte of a V tile's scales for channel ch and key block b: lane (m, h) reads
-// the word 2m + h, whose byte db is its A scale in the P.V MFMA of channel
-// block db.
+// Byte of a V tile's scales for channel ch and key block b: lane L = 32 h + m
+// reads word L, whose byte db is its A scale in the P.V MFMA of channel block
+// db.
 __device__ __forceinline__ int mx_vscale_pos(int ch, int b)
 {
-    return 8 * (ch & 31) + 4 * b + (ch >> 5);
+    return 4 * ((ch & 31) + 32 * b) + (ch >> 5);
 }
 
 // Decode of the XCD-aware (tile, head) numbering of the prologue launches.
@@ -316,7 +328,7 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int m = lane & 31, hh = lane >> 5;
+    int m = lane & 31, hh = lane >> 5;    // re-derived before the tail loop
     const int q0 = qb * kBlockM + wave * 32;
 
     // Q row q0 + m: channels 64 st + 32 hh .. +31 of step st (16 bytes each);
@@ -347,9 +359,15 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
                                                  4, 4 * lane, jj * kScaleBytes, 0, 0);
     };
 
-    f32x16 o0 = {}, o1 = {}, o2 = {}, o3 = {}, ol = {};
-    // A operand of the row-sum MFMA: channel row 0 all e2m1 1.0 (code 2), rows 1..31 zero
-    const int one4 = m == 0 ? 0x22222222 : 0;
+    f32x16 o0 = {}, o1 = {}, o2 = {}, o3 = {};
+    // Row sum on the half-size matrix core (16 x 16 x 128, a 4-register
+    // accumulator): its B operand is the P operand as it stands, read as lane L
+    // = column L % 16, keys 32 (L / 16) .. +31, so column j holds queries j and
+    // j + 16.  A row 0 is e2m1 1.0 (code 2) over keys 0-31 and 64-95 (lanes 0
+    // and 32), row 1 over keys 32-63 and 96-127 (lanes 17 and 49), the rest 0:
+    // register 0 of lane j < 16 sums query j's P, register 1 query j + 16's.
+    f32x4 ol = {};
+    const int one4 = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? 0x22222222 : 0;
     const i32x8 ones = {one4, one4, one4, one4, 0, 0, 0, 0};
     float m_run = 0.f;              // running max of the scores (log2 units)
     bool first = true;
@@ -376,7 +394,7 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
     auto step = [&](int jj, const uint8_t *kl, const uint8_t *vl, const uint32_t *ksl, const uint32_t *vsl,
                     bool more, void *kn, void *vn, uint32_t *ksn, uint32_t *vsn, bool mask, int jfill) {
         const i32x4 k00 = kfrag(kl, 0, 0), k10 = kfrag(kl, 1, 0), k01 = kfrag(kl, 0, 1), k11 = kfrag(kl, 1, 1);
-        const uint32_t ksw = ksl[2 * m + hh];
+        const uint32_t ksw = ksl[lane];
 
         f32x16 s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k00), wide(qf0), ninit, 4, 4, 0, ksw, 0, qsc);
         f32x16 s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(k10), wide(qf0), ninit, 4, 4, 2, ksw, 0, qsc);
@@ -405,7 +423,10 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
             const float delta = need ? x : 0.f;
             if (!first) {
                 const float alpha = __builtin_amdgcn_exp2f(-delta);
-                ol[0] *= alpha;     // rows 1..31 of the row-sum block are zero
+                ol[0] *= alpha;                     // query m of lane m < 16
+                // query m + 16 (registers 2, 3 are zero): alpha of lane m + 16
+                ol[1] *= __int_as_float(
+                    __builtin_amdgcn_ds_bpermute(((lane_here() + 16) & 63) << 2, __float_as_int(alpha)));
                 o0 *= alpha;
                 o1 *= alpha;
                 o2 *= alpha;
@@ -432,14 +453,14 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
         const float psc = mx_scale_value(pbyte);
         const i32x8 pf = {(int)fp4x8(p, psc), (int)fp4x8(p + 8, psc), (int)fp4x8(p + 16, psc),
                           (int)fp4x8(p + 24, psc), 0, 0, 0, 0};
-        const uint32_t vsw = vsl[2 * m + hh];
+        const uint32_t vsw = vsl[lane];
         const i32x4 v0 = vfrag(vl, 0), v1 = vfrag(vl, 1), v2 = vfrag(vl, 2), v3 = vfrag(vl, 3);
         if (more) fill(jfill, kn, vn, ksn, vsn);
         o0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(v0), pf, o0, 4, 4, 0, vsw, 0, pbyte);
         o1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(v1), pf, o1, 4, 4, 1, vsw, 0, pbyte);
         o2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(v2), pf, o2, 4, 4, 2, vsw, 0, pbyte);
         o3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(v3), pf, o3, 4, 4, 3, vsw, 0, pbyte);
-        ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, ol, 4, 4, 0, 127u, 0, pbyte);
+        ol = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf, ol, 4, 4, 0, 127u, 0, pbyte);
     };
 
     // Tile t lives in buffer t % 3.  A fill is three loads per wave (K codes,
@@ -471,6 +492,13 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
     // masked), with the buffer picked at run time: the compiler then waits
     // for every fill before reading LDS, which only costs these few steps,
     // and one copy of the step keeps the code small.
+    // The lane's row and half again from the hardware counter: the tail's
+    // fragment addresses then need nothing kept live across the main loop.
+    {
+        const int lr = lane_here();
+        m = lr & 31;
+        hh = lr >> 5;
+    }
     auto kb = [&](int r) -> uint8_t * { return r == 0 ? lk0 : r == 1 ? lk1 : lk2; };
     auto vb = [&](int r) -> uint8_t * { return r == 0 ? lv0 : r == 1 ? lv1 : lv2; };
     auto ksb = [&](int r) -> uint32_t * { return r == 0 ? lks0 : r == 1 ? lks1 : lks2; };
@@ -489,9 +517,14 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
     // no fill may still be writing LDS when the workgroup ends
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
-    // row sum: channel row 0 of the ones block lives in register 0 of the lanes with hh = 0
-    const float inv = 1.0f / row_sum2(hh == 0 ? ol[0] : 0.f);
-    const int qr = q0 + m;
+    // The lane index again: nothing lane-dependent from before the loop has to
+    // stay live (or spill) across it.
+    const int lane_e = lane_here();
+    const int m_e = lane_e & 31, hh_e = lane_e >> 5;
+    // row sum of query m: register m / 16 of lane m % 16
+    const float l0 = __shfl(ol[0], m_e & 15), l1 = __shfl(ol[1], m_e & 15);
+    const float inv = 1.0f / (m_e < 16 ? l0 : l1);
+    const int qr = q0 + m_e;
     if (qr < n) {
         uint16_t *op = a.out + ((int64_t)a.seq_cu[si] + qr) * a.o_stride + (int64_t)head * MD;
         const f32x16 *os[4] = {&o0, &o1, &o2, &o3};
@@ -500,7 +533,7 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x16 &ov = *os[db];
-                const int d0 = 32 * db + 8 * i + 4 * hh;
+                const int d0 = 32 * db + 8 * i + 4 * hh_e;
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                 const u32x2 w = {pack2(ov[4 * i] * inv, ov[4 * i + 1] * inv),
                                  pack2(ov[4 * i + 2] * inv, ov[4 * i + 3] * inv)};
