@@ -97,8 +97,25 @@ __device__ __forceinline__ bool fixed_shift_bound(const bf16x8 (&qf)[KSTEPS], co
     return __all(mb <= kFixedShiftMax);
 }
 
+// Work item of workgroup b of n under the dispatcher's round-robin spread of
+// workgroups over the 8 XCDs (b goes to XCD b % 8).  Items are taken in
+// windows of W = 512 (the workgroups resident at once, two per CU): a window
+// stays on one head, so every XCD streams the same keys through the shared
+// last-level cache, and inside it XCD x runs the contiguous items x*64 ..
+// x*64 + 63, so the query blocks that share its L2 are neighbours.  The last
+// partial window keeps the dispatch order.
+__device__ __forceinline__ int xcd_window_item(int b, int n)
+{
+    constexpr int X = 8, W = 512, C = W / X;
+    if (b >= n / W * W) return b;
+    const int r = b % W;
+    return b - r + (r % X) * C + r / X;
+}
+
 // SPARSE: visit only the 64-key tiles listed for this query block (block-sparse
-// attention, a.tiles); otherwise every tile of the sequence.
+// attention, a.tiles); otherwise every tile of the sequence.  Sparse work items
+// are numbered by xcd_window_item: neighbouring query blocks keep most of the
+// same tiles, so running them on one XCD lets its L2 serve the shared tiles.
 template <int D, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 {
@@ -113,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     __shared__ int32_t ltiles[SPARSE ? kMaxSparseTiles : 1];     // the block's tile list
 
     // ---- work item: (sequence, head, 128-row query block)
-    const int b = blockIdx.x;
+    const int b = SPARSE ? xcd_window_item((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
     int si = 0;
     while (b >= a.item_pre[si + 1]) ++si;
     const int rem = b - a.item_pre[si];

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void out_proj_kernel(OutProjArg
 
     const int nfb = a.model_dim / D;
     int blk, F2;
-    if (!gemm_tile(a.nblk, (nfb + 1) / 2, blk, F2)) return;
+    if (!gemm_tile<2>(a.nblk, (nfb + 1) / 2, blk, F2)) return;
     const int rows_blk = (int)min(a.N - (int64_t)kGemmBM * blk, (int64_t)kGemmBM);
 
     const int tid = threadIdx.x;

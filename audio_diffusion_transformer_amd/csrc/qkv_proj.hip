@@ -64,7 +64,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void qkv_proj_kernel(ProjArgs a
     const int H = a.H;
     const int64_t nfb = 3 * (int64_t)H;
     int b, F2;
-    if (!gemm_tile(a.nblk, (nfb + 1) / 2, b, F2)) return;
+    if (!gemm_tile<8>(a.nblk, (nfb + 1) / 2, b, F2)) return;
 
     int s, j0, valid0;
     tile_seq(a.seq.cu, a.seq.off, a.seq.S, 4 * b, s, j0, valid0);
