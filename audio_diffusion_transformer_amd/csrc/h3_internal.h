@@ -267,6 +267,7 @@ hipError_t launch_out_proj(const OutProjArgs &a, hipStream_t st);
 hipError_t launch_sparse_select(const SparseSelectArgs &a, int d, hipStream_t st);
 hipError_t launch_mx_prep(const MxArgs &a, int d, hipStream_t st);
 hipError_t launch_attn_mx(const MxAttnArgs &a, int d, int64_t nitems, hipStream_t st);
+hipError_t launch_mfma_ceiling(int mix, int workgroups, int iters, float *out, hipStream_t st);
 hipError_t launch_mx_export(const MxExportArgs &a, hipStream_t st);
 
 // Queries per workgroup of the attention kernels (work-item granularity).

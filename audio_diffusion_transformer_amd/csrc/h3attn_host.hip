@@ -421,6 +421,20 @@ h3attn_status h3attn_fwd_static(const h3attn_params *p, const void *q, const voi
                              H3ATTN_STATIC_WORKSPACE_BYTES, stream, 3);
 }
 
+h3attn_status h3attn_mfma_ceiling(int mix, int workgroups, int iters, float *out, void *stream)
+{
+    if (mix != 0 && mix != 1) return fail(H3ATTN_ERR_INVALID_ARG, "mix must be 0 or 1 (got %d)", mix);
+    if (workgroups < 1 || workgroups > (1 << 20))
+        return fail(H3ATTN_ERR_INVALID_ARG, "workgroups must be in [1, 2^20] (got %d)", workgroups);
+    if (iters < 1 || iters > (1 << 20)) return fail(H3ATTN_ERR_INVALID_ARG, "iters must be in [1, 2^20] (got %d)", iters);
+    if (!out) return fail(H3ATTN_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned(out, 4)) return fail(H3ATTN_ERR_INVALID_ARG, "out is not 4-byte aligned");
+    h3attn_status st;
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return launch_status(hs, "mfma ceiling launch", [&] { return launch_mfma_ceiling(mix, workgroups, iters, out, hs); });
+}
+
 h3attn_status h3attn_prologue(const h3attn_params *p, const void *q, const void *k, const float *norm_w,
                               const float *rope_tables, const int32_t *cu_seqlens_host, void *q_hat,
                               void *k_hat, void *stream)

@@ -31,7 +31,7 @@ EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_
             "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
             "h3attn_proj_prologue", "h3attn_out_proj", "h3attn_fwd_sparse", "h3attn_fwd_sparse_stages",
             "h3attn_q8_prologue", "h3attn_fwd_mx", "h3attn_fwd_mx_stages", "h3attn_mx_prologue",
-            "h3attn_fwd_static", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
+            "h3attn_fwd_static", "h3attn_mfma_ceiling", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
 
@@ -69,6 +69,8 @@ def lib():
         for name in ("h3attn_fwd_stages", "h3attn_fwd_q8_stages", "h3attn_fwd_mx_stages"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = fwd_args + [C.c_int]
+        L.h3attn_mfma_ceiling.restype = C.c_int
+        L.h3attn_mfma_ceiling.argtypes = [C.c_int, C.c_int, C.c_int, vp, vp]
         L.h3attn_fwd_static.restype = C.c_int
         L.h3attn_fwd_static.argtypes = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp, vp]
         proj_args = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp, P(C.c_int32), vp, vp,
@@ -242,6 +244,11 @@ def h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=Non
                    workspace.numel() * workspace.element_size(), _stream_ptr(stream), quantized,
                    stages))
     return out
+
+
+def mfma_ceiling_raw(mix: int, workgroups: int, iters: int, out, stream) -> int:
+    """Direct call of h3attn_mfma_ceiling (device pointer `out`); returns the status."""
+    return int(lib().h3attn_mfma_ceiling(int(mix), int(workgroups), int(iters), out, stream))
 
 
 def static_raw(params, q, k, v, norm_w, rope_tables, cu_seqlens, out, stream) -> int:

@@ -106,6 +106,41 @@ def device_copy_rate(torch, dev, mib: int = 1024, reps: int = 5) -> float:
     return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def mfma_ceiling(torch, h, dev, stream, target_ms: float = 120.0):
+    """Sustained bf16 matrix-core rate of this device (h3attn_mfma_ceiling):
+    register-only streams of v_mfma_f32_32x32x16_bf16 on changing operands on
+    all 256 CUs, alone and with one v_exp_f32 + one FMA per MFMA (the softmax's
+    vector work).  Each launch runs ~target_ms, long enough for the clock to
+    settle where the power limit holds it; one warm-up launch, then two timed.
+    Returns TFLOP/s for both mixes (after the timed region)."""
+    wg = 256
+    out = torch.empty(512 * wg, dtype=torch.float32, device=dev)
+    sp = int(stream.cuda_stream)
+    flop_per_iter = 32768.0 * 8 * 8 * wg
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(mix, iters, reps):
+        e0.record(stream)
+        for _ in range(reps):
+            st = h.mfma_ceiling_raw(mix, wg, iters, out.data_ptr(), sp)
+            if st != 0:
+                raise RuntimeError("%s: %s" % (h.status_string(st), h.last_error()))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    for mix, key in ((0, "mfma_only_TFLOPs"), (1, "mfma_with_exp_fma_TFLOPs")):
+        probe = 20000
+        ms = timed(mix, probe, 1)
+        iters = int(max(1, min(1 << 20, probe * target_ms / max(ms, 1e-3))))
+        timed(mix, iters, 1)                      # warm-up at the full length
+        ms = timed(mix, iters, 2)
+        res[key] = round(flop_per_iter * iters / (ms * 1e-3) / 1e12, 1)
+    del out
+    return res
+
+
 def one_head_problem(w, inputs, head: int):
     """The oracle problem of one head of a projection workload: its q, k, v
     rows of W_qkv, projected in fp64 (heads are independent)."""
@@ -452,6 +487,7 @@ def main():
     sel_avg = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])) if sparse else 0.0
     step_ms = [ev[i][0].elapsed_time(ev[i][nst]) for i in range(K)]
     copy_gbps = device_copy_rate(torch, dev)        # after the timed region
+    ceiling = mfma_ceiling(torch, h, dev, stream) if not (w.fp4 or w.quantized) else None
     print("[bench] %d steps: %.3f ms/step (attention %.3f, %s %.3f), wall %.3f s" % (
         K, ms_step, att_avg, "projection" if proj else "prologue", pro_avg, wall), file=sys.stderr, flush=True)
     unfused = library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream) if proj else None
@@ -520,6 +556,8 @@ def main():
                      "kernel": {"mx": "attn_mx_kernel", "q8": "attn_q8_kernel",
                                 "bf16": "attn_bf16_pp_kernel<128>"}[kname],
                      "avg_ms": round(att_avg, 4)},
+        # the same box's sustained bf16 matrix-core rate (h3attn_mfma_ceiling), beside the datasheet peak
+        "measured_mfma_ceiling": None,
         "step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 4),
                     "p50": round(float(np.percentile(step_ms, 50)), 4),
                     "p90": round(float(np.percentile(step_ms, 90)), 4)},
@@ -531,6 +569,10 @@ def main():
                     "attention_avg_ms": round(att_avg, 4)},
         "cpu_baseline": None,
     }
+    if ceiling is not None:
+        ceiling["attention_frac_of_mfma_only"] = round(achieved / ceiling["mfma_only_TFLOPs"], 4)
+        ceiling["attention_frac_of_mfma_with_exp_fma"] = round(achieved / ceiling["mfma_with_exp_fma_TFLOPs"], 4)
+        res["measured_mfma_ceiling"] = ceiling
     if sparse:
         res["kernels"].update({
             "selection_avg_ms": round(sel_avg, 4),

@@ -448,3 +448,16 @@ def test_static_workspace_entry_point_injected_failure(monkeypatch):
     monkeypatch.setenv("H3ATTN_FAULT", "launch")
     assert _static_call() == h.H3ATTN_ERR_HIP and "injected" in h.last_error()
     assert _static_call(cu=(0, 7169)) == h.H3ATTN_ERR_WORKSPACE       # the size check comes first
+
+
+def test_mfma_ceiling_argument_errors(monkeypatch):
+    for args, msg in [((2, 256, 10), "mix"), ((0, 0, 10), "workgroups"), ((0, 1 << 21, 10), "workgroups"),
+                      ((0, 256, 0), "iters"), ((1, 256, 1 << 21), "iters")]:
+        assert h.mfma_ceiling_raw(*args, FAKE, None) == h.H3ATTN_ERR_INVALID_ARG
+        assert msg in h.last_error()
+    assert h.mfma_ceiling_raw(0, 256, 10, 0, None) == h.H3ATTN_ERR_INVALID_ARG and "NULL" in h.last_error()
+    assert h.mfma_ceiling_raw(0, 256, 10, FAKE + 2, None) == h.H3ATTN_ERR_INVALID_ARG
+    if not _gpu_present():
+        assert h.mfma_ceiling_raw(0, 256, 10, FAKE, None) == h.H3ATTN_ERR_DEVICE
+    monkeypatch.setenv("H3ATTN_FAULT", "launch")
+    assert h.mfma_ceiling_raw(1, 256, 10, FAKE, None) == h.H3ATTN_ERR_HIP and "mfma ceiling" in h.last_error()
