@@ -24,7 +24,7 @@
 //          than 1, so p <= 2; P quantised to e4m3 as p * 224 (a fixed per-row
 //          scale mapping the largest possible p to 448); O^T += V8^T . P8^T on
 //          v_mfma_f32_32x32x64_f8f6f4; the row sum l is the sum of the
-//          quantised P (one more FP8 MFMA against a row of ones).  Finally
+//          quantised P (one more, half-size FP8 MFMA against ones).  Finally
 //          o_c = O_c * vscale_c / l.
 #include "h3_internal.h"
 #include "norm_rope.h"
@@ -309,7 +309,8 @@ __global__ __launch_bounds__(256) void q8_export_kernel(Q8ExportArgs a)
 // 32 channels) and, beside them, the exp2 and FP8 packing of tile j.  The row
 // sum comes from the matrix cores too: one more FP8 MFMA per tile multiplies P
 // by a constant row of ones, so l is the sum of the quantised P actually
-// applied to V.
+// applied to V.  It runs on the half-size 16 x 16 x 128 shape (half the
+// matrix-core cycles of a 32 x 32 x 64 one, a 4-register accumulator).
 __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
 {
     __shared__ __attribute__((aligned(16))) int8_t lk0[kTile * QD], lk1[kTile * QD];
@@ -353,10 +354,17 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     auto load_k = [&](int j, void *dst) { kfill.load(krs, (uint32_t)(j * tbytes), dst, wave); };
     auto load_v = [&](int j, void *dst) { vfill.load(vrs, (uint32_t)(j * tbytes), dst, wave); };
 
-    f32x16 o[4], ol = (f32x16){};   // O^T per 32-channel block; ol row 0 = row sum
+    f32x16 o[4];                    // O^T per 32-channel block
     for (int i = 0; i < 4; ++i) o[i] = (f32x16){};
-    // A operand of the row-sum MFMA: channel row 0 all ones (e4m3 1.0 = 0x38), rows 1..31 zero
-    const uint32_t one4 = m == 0 ? 0x38383838u : 0u;
+    // Row sum on the 16 x 16 x 128 FP8 shape.  Its B operand is the P operand
+    // as it stands, read as lane L = column L % 16 over keys 32 (L / 16) .. +31
+    // (lane L of the 32 x 32 x 64 operand holds query L % 32, key half L / 32),
+    // so column j holds queries j and j + 16.  A row 0 is e4m3 1.0 (0x38) in
+    // lanes 0 and 32, row 1 in lanes 17 and 49, every other row 0: register 0
+    // of lane j < 16 sums query j's P, register 1 query j + 16's, registers
+    // 2, 3 and lanes 16..63 stay 0.
+    f32x4_t ol = {};
+    const uint32_t one4 = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? 0x38383838u : 0u;
     const i32x8 ones = {(int)one4, (int)one4, (int)one4, (int)one4, (int)one4, (int)one4, (int)one4, (int)one4};
     i32x8 pp = (i32x8){};          // FP8 P of the previous tile, whose P.V is still pending
     float m_run = 0.f;              // running max (log2 units) of the scaled scores
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
 #pragma unroll
         for (int db = 0; db < 4; ++db)
             o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vfrag(vl, db), pf, o[db], 0, 0, 0, 0, 0, 0);
-        ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, ol, 0, 0, 0, 0, 0, 0);
+        ol = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf, ol, 0, 0, 0, 0, 0, 0);
     };
     // Key (0..63 within the tile) of element r of the lane's score block kb.
     auto key_of = [&](int kb, int r) { return 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3); };
@@ -445,7 +453,9 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
                 pv(vprev, pp);
                 pp = (i32x8){};
                 const float alpha = __builtin_amdgcn_exp2f(-delta);
-                ol[0] *= alpha;     // rows 1..31 of the row-sum block are zero
+                ol[0] *= alpha;     // query m of lane m < 16
+                // query m + 16: the alpha of lane m + 16
+                ol[1] *= __int_as_float(__builtin_amdgcn_ds_bpermute(((lane + 16) & 63) << 2, __float_as_int(alpha)));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] *= alpha;
             }
@@ -485,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
             else
                 n1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[i], qf[st], st ? n1 : magic, 0, 0, 0);
             if (i == 0)
-                ol = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pp, ol, 0, 0, 0, 0, 0, 0);
+                ol = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pp, ol, 0, 0, 0, 0, 0, 0);
             else if (i & 1)
                 o[i >> 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[i >> 1], pp, o[i >> 1], 0, 0, 0, 0, 0, 0);
             // The empty asm consumes the word here: without it the compiler
@@ -567,8 +577,9 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
         pv(vl, pf);
     }
 
-    // row sum: channel row 0 of the ones block lives in register 0 of the lanes with hh = 0
-    const float inv = 1.0f / row_sum2(hh == 0 ? ol[0] : 0.f);
+    // row sum of query m: register m / 16 of lane m % 16
+    const float l0 = __shfl(ol[0], m & 15), l1 = __shfl(ol[1], m & 15);
+    const float inv = 1.0f / (m < 16 ? l0 : l1);
     const int qrow = q0 + m;
     if (qrow < n) {
         const float *vs = a.vscale + ((int64_t)a.seq_idx[si] * a.H + head) * QD;
