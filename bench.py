@@ -106,17 +106,19 @@ def device_copy_rate(torch, dev, mib: int = 1024, reps: int = 5) -> float:
     return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
-def mfma_ceiling(torch, h, dev, stream, target_ms: float = 120.0):
-    """Sustained bf16 matrix-core rate of this device (h3attn_mfma_ceiling):
-    register-only streams of v_mfma_f32_32x32x16_bf16 on changing operands on
-    all 256 CUs, alone and with one v_exp_f32 + one FMA per MFMA (the softmax's
-    vector work).  Each launch runs ~target_ms, long enough for the clock to
-    settle where the power limit holds it; one warm-up launch, then two timed.
-    Returns TFLOP/s for both mixes (after the timed region)."""
+def mfma_ceiling(torch, h, dev, stream, quantized: bool = False, target_ms: float = 120.0):
+    """Sustained matrix-core rate of this device (h3attn_mfma_ceiling):
+    register-only MFMA streams on changing operands on all 256 CUs, alone and
+    with the vector work the attention adds beside its MFMAs.  bf16 (mixes 0,
+    1): v_mfma_f32_32x32x16_bf16, then with one v_exp_f32 + one FMA per MFMA.
+    Quantised (mixes 2, 3): v_mfma_i32_32x32x32_i8, then with two FMAs, two
+    v_exp_f32, one FP8 pack and one max per MFMA (the quantised kernel's
+    ratio).  Each launch runs ~target_ms, long enough for the clock to settle
+    where the power limit holds it; one warm-up launch, then two timed.
+    Returns the rates (TFLOP/s or TOP/s) of both mixes (after the timed region)."""
     wg = 256
     out = torch.empty(512 * wg, dtype=torch.float32, device=dev)
     sp = int(stream.cuda_stream)
-    flop_per_iter = 32768.0 * 8 * 8 * wg
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed(mix, iters, reps):
@@ -129,8 +131,15 @@ def mfma_ceiling(torch, h, dev, stream, target_ms: float = 120.0):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    if quantized:
+        mixes = ((2, "int8_mfma_only_TOPs"), (3, "int8_mfma_with_q8_vector_work_TOPs"))
+        ops_per_mfma = 65536.0
+    else:
+        mixes = ((0, "mfma_only_TFLOPs"), (1, "mfma_with_exp_fma_TFLOPs"))
+        ops_per_mfma = 32768.0
+    flop_per_iter = ops_per_mfma * 8 * 8 * wg
     res = {}
-    for mix, key in ((0, "mfma_only_TFLOPs"), (1, "mfma_with_exp_fma_TFLOPs")):
+    for mix, key in mixes:
         probe = 20000
         ms = timed(mix, probe, 1)
         iters = int(max(1, min(1 << 20, probe * target_ms / max(ms, 1e-3))))
@@ -487,7 +496,7 @@ def main():
     sel_avg = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])) if sparse else 0.0
     step_ms = [ev[i][0].elapsed_time(ev[i][nst]) for i in range(K)]
     copy_gbps = device_copy_rate(torch, dev)        # after the timed region
-    ceiling = mfma_ceiling(torch, h, dev, stream) if not (w.fp4 or w.quantized) else None
+    ceiling = mfma_ceiling(torch, h, dev, stream, quantized=w.quantized) if not w.fp4 else None
     print("[bench] %d steps: %.3f ms/step (attention %.3f, %s %.3f), wall %.3f s" % (
         K, ms_step, att_avg, "projection" if proj else "prologue", pro_avg, wall), file=sys.stderr, flush=True)
     unfused = library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream) if proj else None
@@ -556,7 +565,8 @@ def main():
                      "kernel": {"mx": "attn_mx_kernel", "q8": "attn_q8_kernel",
                                 "bf16": "attn_bf16_pp_kernel<128>"}[kname],
                      "avg_ms": round(att_avg, 4)},
-        # the same box's sustained bf16 matrix-core rate (h3attn_mfma_ceiling), beside the datasheet peak
+        # the same box's sustained matrix-core rate for this path's MFMA type, alone and with the
+        # path's vector work beside it (h3attn_mfma_ceiling), beside the datasheet peak
         "measured_mfma_ceiling": None,
         "step_ms": {"p10": round(float(np.percentile(step_ms, 10)), 4),
                     "p50": round(float(np.percentile(step_ms, 50)), 4),
@@ -570,8 +580,8 @@ def main():
         "cpu_baseline": None,
     }
     if ceiling is not None:
-        ceiling["attention_frac_of_mfma_only"] = round(achieved / ceiling["mfma_only_TFLOPs"], 4)
-        ceiling["attention_frac_of_mfma_with_exp_fma"] = round(achieved / ceiling["mfma_with_exp_fma_TFLOPs"], 4)
+        for key in list(ceiling):
+            ceiling["attention_frac_of_" + key.rsplit("_", 1)[0]] = round(achieved / ceiling[key], 4)
         res["measured_mfma_ceiling"] = ceiling
     if sparse:
         res["kernels"].update({

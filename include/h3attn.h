@@ -385,19 +385,23 @@ const char *h3attn_last_error(void);
 int h3attn_version(void);
 
 /*
- * Diagnostic, not part of the attention path: the sustained bf16 matrix-core
- * rate of the current device, a measured ceiling beside the datasheet peak
- * for the roofline of the attention kernels.  Launches `workgroups`
- * workgroups of 512 threads on `stream`; every wave runs iters x 8
- * v_mfma_f32_32x32x16_bf16 on register operands that change from instruction
- * to instruction (hashed values, like a real product, so the part runs at the
- * clock its power limit sets for such work); mix = 1 adds one v_exp_f32 and
- * one FMA per MFMA (the vector work of the attention's softmax).  Work:
- * 32768 * 8 * iters * 8 * workgroups FLOP.  out: device float [512 *
- * workgroups], caller-owned, receives values that only keep the work live.
- * The caller times the launch (events on the stream).  Errors:
- * H3ATTN_ERR_INVALID_ARG for mix not 0/1, workgroups or iters outside
- * [1, 2^20], out NULL or not 4-byte aligned; H3ATTN_ERR_DEVICE; H3ATTN_ERR_HIP.
+ * Diagnostic, not part of the attention path: the sustained matrix-core rate
+ * of the current device, a measured ceiling beside the datasheet peak for
+ * the roofline of the attention kernels.  Launches `workgroups` workgroups of
+ * 512 threads on `stream`; every wave runs iters x 8 MFMAs on register
+ * operands that change from instruction to instruction (hashed values, like a
+ * real product, so the part runs at the clock its power limit sets for such
+ * work).  mix 0: v_mfma_f32_32x32x16_bf16 alone; mix 1: the same with one
+ * v_exp_f32 and one FMA per MFMA (the vector work of the bf16 attention's
+ * softmax); mix 2: v_mfma_i32_32x32x32_i8 alone; mix 3: the same with two
+ * FMAs, two v_exp_f32, one v_cvt_pk_fp8_f32 and one v_max3_f32 per MFMA (the
+ * quantised attention's vector work per 32 matrix-core cycles).  Work:
+ * 32768 (mix 0, 1) or 65536 (mix 2, 3) * 8 * iters * 8 * workgroups
+ * operations.  out: device float [512 * workgroups], caller-owned, receives
+ * values that only keep the work live.  The caller times the launch (events
+ * on the stream).  Errors: H3ATTN_ERR_INVALID_ARG for mix outside 0..3,
+ * workgroups or iters outside [1, 2^20], out NULL or not 4-byte aligned;
+ * H3ATTN_ERR_DEVICE; H3ATTN_ERR_HIP.
  */
 h3attn_status h3attn_mfma_ceiling(int mix, int workgroups, int iters, float *out, void *stream);
 
