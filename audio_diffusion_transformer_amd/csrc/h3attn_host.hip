@@ -423,7 +423,7 @@ h3attn_status h3attn_fwd_static(const h3attn_params *p, const void *q, const voi
 
 h3attn_status h3attn_mfma_ceiling(int mix, int workgroups, int iters, float *out, void *stream)
 {
-    if (mix < 0 || mix > 3) return fail(H3ATTN_ERR_INVALID_ARG, "mix must be 0, 1, 2 or 3 (got %d)", mix);
+    if (mix < 0 || mix > 5) return fail(H3ATTN_ERR_INVALID_ARG, "mix must be in 0..5 (got %d)", mix);
     if (workgroups < 1 || workgroups > (1 << 20))
         return fail(H3ATTN_ERR_INVALID_ARG, "workgroups must be in [1, 2^20] (got %d)", workgroups);
     if (iters < 1 || iters > (1 << 20)) return fail(H3ATTN_ERR_INVALID_ARG, "iters must be in [1, 2^20] (got %d)", iters);

@@ -4,7 +4,7 @@
 // fragments of hashed values), alone or with vector work beside them.  Under
 // a sustained load the engine clock settles where the part's power limit
 // puts it for this kind of work, so the measured rate, not the datasheet
-// figure, is what a dense kernel can reach on the box.  Four mixes:
+// figure, is what a dense kernel can reach on the box.  Six mixes:
 //   0  v_mfma_f32_32x32x16_bf16 alone;
 //   1  the same with one v_exp_f32 and one FMA per MFMA (the vector work the
 //      bf16 attention's softmax adds per MFMA);
@@ -13,9 +13,15 @@
 //      cycles: two FMAs, two v_exp_f32, one v_cvt_pk_fp8_f32 and one
 //      v_max3_f32 (per 64-key tile and wave that kernel issues 544 cycles of
 //      MFMA beside 32 FMAs, 32 exp2, 16 FP8 packs and the tile maximum), on
-//      eight independent chains.
-// Mix 3 against mix 2 shows how far the vector work of the quantised path
-// can hide under its matrix-core time on one SIMD.
+//      eight independent chains;
+//   4  v_mfma_scale_f32_32x32x64_f8f6f4 on e2m1 (FP4) operands alone;
+//   5  the same with the MXFP4 attention's vector work per 32 matrix-core
+//      cycles: four v_exp_f32, two v_cvt_scalef32_pk_fp4_f32, two v_max3_f32
+//      and one FMA (per 64-key tile and wave that kernel issues 272 cycles of
+//      MFMA beside 32 exp2, 16 FP4 packs, the tile maximum and the block
+//      scale).
+// Mix 3 against mix 2 (5 against 4) shows how far the vector work of the
+// quantised (MXFP4) path can hide under its matrix-core time on one SIMD.
 #include "h3_internal.h"
 
 namespace h3 {
@@ -23,6 +29,7 @@ namespace h3 {
 typedef __bf16 bf16x8c __attribute__((ext_vector_type(8)));
 typedef float f32x16c __attribute__((ext_vector_type(16)));
 typedef int i32x4c __attribute__((ext_vector_type(4)));
+typedef int i32x8c __attribute__((ext_vector_type(8)));
 typedef int i32x16c __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float mix_hash(unsigned x)
@@ -108,6 +115,52 @@ __global__ __launch_bounds__(512) void mfma_ceiling_i8_kernel(float *out, int it
     out[t] = s;
 }
 
+template <bool MIX>
+__global__ __launch_bounds__(512) void mfma_ceiling_fp4_kernel(float *out, int iters, float cs)
+{
+    i32x8c A[8], B[8];
+    const unsigned t = blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // e2m1 codes: every nibble is a finite value; registers 4..7 are not read
+            A[j][i] = i < 4 ? (int)(t * 2654435761u + 97u * j + 13u * i) : 0;
+            B[j][i] = i < 4 ? (int)((t + 7777u) * 40503u + 31u * j + 29u * i) : 0;
+        }
+    f32x16c acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = (f32x16c){};
+    float x[8], mx0 = 0.f, mx1 = 0.f, y = 0.f;
+    uint32_t w = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = 0.5f + 0.01f * k;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            acc[j & 3] =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[j], B[(3 * j + 1) & 7], acc[j & 3], 4, 4, 0, 127u, 0, 127u);
+            if (MIX) {
+                // x -> 2^-x stays near its fixed point 0.64, so the chains stay finite
+                const int k = (4 * j) & 7;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[k + i] = __builtin_amdgcn_exp2f(-x[k + i]);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k], x[k + 1], cs, 0);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[k + 2], x[k + 3], cs, 1);
+                mx0 = fmaxf(fmaxf(mx0, x[k]), x[k + 1]);
+                mx1 = fmaxf(fmaxf(mx1, x[k + 2]), x[k + 3]);
+                y = fmaf(y, cs, x[k]);
+            }
+        }
+    }
+    float s = mx0 + mx1 + y + (float)w;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += x[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s += acc[k][threadIdx.x & 15];
+    out[t] = s;
+}
+
 hipError_t launch_mfma_ceiling(int mix, int workgroups, int iters, float *out, hipStream_t st)
 {
     const dim3 g((unsigned)workgroups), b(512);
@@ -115,7 +168,9 @@ hipError_t launch_mfma_ceiling(int mix, int workgroups, int iters, float *out, h
     case 0: hipLaunchKernelGGL((mfma_ceiling_kernel<false>), g, b, 0, st, out, iters); break;
     case 1: hipLaunchKernelGGL((mfma_ceiling_kernel<true>), g, b, 0, st, out, iters); break;
     case 2: hipLaunchKernelGGL((mfma_ceiling_i8_kernel<false>), g, b, 0, st, out, iters, 0.999f, -0.001f); break;
-    default: hipLaunchKernelGGL((mfma_ceiling_i8_kernel<true>), g, b, 0, st, out, iters, 0.999f, -0.001f); break;
+    case 3: hipLaunchKernelGGL((mfma_ceiling_i8_kernel<true>), g, b, 0, st, out, iters, 0.999f, -0.001f); break;
+    case 4: hipLaunchKernelGGL((mfma_ceiling_fp4_kernel<false>), g, b, 0, st, out, iters, 1.0f); break;
+    default: hipLaunchKernelGGL((mfma_ceiling_fp4_kernel<true>), g, b, 0, st, out, iters, 1.0f); break;
     }
     return hipGetLastError();
 }

@@ -106,14 +106,15 @@ def device_copy_rate(torch, dev, mib: int = 1024, reps: int = 5) -> float:
     return 2.0 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
-def mfma_ceiling(torch, h, dev, stream, quantized: bool = False, target_ms: float = 120.0):
+def mfma_ceiling(torch, h, dev, stream, path: str = "bf16", target_ms: float = 120.0):
     """Sustained matrix-core rate of this device (h3attn_mfma_ceiling):
     register-only MFMA streams on changing operands on all 256 CUs, alone and
     with the vector work the attention adds beside its MFMAs.  bf16 (mixes 0,
     1): v_mfma_f32_32x32x16_bf16, then with one v_exp_f32 + one FMA per MFMA.
     Quantised (mixes 2, 3): v_mfma_i32_32x32x32_i8, then with two FMAs, two
     v_exp_f32, one FP8 pack and one max per MFMA (the quantised kernel's
-    ratio).  Each launch runs ~target_ms, long enough for the clock to settle
+    ratio).  MXFP4 (mixes 4, 5): the scaled FP4 MFMA, then with four v_exp_f32,
+    two FP4 packs, two max3 and one FMA per MFMA.  Each launch runs ~target_ms, long enough for the clock to settle
     where the power limit holds it; one warm-up launch, then two timed.
     Returns the rates (TFLOP/s or TOP/s) of both mixes (after the timed region)."""
     wg = 256
@@ -131,12 +132,11 @@ def mfma_ceiling(torch, h, dev, stream, quantized: bool = False, target_ms: floa
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    if quantized:
-        mixes = ((2, "int8_mfma_only_TOPs"), (3, "int8_mfma_with_q8_vector_work_TOPs"))
-        ops_per_mfma = 65536.0
-    else:
-        mixes = ((0, "mfma_only_TFLOPs"), (1, "mfma_with_exp_fma_TFLOPs"))
-        ops_per_mfma = 32768.0
+    mixes, ops_per_mfma = {
+        "bf16": (((0, "mfma_only_TFLOPs"), (1, "mfma_with_exp_fma_TFLOPs")), 32768.0),
+        "q8": (((2, "int8_mfma_only_TOPs"), (3, "int8_mfma_with_q8_vector_work_TOPs")), 65536.0),
+        "mx": (((4, "fp4_mfma_only_TFLOPs"), (5, "fp4_mfma_with_mx_vector_work_TFLOPs")), 131072.0),
+    }[path]
     flop_per_iter = ops_per_mfma * 8 * 8 * wg
     res = {}
     for mix, key in mixes:
@@ -496,7 +496,7 @@ def main():
     sel_avg = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])) if sparse else 0.0
     step_ms = [ev[i][0].elapsed_time(ev[i][nst]) for i in range(K)]
     copy_gbps = device_copy_rate(torch, dev)        # after the timed region
-    ceiling = mfma_ceiling(torch, h, dev, stream, quantized=w.quantized) if not w.fp4 else None
+    ceiling = mfma_ceiling(torch, h, dev, stream, path="mx" if w.fp4 else "q8" if w.quantized else "bf16")
     print("[bench] %d steps: %.3f ms/step (attention %.3f, %s %.3f), wall %.3f s" % (
         K, ms_step, att_avg, "projection" if proj else "prologue", pro_avg, wall), file=sys.stderr, flush=True)
     unfused = library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream) if proj else None

@@ -395,11 +395,14 @@ int h3attn_version(void);
  * v_exp_f32 and one FMA per MFMA (the vector work of the bf16 attention's
  * softmax); mix 2: v_mfma_i32_32x32x32_i8 alone; mix 3: the same with two
  * FMAs, two v_exp_f32, one v_cvt_pk_fp8_f32 and one v_max3_f32 per MFMA (the
- * quantised attention's vector work per 32 matrix-core cycles).  Work:
- * 32768 (mix 0, 1) or 65536 (mix 2, 3) * 8 * iters * 8 * workgroups
- * operations.  out: device float [512 * workgroups], caller-owned, receives
+ * quantised attention's vector work per 32 matrix-core cycles); mix 4:
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on e2m1 operands alone; mix 5: the same
+ * with four v_exp_f32, two v_cvt_scalef32_pk_fp4_f32, two v_max3_f32 and one
+ * FMA per MFMA (the MXFP4 attention's vector work per 32 matrix-core
+ * cycles).  Work: 32768 (mix 0, 1), 65536 (mix 2, 3) or 131072 (mix 4, 5)
+ * * 8 * iters * 8 * workgroups operations.  out: device float [512 * workgroups], caller-owned, receives
  * values that only keep the work live.  The caller times the launch (events
- * on the stream).  Errors: H3ATTN_ERR_INVALID_ARG for mix outside 0..3,
+ * on the stream).  Errors: H3ATTN_ERR_INVALID_ARG for mix outside 0..5,
  * workgroups or iters outside [1, 2^20], out NULL or not 4-byte aligned;
  * H3ATTN_ERR_DEVICE; H3ATTN_ERR_HIP.
  */

@@ -451,7 +451,7 @@ def test_static_workspace_entry_point_injected_failure(monkeypatch):
 
 
 def test_mfma_ceiling_argument_errors(monkeypatch):
-    for args, msg in [((4, 256, 10), "mix"), ((-1, 256, 10), "mix"), ((0, 0, 10), "workgroups"), ((0, 1 << 21, 10), "workgroups"),
+    for args, msg in [((6, 256, 10), "mix"), ((-1, 256, 10), "mix"), ((0, 0, 10), "workgroups"), ((0, 1 << 21, 10), "workgroups"),
                       ((0, 256, 0), "iters"), ((1, 256, 1 << 21), "iters")]:
         assert h.mfma_ceiling_raw(*args, FAKE, None) == h.H3ATTN_ERR_INVALID_ARG
         assert msg in h.last_error()
