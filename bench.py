@@ -391,7 +391,7 @@ def main():
                          "(reference kernel for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
 
