@@ -110,3 +110,20 @@ def test_side_stream_without_workspace(torch_dev, quantized):
     torch.cuda.synchronize()
     del junk
     assert np.array_equal(G.bits(o), want)
+
+
+@pytest.mark.parametrize("mix", range(6))
+def test_mfma_ceiling_mixes_run(torch_dev, mix):
+    """The matrix-core ceiling diagnostic (every mix: bf16, INT8 and FP4
+    MFMAs, alone and with each path's vector work) runs on a small grid and
+    leaves only finite values: its hashed operands and vector chains stay in
+    range, so the measured rates come from well-defined arithmetic."""
+    torch = torch_dev
+    wg = 3
+    out = torch.full((512 * wg,), float("nan"), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    G.announce("mfma_ceiling mix=%d workgroups=%d" % (mix, wg))
+    st = h.mfma_ceiling_raw(mix, wg, 50, out.data_ptr(), int(stream.cuda_stream))
+    assert st == 0, h.last_error()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
