@@ -71,10 +71,12 @@ __device__ __forceinline__ int lane_here()
     return l;
 }
 
-// Eight values -> eight e2m1 codes of x / scale (value i in nibble i).
+// Eight values -> eight e2m1 codes of x / scale (value i in nibble i).  The
+// four conversions write the word's four bytes, so its starting value is
+// never read; passing a dead input avoids materialising a zero.
 __device__ __forceinline__ uint32_t fp4x8(const float *y, float scale)
 {
-    uint32_t w = 0u;
+    uint32_t w = __float_as_uint(y[0]);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], scale, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], scale, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);
