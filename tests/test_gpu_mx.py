@@ -176,9 +176,11 @@ def test_mx_attention_matches_stepwise_emulation(torch_dev, name):
     G.check(m, G.MX_EMULATION_GATE, name + " vs emulation")
 
 
-@pytest.mark.parametrize("name", ["mx", "joint_mx"])
+@pytest.mark.parametrize("name", ["mx", "joint_mx", "ragged_mx"])
 def test_mx_attention_full_size_sampled(torch_dev, name):
-    w = synth.WORKLOADS["mx"] if name == "mx" else synth.WORKLOADS["joint"].replace(name="joint_mx", fp4=True)
+    w = {"mx": lambda: synth.WORKLOADS["mx"],
+         "joint_mx": lambda: synth.WORKLOADS["joint"].replace(name="joint_mx", fp4=True),
+         "ragged_mx": lambda: synth.WORKLOADS["ragged"].replace(name="ragged_mx", fp4=True)}[name]()
     inp = synth.generate(w)
     t = G.to_device(inp, w)
     out = G.bits(G.run(w, t, quantized="mx", label=name))

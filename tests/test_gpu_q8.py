@@ -101,10 +101,14 @@ def test_quantised_attention_all_rows(torch_dev, name):
     G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.Q8_GATE, name)
 
 
-@pytest.mark.parametrize("name", ["q8", "joint_q8"])
+@pytest.mark.parametrize("name", ["q8", "joint_q8", "ragged_q8"])
 def test_quantised_attention_full_size_sampled(torch_dev, name):
-    w = synth.WORKLOADS["q8"] if name == "q8" else synth.WORKLOADS["joint"].replace(
-        name="joint_q8", quantized=True)
+    """Sampled rows at full size: the 58k-token video shape, the 125k joint
+    shape, and the three-sequence ragged batch (per-sequence K means, V scales
+    and query blocks that end mid-tile in every sequence)."""
+    w = {"q8": lambda: synth.WORKLOADS["q8"],
+         "joint_q8": lambda: synth.WORKLOADS["joint"].replace(name="joint_q8", quantized=True),
+         "ragged_q8": lambda: synth.WORKLOADS["ragged"].replace(name="ragged_q8", quantized=True)}[name]()
     inp = synth.generate(w)
     t = G.to_device(inp, w)
     out = G.bits(G.run(w, t, quantized=True, label=name))
