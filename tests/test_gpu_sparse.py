@@ -159,3 +159,46 @@ def test_full_size_two_heads(torch_dev):
     tok, j = rows // len(heads), rows % len(heads)
     gotr = G.decode(got[tok, np.array(heads)[j]])
     G.check(G.metrics(gotr, ref), G.BF16_GATE, "sparse_joint sampled")
+
+
+def test_full_size_ragged_two_heads(torch_dev):
+    """The three-sequence ragged batch at full size (18,144 + 45,250 + 7,200
+    tokens) with 177 tiles kept per block, so the last sequence keeps all of
+    its 113 tiles: the GPU selection of two heads against the oracle's, then
+    sampled rows of agreeing blocks against the oracle's softmax over the
+    kept keys."""
+    w = synth.WORKLOADS["ragged"].replace(name="sparse_ragged_full", keep_tiles=177)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    got, lists = _run_sparse(torch_dev, w, t, w.keep_tiles, select=True, label=w.name)
+    del t
+    heads = [5, 19]
+    sub = {key: np.ascontiguousarray(inp[key][:, heads]) for key in ("q", "k", "v")}
+    sub["norm_w"] = np.ascontiguousarray(inp["norm_w"][:, heads])
+    ws = w.replace(H=len(heads))
+    p = oracle.Problem.from_workload(ws, sub)
+    ref_lists, scores = p.sparse_select(w.keep_tiles)
+    # the GPU's list rows run sequence by sequence, then over all H heads, then 128-row block
+    gpu_rows, base = [], 0
+    for s in w.seqs:
+        nqb = (s.n + 127) // 128
+        for hh in heads:
+            gpu_rows += list(range(base + hh * nqb, base + (hh + 1) * nqb))
+        base += w.H * nqb
+    gl = lists[np.array(gpu_rows)]
+    same = _compare_selection(gl, ref_lists, scores, w.name)
+    items = p.sparse_items()                  # (sequence, head of the two, block), the order of gl
+    rng = np.random.default_rng(13)
+    pick = np.sort(rng.choice(np.nonzero(same)[0], 96, replace=False))
+    rows = []
+    for i in pick:
+        s, j, qb = items[int(i)]
+        lo = int(p.cu[s]) + 128 * qb
+        hi = min(lo + 128, int(p.cu[s + 1]))
+        toks = rng.choice(np.arange(lo, hi), min(8, hi - lo), replace=False)
+        rows += [int(tk) * len(heads) + j for tk in toks]
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ref = p.sparse_attention_rows(rows, ref_lists, w.keep_tiles, nthreads=G.oracle_threads())
+    tok, j = rows // len(heads), rows % len(heads)
+    gotr = G.decode(got[tok, np.array(heads)[j]])
+    G.check(G.metrics(gotr, ref), G.BF16_GATE, w.name + " sampled")
