@@ -8,9 +8,9 @@
 // the softmax over the keys of its own sequence tile by tile (an online
 // softmax), never materialising the N x N score matrix.
 //
-// Two kernels.  attn_bf16_pp_kernel runs dense attention at head_dim 128
+// Two kernels.  attn_bf16_pp_kernel runs head_dim 128, dense and block-sparse
 // (eight waves, 256 query rows per workgroup, its own notes further down);
-// attn_bf16_kernel runs head_dim 64 and the block-sparse path, and the notes
+// attn_bf16_kernel runs head_dim 64, dense and block-sparse, and the notes
 // here describe it.  Both share the matrix-core layout and the softmax below.
 //
 // Work decomposition.  One workgroup = 4 waves = 128 query rows of one
@@ -112,10 +112,11 @@ __device__ __forceinline__ int xcd_window_item(int b, int n)
     return b - r + (r % X) * C + r / X;
 }
 
-// SPARSE: visit only the 64-key tiles listed for this query block (block-sparse
-// attention, a.tiles); otherwise every tile of the sequence.  Sparse work items
-// are numbered by xcd_window_item: neighbouring query blocks keep most of the
-// same tiles, so running them on one XCD lets its L2 serve the shared tiles.
+// SPARSE: visit only the 64-key tiles listed for this query block's
+// kSparseBlockM-row block (block-sparse attention, a.tiles; the two 128-row
+// halves of a block read the same list); otherwise every tile of the sequence.
+// Sparse work items are numbered by xcd_window_item, so the halves of a block
+// and neighbouring blocks run on one XCD and share the tiles its L2 holds.
 template <int D, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 {
@@ -159,8 +160,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     if constexpr (SPARSE) {
         // the list, clamped to the sequence's tiles, goes to LDS; each visit
         // reads its entry back as a wave-uniform scalar
+        constexpr int R = kSparseBlockM / kBlockM;   // work items per list
         nt = min(a.tpb, ntk);
-        const int32_t *lst = a.tiles + ((int64_t)a.seq_item_base[si] + (int64_t)head * nqb + qb) * a.tpb;
+        const int32_t *lst =
+            a.tiles + ((int64_t)a.seq_item_base[si] + (int64_t)head * ((nqb + R - 1) / R) + qb / R) * a.tpb;
         for (int i = threadIdx.x; i < nt; i += 256) ltiles[i] = min(max(lst[i], 0), ntk - 1);
         __syncthreads();
     }
@@ -408,10 +411,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
 // Explicit instantiations (the host pass emits launch stubs only for these).
 template __global__ void attn_bf16_kernel<64, false>(AttnArgs);
 template __global__ void attn_bf16_kernel<64, true>(AttnArgs);
-template __global__ void attn_bf16_kernel<128, true>(AttnArgs);
 
 // ---------------------------------------------------------------------------
-// Dense attention at head_dim 128: two groups of four waves per workgroup.
+// Attention at head_dim 128: two groups of four waves per workgroup.  SPARSE
+// visits only the tiles of the block's list (block-sparse attention: one list
+// per 256-row block, read into LDS at the start; every fill takes its tile
+// index from it); otherwise every tile of the sequence.
 //
 // Work item: (sequence, head, 256-row query block).  Waves 0-3 form group 0
 // and waves 4-7 group 1, 32 query rows each; the dispatcher places wave w and
@@ -444,7 +449,7 @@ template __global__ void attn_bf16_kernel<128, true>(AttnArgs);
 // the same P.V accumulation order.
 static_assert(kBlockM2 == 8 * 32, "eight waves of 32 query rows");
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
 {
     static_assert(D == 128, "tile fills assume 16 KB K and V^T tiles");
@@ -456,6 +461,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     static_assert(NQK == 16 && NPV == 16, "one exp2 pair per MFMA slot below");
     __shared__ __attribute__((aligned(16))) uint16_t lk0[kTile * D], lk1[kTile * D], lk2[kTile * D];
     __shared__ __attribute__((aligned(16))) uint16_t lv0[D * kTile], lv1[D * kTile], lv2[D * kTile];
+    __shared__ int32_t ltiles[SPARSE ? kMaxSparseTiles : 1];     // the block's tile list
 
     // ---- work item: (sequence, head, 256-row query block)
     const int b = blockIdx.x;
@@ -482,12 +488,28 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
 
     const uint16_t *kbase = a.khat + ((int64_t)head * a.Npad + off) * D;
     const uint16_t *vbase = a.vt + ((int64_t)head * (a.Npad / kTile) + off / kTile) * (D * kTile);
-    const int nt = (n + kTile - 1) / kTile;
+    const int ntk = (n + kTile - 1) / kTile;           // tiles of the sequence
+    int nt = ntk;                                     // tiles this block visits
+    if constexpr (SPARSE) {
+        // the list, clamped to the sequence's tiles, goes to LDS; each visit
+        // reads its entry back as a wave-uniform scalar
+        nt = min(a.tpb, ntk);
+        const int32_t *lst = a.tiles + ((int64_t)a.seq_item_base[si] + (int64_t)head * nqb + qb) * a.tpb;
+        for (int i = tid; i < nt; i += 512) ltiles[i] = min(max(lst[i], 0), ntk - 1);
+        __syncthreads();
+    }
+    // Sequence tile of visit j (j < nt).
+    auto tix = [&](int j) -> int {
+        if constexpr (SPARSE)
+            return __builtin_amdgcn_readfirstlane(ltiles[j]);
+        else
+            return j;
+    };
     const int tbytes = kTile * D * 2;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(kbase), 0, nt * tbytes, kBufferFlags);
+        const_cast<uint16_t *>(kbase), 0, ntk * tbytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(vbase), 0, nt * tbytes, kBufferFlags);
+        const_cast<uint16_t *>(vbase), 0, ntk * tbytes, kBufferFlags);
     // group 0 fills K tiles, group 1 V^T tiles: four 1 KB pieces per wave
     uint32_t fgoff[4];
     {
@@ -500,12 +522,14 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
         for (int i = 0; i < 4; ++i) fgoff[i] = grp ? vf.goff[i] : kf.goff[i];
     }
     const __amdgpu_buffer_rsrc_t frs = grp ? vrs : krs;
+    // sequence tile t into dst
     auto fill = [&](__amdgpu_buffer_rsrc_t rs, int t, uint16_t *dst) {
+        const uint32_t toff = (uint32_t)(t * tbytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rs, (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(dst) + (gw * 4 + i) * 1024),
-                16, fgoff[i], (uint32_t)(t * tbytes), 0, 0);
+                16, fgoff[i], toff, 0, 0);
     };
 
     f32x16 o[DB];
@@ -517,7 +541,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float mb;
     const bool fixed_shift =
-        fixed_shift_bound(qf, a.knorm + (int64_t)head * (a.Npad / kTile) + off / kTile, nt, lane, mb);
+        fixed_shift_bound(qf, a.knorm + (int64_t)head * (a.Npad / kTile) + off / kTile, ntk, lane, mb);
     if (fixed_shift) {
         m_run = mb;
         ninit = -m_run;
@@ -546,11 +570,12 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(2 * st + 1, kl), qf[st], s1, 0, 0, 0);
         }
     };
-    // Tile j's row max (masking keys past the sequence end on the last tile);
-    // raise m_run when the tile exceeds it by more than kLazyRescale (always on
-    // the first tile), rescaling O and l and shifting the tile's x.
-    auto row_max_update = [&](int j, f32x16 &s0, f32x16 &s1) {
-        const int valid = n - j * kTile;
+    // Row max of the visit to sequence tile t (masking keys past the sequence
+    // end in its partial last tile, which a sparse list may hold at any
+    // position); raise m_run when the tile exceeds it by more than kLazyRescale
+    // (always on the first visit), rescaling O and l and shifting the tile's x.
+    auto row_max_update = [&](int t, f32x16 &s0, f32x16 &s1) {
+        const int valid = n - t * kTile;
         if (valid < kTile) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -653,12 +678,12 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     // wave's scores of tile 0, then a barrier before lk0 is refilled
     __builtin_amdgcn_sched_barrier(0);
     if (grp == 0) {
-        fill(krs, 0, lk0);
-        if (nt > 1) fill(krs, 1, lk1);
-        if (nt > 2) fill(krs, 2, lk2);
+        fill(krs, tix(0), lk0);
+        if (nt > 1) fill(krs, tix(1), lk1);
+        if (nt > 2) fill(krs, tix(2), lk2);
     } else {
-        fill(vrs, 0, lv0);
-        if (nt > 1) fill(vrs, 1, lv1);
+        fill(vrs, tix(0), lv0);
+        if (nt > 1) fill(vrs, tix(1), lv1);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -675,8 +700,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     // kf = lk[j%3] and vf = lv[(j+2)%3] (this tile's fills).
     auto tile = [&](int j, const uint16_t *kn, const uint16_t *vc, const uint16_t *kn2, uint16_t *kf, uint16_t *vf,
                     f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1) {
-        if (j + 3 - grp < nt) fill(frs, j + 3 - grp, grp ? vf : kf);
-        row_max_update(j, c0, c1);
+        if (j + 3 - grp < nt) fill(frs, tix(j + 3 - grp), grp ? vf : kf);
+        row_max_update(tix(j), c0, c1);
         phase_s(kn, vc, c0, n0, n1, pre);
         end_s();
         phase_p(vc, kn2, c1, pre);
@@ -715,7 +740,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     }
 }
 
-template __global__ void attn_bf16_pp_kernel<128>(AttnArgs);
+template __global__ void attn_bf16_pp_kernel<128, false>(AttnArgs);
+template __global__ void attn_bf16_pp_kernel<128, true>(AttnArgs);
 
 // Dense attention at head_dim 128 runs attn_bf16_pp_kernel over 256-row query
 // blocks; head_dim 64 and the block-sparse path run attn_bf16_kernel over
@@ -726,12 +752,12 @@ hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_
     const dim3 grid((unsigned)nitems);
     if (a.tiles) {
         if (d == 128)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((attn_bf16_pp_kernel<128, true>), grid, dim3(512), 0, st, a);
         else
             hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, dim3(256), 0, st, a);
     } else {
         if (d == 128)
-            hipLaunchKernelGGL((attn_bf16_pp_kernel<128>), grid, dim3(512), 0, st, a);
+            hipLaunchKernelGGL((attn_bf16_pp_kernel<128, false>), grid, dim3(512), 0, st, a);
         else
             hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, dim3(256), 0, st, a);
     }

@@ -90,11 +90,14 @@ struct AttnArgs {
 // Longest tile list (and longest sequence, in 64-key tiles) of the
 // block-sparse path.
 constexpr int kMaxSparseTiles = 2048;
+// Query rows sharing one block-sparse tile list: the workgroup of the head_dim
+// 128 attention kernel, so each workgroup streams exactly one list.
+constexpr int kSparseBlockM = 256;
 
 // Block-sparse tile selection (sparse_select.hip).  From the prologue's qhat'
 // and khat in the workspace: per (head, padded 64-token tile) the mean khat row
 // (kbar) and the sum of qhat' rows (qsum), and per tile its valid row count;
-// then per (sequence, head, 128-row query block) the tpb tiles with the
+// then per (sequence, head, kSparseBlockM-row query block) the tpb tiles with the
 // largest qbar . kbar, written ascending to tiles [items][tpb] (-1 past
 // min(tpb, tiles of the sequence)).
 struct SparseSelectArgs {
@@ -277,7 +280,9 @@ constexpr int kBlockM = 128;
 // multiple of it, so its query blocks stay inside the sequence's rows.
 constexpr int kBlockM2 = 256;
 static_assert(kSeqPad % kBlockM2 == 0, "query blocks stay within a padded sequence");
-// Rows per work item launch_attn_bf16 expects for (head_dim, block-sparse).
-inline int attn_bf16_block_m(int d, bool sparse) { return d == 128 && !sparse ? kBlockM2 : kBlockM; }
+static_assert(kSparseBlockM == kBlockM2 && kSparseBlockM % kBlockM == 0, "a sparse block is one 8-wave workgroup");
+// Rows per work item launch_attn_bf16 expects at head_dim d (dense and
+// block-sparse alike: the 8-wave kernel at 128, the 4-wave kernel at 64).
+inline int attn_bf16_block_m(int d) { return d == 128 ? kBlockM2 : kBlockM; }
 
 }  // namespace h3

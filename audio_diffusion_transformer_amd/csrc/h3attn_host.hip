@@ -348,7 +348,7 @@ h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const voi
     aa.o_stride = p->o_stride;
     aa.Npad = pl.Npad;
     aa.H = pl.H;
-    const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d, false));
+    const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d));
     return launch_status(hs, "attention launch", [&] { return launch_attn_bf16(aa, pl.d, items, hs); });
 }
 
@@ -546,7 +546,7 @@ h3attn_status h3attn_fwd_proj_stages(const h3attn_params *p, int32_t model_dim, 
     aa.o_stride = p->o_stride;
     aa.Npad = pl.Npad;
     aa.H = pl.H;
-    const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d, false));
+    const int64_t items = order_work(pl, aa, nullptr, attn_bf16_block_m(pl.d));
     return launch_status(hs, "attention launch", [&] { return launch_attn_bf16(aa, pl.d, items, hs); });
 }
 
@@ -656,14 +656,17 @@ h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model
             [&] { return launch_out_proj(a, static_cast<hipStream_t>(stream)); });
 }
 
+// Query blocks (tile lists) of a sequence of n tokens on the block-sparse path.
+static int64_t sparse_blocks(int64_t n) { return (n + kSparseBlockM - 1) / kSparseBlockM; }
+
 // Caller-order item bases of the block-sparse lists: items run sequence by
-// sequence, then head, then 128-row query block.
+// sequence, then head, then kSparseBlockM-row query block.
 static void sparse_item_base(const Plan &pl, int32_t *base, int64_t *total)
 {
     int64_t at = 0;
     for (int s = 0; s < pl.S; ++s) {
         base[s] = (int32_t)at;
-        at += (int64_t)pl.H * ((pl.cu[s + 1] - pl.cu[s] + 127) / 128);
+        at += (int64_t)pl.H * sparse_blocks(pl.cu[s + 1] - pl.cu[s]);
     }
     *total = at;
 }
@@ -731,7 +734,7 @@ h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, co
         for (int s = 0; s < pl.S; ++s) {
             sa.item_base[s] = base[s];
             sa.group_pre[s] = (int32_t)g;
-            g += (int64_t)pl.H * (((pl.cu[s + 1] - pl.cu[s] + 127) / 128 + 3) / 4);
+            g += (int64_t)pl.H * ((sparse_blocks(pl.cu[s + 1] - pl.cu[s]) + 3) / 4);
         }
         sa.group_pre[pl.S] = (int32_t)g;
         if ((st = launch_status(hs, "sparse selection launch",
@@ -751,7 +754,7 @@ h3attn_status h3attn_fwd_sparse_stages(const h3attn_params *p, const void *q, co
     aa.Npad = pl.Npad;
     aa.H = pl.H;
     int32_t seq_idx[kMaxSeqs];
-    const int64_t items = order_work(pl, aa, seq_idx, attn_bf16_block_m(pl.d, true));
+    const int64_t items = order_work(pl, aa, seq_idx, attn_bf16_block_m(pl.d));
     aa.tiles = block_tiles;
     aa.tpb = tiles_per_block;
     for (int i = 0; i < aa.nseq; ++i) aa.seq_item_base[i] = base[seq_idx[i]];

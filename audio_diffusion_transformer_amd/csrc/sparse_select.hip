@@ -1,5 +1,6 @@
-// Block-sparse tile selection for gfx950: which 64-key tiles each 128-row
-// query block attends to.
+// Block-sparse tile selection for gfx950: which 64-key tiles each 256-row
+// query block (kSparseBlockM rows, one workgroup of the attention kernel)
+// attends to.
 //
 // The page "Open-H3-Regenerate-2K" ("Speed on one B200 (GB200)", per-module
 // table) credits a sparse attention backend with most of a refine's speed-up
@@ -14,11 +15,12 @@
 // reads; padding rows are zeros) and stores the khat mean (channel-major) and
 // the qhat' sum.
 // Pass 2 (sparse_select_kernel): one workgroup per (sequence, head, group of 4
-// query blocks) forms the 4 query means, scores every tile of the sequence
-// (each kbar value read once for the 4 blocks), finds each block's L-th
-// largest score by a radix select over order-preserving keys (four 8-bit
-// histogram passes in LDS), and writes the kept tiles in tile order through a
-// workgroup prefix sum (ties at the threshold go to the lower tiles).
+// query blocks) forms the 4 query means (each over the block's four tiles),
+// scores every tile of the sequence (each kbar value read once for the 4
+// blocks), finds each block's L-th largest score by a radix select over
+// order-preserving keys (four 8-bit histogram passes in LDS), and writes the
+// kept tiles in tile order through a workgroup prefix sum (ties at the
+// threshold go to the lower tiles).
 #include "h3_internal.h"
 #include "norm_rope.h"
 
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a)
     int s = 0;
     while (s + 1 < a.seq.S && b >= a.group_pre[s + 1]) ++s;
     const int n = a.seq.cu[s + 1] - a.seq.cu[s];
-    const int nqb = (n + 127) / 128, ntk = (n + kTile - 1) / kTile;
+    const int nqb = (n + kSparseBlockM - 1) / kSparseBlockM, ntk = (n + kTile - 1) / kTile;
     const int ng = (nqb + kSelectGroup - 1) / kSelectGroup;
     const int rem = b - a.group_pre[s];
     const int h = rem / ng, g = rem % ng;
@@ -95,15 +97,23 @@ __global__ __launch_bounds__(256) void sparse_select_kernel(SparseSelectArgs a)
     const int t0 = a.seq.off[s] / kTile;                    // the sequence's first padded tile
     const int tid = threadIdx.x;
 
-    // ---- query block means (two 64-token tiles each)
+    // ---- query block means (TPB 64-token tiles each; the padded sequence
+    // holds whole blocks, so every one of them exists)
+    constexpr int TPB = kSparseBlockM / kTile;
     for (int i = tid; i < kSelectGroup * D; i += 256) {
         const int jq = i / D, c = i % D;
         float v = 0.f;
         if (jq < nq) {
-            const int t = t0 + 2 * (kSelectGroup * g + jq);
+            const int t = t0 + TPB * (kSelectGroup * g + jq);
             const int64_t o = ((int64_t)h * a.ntiles + t) * D + c;
-            const int cnt = a.cnt[t] + a.cnt[t + 1];
-            v = (a.qsum[o] + a.qsum[o + D]) / (float)max(cnt, 1);
+            int cnt = 0;
+            float sum = 0.f;
+#pragma unroll
+            for (int u = 0; u < TPB; ++u) {
+                cnt += a.cnt[t + u];
+                sum += a.qsum[o + (int64_t)u * D];
+            }
+            v = sum / (float)max(cnt, 1);
         }
         qv[jq][c] = v;
     }

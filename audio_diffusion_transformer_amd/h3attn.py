@@ -25,7 +25,9 @@ H3ATTN_ERR_WORKSPACE = 3
 H3ATTN_ERR_DEVICE = 4
 H3ATTN_ERR_HIP = 5
 H3ATTN_MAX_SEQS = 64
+H3ATTN_VERSION = 2                 # the ABI version of include/h3attn.h this binding follows
 H3ATTN_STATIC_WORKSPACE_BYTES = 128 << 20
+SPARSE_BLOCK_ROWS = 256            # query rows per block-sparse tile list
 
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
             "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
@@ -106,6 +108,12 @@ def lib():
         L.h3attn_status_string.argtypes = [C.c_int]
         L.h3attn_last_error.restype = C.c_char_p
         L.h3attn_version.restype = C.c_int
+        got = int(L.h3attn_version())
+        if got != H3ATTN_VERSION:
+            # the array layouts this binding allocates (tile lists, workspaces) are
+            # those of its own ABI version; another build would read and write past them
+            raise RuntimeError("%s reports ABI version %d; this binding is for version %d (rebuild with "
+                               "`python -m audio_diffusion_transformer_amd.build`)" % (LIB_PATH, got, H3ATTN_VERSION))
         _lib = L
     return _lib
 
@@ -349,9 +357,10 @@ def h3attn_proj_prologue(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: i
 
 
 def sparse_items(cu_seqlens, num_heads: int) -> int:
-    """Rows of the block-sparse tile lists: sum over sequences of H * ceil(n_s / 128)."""
+    """Rows of the block-sparse tile lists: sum over sequences of H * ceil(n_s / SPARSE_BLOCK_ROWS)."""
     cu = _cu_array(cu_seqlens)
-    return int(sum(num_heads * ((int(cu[s + 1] - cu[s]) + 127) // 128) for s in range(len(cu) - 1)))
+    B = SPARSE_BLOCK_ROWS
+    return int(sum(num_heads * ((int(cu[s + 1] - cu[s]) + B - 1) // B) for s in range(len(cu) - 1)))
 
 
 def sparse_raw(params, q, k, v, norm_w, rope_tables, cu_seqlens, tiles_per_block: int, block_tiles, out,

@@ -64,7 +64,7 @@ class Workload:
     fp4: bool = False                    # MXFP4 path (h3attn_fwd_mx)
     sharp: bool = False                  # diagnostic: per-token scale + larger weights
     model_dim: int = 0                   # D > 0: inputs are hidden states x [N, D] and W_qkv
-    keep_tiles: int = 0                  # > 0: block-sparse attention keeping this many 64-key tiles per 128-row block
+    keep_tiles: int = 0                  # > 0: block-sparse attention keeping this many 64-key tiles per 256-row block
     description: str = ""
 
     @property
@@ -130,7 +130,7 @@ WORKLOADS: Dict[str, Workload] = {
         "sparse_joint", H=24, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128,
         k_offset_std=0.5, seed=1003, keep_tiles=490,
         description="block-sparse attention on the joint 125,242-token sequence (the joint inputs), "
-                    "490 of its 1,957 64-key tiles (25%) kept per 128-row query block by pooled score"),
+                    "490 of its 1,957 64-key tiles (25%) kept per 256-row query block by pooled score"),
     "proj_tiny": Workload(
         "proj_tiny", H=2, d=64, seqs=(Seq(4, 8, 8),), split=(16, 24, 24), seed=1011, model_dim=128,
         description="QKV projection (D=128) + attention on the t4 x h8 x w8 grid, H=2, d=64"),

@@ -34,6 +34,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from audio_diffusion_transformer_amd.h3attn import SPARSE_BLOCK_ROWS  # noqa: E402  (no library load)
+
 MI355X_BF16_DENSE_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense, no sparsity)
 MI355X_FP8_DENSE_TFLOPS = 5033.2
 MI355X_FP4_DENSE_TFLOPS = 10066.4     # FP4 (and FP6) dense MFMA
@@ -179,12 +181,13 @@ def cpu_baseline_sparse(w, inputs, seconds: float, threads: int):
     keys_per_block = [int(np.minimum(64, n - 64 * tiles[qb, :min(w.keep_tiles, nt)].astype(np.int64)).sum())
                       for qb in range(tiles.shape[0])]
 
-    nqb = (n + 127) // 128
+    B = oracle.SPARSE_BLOCK
+    nqb = (n + B - 1) // B
 
     def run(nblocks):
         # whole query blocks: the kept keys' khat is formed once per block, as in a full run
         blocks = np.sort(rng.choice(nqb, size=nblocks, replace=False))
-        toks = np.concatenate([np.arange(128 * qb, min(128 * qb + 128, n)) for qb in blocks]).astype(np.int64)
+        toks = np.concatenate([np.arange(B * qb, min(B * qb + B, n)) for qb in blocks]).astype(np.int64)
         t1 = time.perf_counter()
         p.sparse_attention_rows(toks, tiles, w.keep_tiles, nthreads=threads)
         return time.perf_counter() - t1, toks
@@ -193,22 +196,22 @@ def cpu_baseline_sparse(w, inputs, seconds: float, threads: int):
     nb = int(max(1, min(nqb, seconds / max(t_probe, 1e-6))))
     t, toks = run(nb)
     nrows = len(toks)
-    flops = sum(4.0 * w.d * keys_per_block[int(tk) // 128] for tk in toks)
+    flops = sum(4.0 * w.d * keys_per_block[int(tk) // B] for tk in toks)
     t += sel_s * nrows / n                 # the head's selection, spread over its rows
     value = flops / t / 1e12
     return {
         "value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "cpu_model": cpu_model(),
         "extrapolated_full_s": round(sparse_total_flops_estimate(w, keys_per_block) / (value * 1e12), 1),
         "kind": "oracle",
-        "sample": "%d query rows (%d whole 128-row blocks) of head %d (of %d x %d rows), each over the keys of "
+        "sample": "%d query rows (%d whole %d-row blocks) of head %d (of %d x %d rows), each over the keys of "
                   "the %d tiles the oracle keeps for its block; fp64; the head's pooled-score selection (%.1f s) "
-                  "spread over its rows; %.1f s" % (nrows, nb, head, w.N, w.H, w.keep_tiles, sel_s, t),
+                  "spread over its rows; %.1f s" % (nrows, nb, B, head, w.N, w.H, w.keep_tiles, sel_s, t),
     }
 
 
 def sparse_total_flops_estimate(w, keys_per_block) -> float:
-    n = w.seqs[0].n
-    return float(sum(4.0 * w.d * min(128, n - 128 * qb) * k for qb, k in enumerate(keys_per_block))) * w.H
+    n, B = w.seqs[0].n, SPARSE_BLOCK_ROWS
+    return float(sum(4.0 * w.d * min(B, n - B * qb) * k for qb, k in enumerate(keys_per_block))) * w.H
 
 
 def cpu_baseline(w, inputs, seconds: float, threads: int):
@@ -322,8 +325,8 @@ def sparse_flops(w, tiles) -> float:
         nt = (n + 63) // 64
         L = min(w.keep_tiles, nt)
         for _ in range(w.H):
-            for qb in range((n + 127) // 128):
-                rows = min(128, n - 128 * qb)
+            for qb in range((n + SPARSE_BLOCK_ROWS - 1) // SPARSE_BLOCK_ROWS):
+                rows = min(SPARSE_BLOCK_ROWS, n - SPARSE_BLOCK_ROWS * qb)
                 kept = tiles[it, :L].astype(np.int64)
                 keys = np.minimum(64, n - 64 * kept).sum()
                 total += 4.0 * w.d * rows * float(keys)
@@ -543,7 +546,8 @@ def main():
             "attention TFLOP/s and %% of bf16 MFMA peak at N=%d packed tokens, H=%d, d=%d" % (N, H, d))
         if sparse:
             metric = ("block-sparse attention TFLOP/s of the computed (kept) work, %d of the 64-key tiles kept "
-                      "per 128-row query block, at N=%d packed tokens, H=%d, d=%d" % (w.keep_tiles, N, H, d))
+                      "per %d-row query block, at N=%d packed tokens, H=%d, d=%d" % (
+                          w.keep_tiles, SPARSE_BLOCK_ROWS, N, H, d))
     res = {
         "metric": metric,
         "value": round(value, 3),
@@ -589,7 +593,7 @@ def main():
             "kept_fraction": round(attn_flops / w.flops(), 4),
             "dense_attention_ms": round(dense_att, 4),
             "speedup_vs_dense_step": round((pro_avg + dense_att) / ms_step, 3)})
-        res["roofline"]["kernel"] = "attn_bf16_kernel<128, sparse>"
+        res["roofline"]["kernel"] = "attn_bf16_pp_kernel<128, sparse>"
         res["roofline"]["traffic"] = None
         res["config"]["keep_tiles"] = w.keep_tiles
     if proj:

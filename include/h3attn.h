@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_VERSION 1
+#define H3ATTN_VERSION 2   /* 2: block-sparse tile lists per 256-row query block (1: per 128 rows) */
 #define H3ATTN_MAX_SEQS 64      /* sequences per call */
 
 typedef enum h3attn_status {
@@ -323,14 +323,14 @@ h3attn_status h3attn_out_proj(int32_t num_heads, int32_t head_dim, int32_t model
                               void *out, int64_t out_stride, void *stream);
 
 /*
- * Block-sparse attention: each 128-row query block attends to a kept subset of
+ * Block-sparse attention: each 256-row query block attends to a kept subset of
  * its sequence's 64-key tiles, softmax over the kept keys only.  The page
  * "Open-H3-Regenerate-2K" ("Speed on one B200 (GB200)", per-module table)
  * credits a sparse attention backend with most of a refine's speed-up over
  * dense attention and calls it lossy; the pages give no algorithm.  Here:
  *  - block_tiles: device int32 [items][tiles_per_block], items in the order
- *    sequence, then head, then 128-row query block (items = sum over sequences
- *    of H * ceil(n_s / 128)).  Of each row the first
+ *    sequence, then head, then 256-row query block (items = sum over sequences
+ *    of H * ceil(n_s / 256)).  Of each row the first
  *    L = min(tiles_per_block, ceil(n_s / 64)) entries are tile indices within
  *    the sequence (tile t = its tokens 64t .. 64t+63), distinct; the rest are
  *    ignored.  Out-of-range entries are clamped to the sequence's tiles.

@@ -25,6 +25,14 @@ _BUILD = os.path.join(_HERE, "_build")
 # H3_ORACLE_LIB points at another build of h3_oracle.c (a sanitized one in the tests).
 _LIB_PATH = os.environ.get("H3_ORACLE_LIB") or os.path.join(_BUILD, "liboracle.so")
 
+# Query rows sharing one block-sparse tile list.  The pages credit a sparse
+# attention backend with the refine's speed-up ("Open-H3-Regenerate-2K", "Speed
+# on one B200 (GB200)", per-module table) but fix no algorithm and no block
+# size; this definition takes blocks of 256 query rows (the granularity at which
+# the attention kernel streams keys) by 64-key tiles, the softmax exactly over
+# the kept keys.
+SPARSE_BLOCK = 256
+
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
     """Compile the oracle with gcc (plain -O2, no fast-math)."""
@@ -205,21 +213,22 @@ class Problem:
             raise ValueError("oracle: row outside every sequence")
         return out
 
-    # -- block-sparse attention (kept 64-key tiles per 128-row query block) --
+    # -- block-sparse attention (kept 64-key tiles per SPARSE_BLOCK-row query block) --
     def sparse_items(self):
         """(sequence, head, query block) work items in the order block-sparse
-        tile lists are laid out: sequence-major, then head, then 128-row block."""
+        tile lists are laid out: sequence-major, then head, then SPARSE_BLOCK-row
+        block."""
         items = []
         for s in range(len(self.cu) - 1):
             n = int(self.cu[s + 1] - self.cu[s])
             for hh in range(self.H):
-                for qb in range((n + 127) // 128):
+                for qb in range((n + SPARSE_BLOCK - 1) // SPARSE_BLOCK):
                     items.append((s, hh, qb))
         return items
 
     def sparse_attention_rows(self, rows, tiles, tiles_per_block: int, nthreads: int = 0) -> np.ndarray:
         """Attention of the rows (token * H + head) over only the keys of the
-        64-key tiles kept for their 128-row query block: tiles is int32
+        64-key tiles kept for their SPARSE_BLOCK-row query block: tiles is int32
         [items, tiles_per_block] (items as sparse_items()); of an item's row
         the first min(tiles_per_block, ceil(n_s / 64)) entries are tile
         indices within the sequence, the rest are ignored.  The softmax runs
@@ -234,7 +243,7 @@ class Problem:
         for r_i, r in enumerate(rows.tolist()):
             tok, hh = divmod(r, self.H)
             s = int(np.searchsorted(self.cu, tok, side="right") - 1)
-            qb = (tok - int(self.cu[s])) // 128
+            qb = (tok - int(self.cu[s])) // SPARSE_BLOCK
             groups.setdefault((s, hh, qb), []).append(r_i)
         for (s, hh, qb), idx in groups.items():
             n = int(self.cu[s + 1] - self.cu[s])
@@ -260,7 +269,7 @@ class Problem:
         return vv.astype(np.float64) if vv.dtype == np.float64 else _bf16_bits_to_f64(vv)
 
     def sparse_select(self, tiles_per_block: int) -> np.ndarray:
-        """Top-k kept tiles per (sequence, head, 128-row query block) by pooled
+        """Top-k kept tiles per (sequence, head, SPARSE_BLOCK-row query block) by pooled
         score: qbar = mean of the block's qhat' rows (qhat * scale * log2 e),
         kbar_t = mean of tile t's khat rows, both from the values rounded to bf16
         as the attention path stores them, score_t = qbar . kbar_t (fp64).  The
@@ -282,7 +291,7 @@ class Problem:
                 kbar = np.stack([kh[64 * t:64 * t + 64].mean(axis=0) for t in range(nt)])
                 cache = {(s, hh): (qh, kbar)}
             qh, kbar = cache[(s, hh)]
-            qbar = qh[128 * qb:128 * qb + 128].mean(axis=0)
+            qbar = qh[SPARSE_BLOCK * qb:SPARSE_BLOCK * (qb + 1)].mean(axis=0)
             sc = kbar @ qbar
             L = min(tiles_per_block, len(sc))
             order = sorted(range(len(sc)), key=lambda t: (-sc[t], t))[:L]

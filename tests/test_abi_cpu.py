@@ -41,7 +41,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), "libh3attn.so does not export %s" % n
     assert set(names) == set(h.EXPORTED)
-    assert h.version() == 1
+    assert h.version() == h.H3ATTN_VERSION == 2
 
 
 def test_status_strings():
@@ -382,7 +382,8 @@ def test_sparse_workspace_sizes():
     assert _sparse_call(ws_bytes=dense, stages=2) == h.H3ATTN_ERR_WORKSPACE and "needs" in h.last_error()
     if not _gpu_present():
         assert _sparse_call(ws_bytes=dense, stages=5) == h.H3ATTN_ERR_DEVICE
-    assert h.sparse_items([0, 1000, 1000, 1129], 24) == 24 * 8 + 24 * 2
+    assert h.sparse_items([0, 1000, 1000, 1129], 24) == 24 * 4 + 24 * 1     # 256-row blocks
+    assert h.SPARSE_BLOCK_ROWS == oracle.SPARSE_BLOCK
     with pytest.raises(h.H3AttnError):
         h.h3attn_workspace_size(p, [0, 1000], 4)
 
@@ -461,3 +462,24 @@ def test_mfma_ceiling_argument_errors(monkeypatch):
         assert h.mfma_ceiling_raw(0, 256, 10, FAKE, None) == h.H3ATTN_ERR_DEVICE
     monkeypatch.setenv("H3ATTN_FAULT", "launch")
     assert h.mfma_ceiling_raw(1, 256, 10, FAKE, None) == h.H3ATTN_ERR_HIP and "mfma ceiling" in h.last_error()
+
+
+def test_binding_refuses_another_abi_version(tmp_path):
+    """A library of another ABI version lays out its tile lists and workspaces
+    differently (version 1 kept one block-sparse list per 128 query rows), so
+    the arrays this binding allocates would be too small for it: the binding
+    refuses to load it instead of letting its kernels write past them."""
+    import subprocess
+    import sys
+    src = tmp_path / "stub.c"
+    names = [n for n in h.EXPORTED if n != "h3attn_version"]
+    src.write_text("".join("int %s(void) { return 0; }\n" % n for n in names) +
+                   "int h3attn_version(void) { return 1; }\n")
+    so = tmp_path / "libstub.so"
+    subprocess.run(["gcc", "-shared", "-fPIC", str(src), "-o", str(so)], check=True)
+    code = ("import audio_diffusion_transformer_amd.h3attn as h\n"
+            "try:\n    h.lib()\n    print('LOADED')\nexcept RuntimeError as e:\n    print('REFUSED', e)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       env=dict(os.environ, H3ATTN_LIB=str(so)))
+    assert "REFUSED" in r.stdout and "ABI version 1" in r.stdout, r.stdout + r.stderr

@@ -4,7 +4,7 @@
   as the dense one, so its output is bit-identical to h3attn_fwd (and meets
   the oracle's bf16 gates).
 - Caller lists (the oracle's inputs, from a seeded generator): random subsets
-  of tiles per (sequence, head, query block), in random order, including the
+  of tiles per (sequence, head, 256-row query block), in random order, including the
   sequence's partial last tile, compared on every row with the oracle's
   softmax over exactly the kept keys.
 - Selection: the tiles the GPU keeps against the oracle's pooled-score top-k.
@@ -24,6 +24,7 @@ from audio_diffusion_transformer_amd import synth
 from tests import gpu_harness as G
 
 pytestmark = pytest.mark.gpu
+B = oracle.SPARSE_BLOCK            # query rows per tile list
 Seq = synth.Seq
 
 SMALL = {
@@ -57,7 +58,7 @@ def _random_lists(w, tpb, seed):
         n = s.n
         nt = (n + 63) // 64
         for _ in range(w.H):
-            for _ in range((n + 127) // 128):
+            for _ in range((n + B - 1) // B):
                 L = min(tpb, nt)
                 pick = rng.choice(nt, L, replace=False)
                 if nt - 1 not in pick and L > 1 and rng.random() < 0.5:
@@ -125,7 +126,7 @@ def test_selection_and_attention_over_it(torch_dev, name):
     same = _compare_selection(lists, ref_lists, scores, name)
     items = p.sparse_items()
     rows = np.array([tok * w.H + hh for i, (s, hh, qb) in enumerate(items) if same[i]
-                     for tok in range(int(p.cu[s]) + 128 * qb, min(int(p.cu[s]) + 128 * qb + 128, int(p.cu[s + 1])))],
+                     for tok in range(int(p.cu[s]) + B * qb, min(int(p.cu[s]) + B * qb + B, int(p.cu[s + 1])))],
                     dtype=np.int64)
     ref = p.sparse_attention_rows(rows, ref_lists, tpb, nthreads=G.oracle_threads())
     G.check(G.metrics(G.gpu_rows(got, rows, w.H), ref), G.BF16_GATE, name + " selected")
@@ -143,7 +144,7 @@ def test_full_size_two_heads(torch_dev):
     ws = w.replace(H=len(heads))
     p = oracle.Problem.from_workload(ws, sub)
     ref_lists, scores = p.sparse_select(w.keep_tiles)
-    nqb = (w.N + 127) // 128
+    nqb = (w.N + B - 1) // B
     gl = np.concatenate([lists[hh * nqb:(hh + 1) * nqb] for hh in heads])
     same = _compare_selection(gl, ref_lists, scores, "sparse_joint")
     rng = np.random.default_rng(12)
@@ -152,7 +153,7 @@ def test_full_size_two_heads(torch_dev):
     rows = []
     for i in pick:
         j, qb = divmod(int(i), nqb)
-        toks = rng.choice(np.arange(128 * qb, min(128 * qb + 128, w.N)), 8, replace=False)
+        toks = rng.choice(np.arange(B * qb, min(B * qb + B, w.N)), 8, replace=False)
         rows += [int(tk) * len(heads) + j for tk in toks]
     rows = np.array(sorted(rows), dtype=np.int64)
     ref = p.sparse_attention_rows(rows, ref_lists, w.keep_tiles, nthreads=G.oracle_threads())
@@ -178,10 +179,10 @@ def test_full_size_ragged_two_heads(torch_dev):
     ws = w.replace(H=len(heads))
     p = oracle.Problem.from_workload(ws, sub)
     ref_lists, scores = p.sparse_select(w.keep_tiles)
-    # the GPU's list rows run sequence by sequence, then over all H heads, then 128-row block
+    # the GPU's list rows run sequence by sequence, then over all H heads, then query block
     gpu_rows, base = [], 0
     for s in w.seqs:
-        nqb = (s.n + 127) // 128
+        nqb = (s.n + B - 1) // B
         for hh in heads:
             gpu_rows += list(range(base + hh * nqb, base + (hh + 1) * nqb))
         base += w.H * nqb
@@ -193,8 +194,8 @@ def test_full_size_ragged_two_heads(torch_dev):
     rows = []
     for i in pick:
         s, j, qb = items[int(i)]
-        lo = int(p.cu[s]) + 128 * qb
-        hi = min(lo + 128, int(p.cu[s + 1]))
+        lo = int(p.cu[s]) + B * qb
+        hi = min(lo + B, int(p.cu[s + 1]))
         toks = rng.choice(np.arange(lo, hi), min(8, hi - lo), replace=False)
         rows += [int(tk) * len(heads) + j for tk in toks]
     rows = np.array(sorted(rows), dtype=np.int64)

@@ -608,7 +608,8 @@ def test_sparse_attention_matches_torch_sdpa_on_kept_keys():
     got = p.sparse_attention_rows(rows, tiles, k)
     for i, (s, hh, qb) in enumerate(items):
         n = int(p.cu[s + 1] - p.cu[s])
-        q_tok = np.arange(128 * qb, min(128 * qb + 128, n)) + int(p.cu[s])
+        B = oracle.SPARSE_BLOCK
+        q_tok = np.arange(B * qb, min(B * qb + B, n)) + int(p.cu[s])
         kept = [int(t) for t in tiles[i] if t >= 0]
         k_tok = np.concatenate([np.arange(64 * t, min(64 * t + 64, n)) for t in kept]) + int(p.cu[s])
         qh = torch.from_numpy(p.prologue_rows(0, q_tok * p.H + hh))
@@ -623,7 +624,7 @@ def test_sparse_select_closed_form_ranking():
     # tile: qhat = sqrt(d) v/|v|, khat_t = sqrt(d) u_t/|u_t| with u_t = a_t v + b_t e (e orthogonal
     # to v, |e| = |v|), so the pooled score ranks the tiles by a_t / sqrt(a_t^2 + b_t^2)
     d, H = 16, 1
-    seqs = [(1, 8, 40, 0)]                                        # 320 tokens: 3 query blocks, 5 tiles
+    seqs = [(1, 8, 40, 0)]                                        # 320 tokens: 2 query blocks, 5 tiles
     N = 320
     v = np.zeros(d); v[0] = 1.0
     e = np.zeros(d); e[1] = 1.0
