@@ -567,7 +567,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": {"mx": "attn_mx_kernel", "q8": "attn_q8_kernel",
-                                "bf16": "attn_bf16_pp_kernel<128>"}[kname],
+                                "bf16": "attn_bf16_pp_kernel<128, false>"}[kname],
                      "avg_ms": round(att_avg, 4)},
         # the same box's sustained matrix-core rate for this path's MFMA type, alone and with the
         # path's vector work beside it (h3attn_mfma_ceiling), beside the datasheet peak
@@ -593,7 +593,7 @@ def main():
             "kept_fraction": round(attn_flops / w.flops(), 4),
             "dense_attention_ms": round(dense_att, 4),
             "speedup_vs_dense_step": round((pro_avg + dense_att) / ms_step, 3)})
-        res["roofline"]["kernel"] = "attn_bf16_pp_kernel<128, sparse>"
+        res["roofline"]["kernel"] = "attn_bf16_pp_kernel<128, true>"
         res["roofline"]["traffic"] = None
         res["config"]["keep_tiles"] = w.keep_tiles
     if proj:
