@@ -743,9 +743,9 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
 template __global__ void attn_bf16_pp_kernel<128, false>(AttnArgs);
 template __global__ void attn_bf16_pp_kernel<128, true>(AttnArgs);
 
-// Dense attention at head_dim 128 runs attn_bf16_pp_kernel over 256-row query
-// blocks; head_dim 64 and the block-sparse path run attn_bf16_kernel over
-// 128-row blocks (attn_bf16_block_m gives the caller the block size).
+// Head_dim 128 runs attn_bf16_pp_kernel over 256-row query blocks, dense or
+// block-sparse (a.tiles); head_dim 64 runs attn_bf16_kernel over 128-row
+// blocks (attn_bf16_block_m gives the caller the block size).
 hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_t st)
 {
     if (nitems <= 0) return hipSuccess;
