@@ -14,6 +14,8 @@
   attention over the GPU's selection is then checked on the rows whose lists
   agree.
 - The 125,242-token joint shape with 25% of the tiles kept, on two heads.
+- The longest sequence the path accepts (131,072 tokens, 2,048 tiles) with
+  every tile selected: lists of the maximum length, bit-identical to dense.
 """
 import numpy as np
 import pytest
@@ -203,3 +205,25 @@ def test_full_size_ragged_two_heads(torch_dev):
     tok, j = rows // len(heads), rows % len(heads)
     gotr = G.decode(got[tok, np.array(heads)[j]])
     G.check(G.metrics(gotr, ref), G.BF16_GATE, w.name + " sampled")
+
+
+def test_longest_sequence_every_tile_selected(torch_dev):
+    """The largest sequence the block-sparse path accepts: 131,072 tokens
+    (32 x 64 x 64 video grid), i.e. 2,048 tiles, with 2,048 tiles per block,
+    the list length's upper bound.  The selection has to keep every tile, so
+    each list is 0..2047 in tile order, and the attention over it is the
+    dense kernel's, bit for bit; sampled rows also against the oracle."""
+    w = synth.Workload("sparse_longest", H=2, d=128, seqs=(Seq(32, 64, 64),), split=(32, 48, 48), seed=53)
+    nt = w.N // 64
+    assert w.N == 131072 and nt == 2048
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    dense = G.bits(G.run(w, t, label=w.name + " dense"))
+    got, lists = _run_sparse(torch_dev, w, t, nt, select=True, label=w.name)
+    del t
+    assert lists.shape == (h.sparse_items(inp["cu_seqlens"], w.H), nt)
+    assert np.array_equal(lists, np.tile(np.arange(nt, dtype=np.int32), (lists.shape[0], 1)))
+    assert np.array_equal(got, dense)
+    rows = np.sort(np.random.default_rng(14).choice(w.N * w.H, 128, replace=False)).astype(np.int64)
+    ref = oracle.Problem.from_workload(w, inp).attention_rows(rows, nthreads=G.oracle_threads())
+    G.check(G.metrics(G.gpu_rows(got, rows, w.H), ref), G.BF16_GATE, w.name + " sampled")
