@@ -1,6 +1,7 @@
 // Device helpers shared by the attention kernels (bf16 and quantised):
 // LDS swizzle, direct-to-LDS tile fills, the row exchange between the two
-// 32-lane halves of a wave that hold one query row, and small packing helpers.
+// 32-lane halves of a wave that hold one query row, and small packing and
+// INT8 coding helpers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -98,6 +99,18 @@ __device__ __forceinline__ float row_sum2(float x)
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// INT8 code of r: round half to even, clamped to [-127, 127].
+__device__ __forceinline__ int32_t i8code(float r)
+{
+    return (int32_t)fminf(fmaxf(__builtin_rintf(r), -127.f), 127.f);
+}
+
+__device__ __forceinline__ uint32_t pack_i8x4(int32_t a, int32_t b, int32_t c, int32_t d)
+{
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
 
 // Row maximum of the 32 scores a lane holds (16 of each 32-key block).
 __device__ __forceinline__ float lane_max32(const f32x16 &s0, const f32x16 &s1)

@@ -33,7 +33,8 @@ struct Plan {
     size_t q8, k8, v8t, qscale, kscale, ksum, vmax, kmean, vscale;
     size_t sp_kbar, sp_qsum, sp_cnt; // block-sparse selection scratch (after the bf16 regions)
     size_t qx, qxs, kx, kxs, vxt, vxs, mx_ksum, mx_kmean;   // MXFP4 path (mx.hip)
-    size_t bytes_bf16, bytes_q8, bytes_sparse, bytes_mx;
+    size_t k32, v16;             // projection's quantised path: fp32 khat, bf16 v (after the q8 regions)
+    size_t bytes_bf16, bytes_q8, bytes_sparse, bytes_mx, bytes_q8p;
 };
 
 // Which sequence a padded 64-token tile belongs to: tiles of sequence s are
@@ -121,6 +122,10 @@ struct Q8Args {
     int8_t *q8, *k8;
     uint8_t *v8t;
     float *qscale, *kscale, *ksum, *vmax, *kmean, *vscale;
+    // Set for the projection's quantised path: khat (fp32) and v (bf16), both
+    // [H][Npad][d], as the projection wrote them; q, k, v are then not read.
+    const float *k32;
+    const uint16_t *v16;
     int32_t H;
     int64_t Npad;
     float eps;
@@ -228,6 +233,12 @@ struct ProjArgs {
     const float *norm_w, *rope;
     uint16_t *qhat, *khat, *vt;
     float *knorm;
+    // Quantised epilogue (qkv_proj_q8 launch, d = 128): INT8 qhat codes with one
+    // scale per (head, tile), fp32 khat and bf16 v, all [H][Npad][d].
+    int8_t *q8;
+    float *qscale;
+    float *k32;
+    uint16_t *v16;
     int64_t out_hstride, out_tstride;
     int32_t natural;
     int32_t H;
@@ -266,6 +277,7 @@ hipError_t launch_q8_prep(const Q8Args &a, int d, hipStream_t st);
 hipError_t launch_attn_q8(const Q8AttnArgs &a, int d, int64_t nitems, hipStream_t st);
 hipError_t launch_q8_export(const Q8ExportArgs &a, hipStream_t st);
 hipError_t launch_qkv_proj(const ProjArgs &a, int d, hipStream_t st);
+hipError_t launch_qkv_proj_q8(const ProjArgs &a, hipStream_t st);
 hipError_t launch_out_proj(const OutProjArgs &a, hipStream_t st);
 hipError_t launch_sparse_select(const SparseSelectArgs &a, int d, hipStream_t st);
 hipError_t launch_mx_prep(const MxArgs &a, int d, hipStream_t st);

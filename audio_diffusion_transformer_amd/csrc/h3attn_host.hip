@@ -120,6 +120,9 @@ h3attn_status make_plan(const h3attn_params *p, const int32_t *cu, Plan *pl)
     pl->kmean = take(S * H * d * 4);
     pl->vscale = take(S * H * d * 4);
     pl->bytes_q8 = std::max<size_t>(at, 256);
+    pl->k32 = take(H * Np * d * 4);
+    pl->v16 = take(H * Np * d * 2);
+    pl->bytes_q8p = std::max<size_t>(at, 256);
     at = 0;
     pl->qx = take(H * Np * d / 2);
     pl->qxs = take(H * Np * d / 32);
@@ -292,17 +295,22 @@ size_t h3attn_workspace_size(const h3attn_params *p, const int32_t *cu_seqlens_h
 {
     Plan pl;
     if (make_plan(p, cu_seqlens_host, &pl) != H3ATTN_OK) return 0;
-    if ((quantized == 1 || quantized == 3) && pl.d != 128) {
+    if (quantized < 0 || quantized > 4) {
+        fail(H3ATTN_ERR_INVALID_ARG, "quantized must be 0, 1, 2, 3 or 4 (got %d)", quantized);
+        return 0;
+    }
+    if ((quantized == 1 || quantized == 3 || quantized == 4) && pl.d != 128) {
         fail(H3ATTN_ERR_UNSUPPORTED, "the quantised paths need head_dim 128");
         return 0;
     }
-    if (quantized < 0 || quantized > 3) {
-        fail(H3ATTN_ERR_INVALID_ARG, "quantized must be 0, 1, 2 or 3 (got %d)", quantized);
-        return 0;
-    }
     ok();
-    return quantized == 1 ? pl.bytes_q8 : quantized == 2 ? pl.bytes_sparse : quantized == 3 ? pl.bytes_mx
-                                                                                            : pl.bytes_bf16;
+    switch (quantized) {
+    case 1: return pl.bytes_q8;
+    case 2: return pl.bytes_sparse;
+    case 3: return pl.bytes_mx;
+    case 4: return pl.bytes_q8p;
+    default: return pl.bytes_bf16;
+    }
 }
 
 h3attn_status h3attn_fwd_stages(const h3attn_params *p, const void *q, const void *k, const void *v,
@@ -851,6 +859,9 @@ h3attn_status h3attn_fwd_q8(const h3attn_params *p, const void *q, const void *k
                                 workspace_bytes, stream, 3);
 }
 
+static h3attn_status q8_export(const Plan &pl, const Q8Args &qa, int8_t *q8, int8_t *k8, float *q_scale,
+                               float *k_scale, float *k_mean, uint8_t *v8, float *v_scale, hipStream_t hs);
+
 h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const void *k, const void *v,
                                  const float *norm_w, const float *rope_tables,
                                  const int32_t *cu_seqlens_host, void *workspace, size_t workspace_bytes,
@@ -869,6 +880,111 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if ((st = launch_status(hs, "quantised prologue launch",
             [&] { return launch_q8_prep(qa, pl.d, hs); })) != H3ATTN_OK) return st;
+    return q8_export(pl, qa, q8, k8, q_scale, k_scale, k_mean, v8, v_scale, hs);
+}
+
+// The projection's quantised path: argument checks, plan and the arguments
+// of its kernels (the projection in its quantised epilogue, the K-mean and
+// coding passes reading what it wrote, the quantised attention).
+static h3attn_status proj_q8_common(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                                    const void *w_qkv, const float *norm_w, const float *rope_tables,
+                                    const int32_t *cu, const void *out, void *workspace, size_t workspace_bytes,
+                                    Plan &pl, ProjArgs &pa, Q8Args &qa)
+{
+    h3attn_status st = proj_plan(p, model_dim, x_stride, cu, pl);
+    if (st != H3ATTN_OK) return st;
+    if (pl.d != 128) return fail(H3ATTN_ERR_UNSUPPORTED, "the quantised path needs head_dim 128 (got %d)", pl.d);
+    if (pl.N == 0) return H3ATTN_OK;
+    if ((st = check_ptrs(x, w_qkv, x, norm_w, rope_tables, out)) != H3ATTN_OK) return st;
+    if (!workspace) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(H3ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < pl.bytes_q8p)
+        return fail(H3ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes_q8p);
+    if ((st = check_device()) != H3ATTN_OK) return st;
+    char *ws = static_cast<char *>(workspace);
+    pa = proj_args(p, pl, model_dim, x, x_stride, w_qkv, norm_w, rope_tables);
+    pa.q8 = reinterpret_cast<int8_t *>(ws + pl.q8);
+    pa.qscale = reinterpret_cast<float *>(ws + pl.qscale);
+    pa.k32 = reinterpret_cast<float *>(ws + pl.k32);
+    pa.v16 = reinterpret_cast<uint16_t *>(ws + pl.v16);
+    std::memset(&qa, 0, sizeof qa);
+    qa.norm_w = norm_w;
+    qa.rope = rope_tables;
+    qa.q8 = pa.q8;
+    qa.k8 = reinterpret_cast<int8_t *>(ws + pl.k8);
+    qa.v8t = reinterpret_cast<uint8_t *>(ws + pl.v8t);
+    qa.qscale = pa.qscale;
+    qa.kscale = reinterpret_cast<float *>(ws + pl.kscale);
+    qa.ksum = reinterpret_cast<float *>(ws + pl.ksum);
+    qa.vmax = reinterpret_cast<float *>(ws + pl.vmax);
+    qa.kmean = reinterpret_cast<float *>(ws + pl.kmean);
+    qa.vscale = reinterpret_cast<float *>(ws + pl.vscale);
+    qa.k32 = pa.k32;
+    qa.v16 = pa.v16;
+    qa.H = pl.H;
+    qa.Npad = pl.Npad;
+    qa.eps = p->eps;
+    qa.ntiles = (int32_t)(pl.Npad / kTile);
+    qa.seq = seq_table(pl);
+    return H3ATTN_OK;
+}
+
+// Stage 1 of the projection's quantised path: projection with the quantised
+// epilogue, then the K means, V scales and the K / V coding.
+static h3attn_status proj_q8_stage1(const Plan &pl, const ProjArgs &pa, const Q8Args &qa, hipStream_t hs)
+{
+    h3attn_status st = launch_status(hs, "projection launch", [&] { return launch_qkv_proj_q8(pa, hs); });
+    if (st != H3ATTN_OK) return st;
+    return launch_status(hs, "quantised prologue launch", [&] { return launch_q8_prep(qa, pl.d, hs); });
+}
+
+h3attn_status h3attn_fwd_proj_q8_stages(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                                        const void *w_qkv, const float *norm_w, const float *rope_tables,
+                                        const int32_t *cu_seqlens_host, void *out, void *workspace,
+                                        size_t workspace_bytes, void *stream, int stages)
+{
+    if (stages < 1 || stages > 3) return fail(H3ATTN_ERR_INVALID_ARG, "stages must be 1, 2 or 3 (got %d)", stages);
+    Plan pl;
+    ProjArgs pa;
+    Q8Args qa;
+    h3attn_status st = proj_q8_common(p, model_dim, x, x_stride, w_qkv, norm_w, rope_tables, cu_seqlens_host, out,
+                                      workspace, workspace_bytes, pl, pa, qa);
+    if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((stages & 1) && (st = proj_q8_stage1(pl, pa, qa, hs)) != H3ATTN_OK) return st;
+    if (!(stages & 2)) return ok();
+    Q8AttnArgs aa;
+    std::memset(&aa, 0, sizeof aa);
+    aa.q8 = qa.q8;
+    aa.k8 = qa.k8;
+    aa.v8t = qa.v8t;
+    aa.qscale = qa.qscale;
+    aa.kscale = qa.kscale;
+    aa.vscale = qa.vscale;
+    aa.out = static_cast<uint16_t *>(out);
+    aa.o_stride = p->o_stride;
+    aa.Npad = pl.Npad;
+    aa.H = pl.H;
+    aa.scale_log2 = scale_log2(p);
+    const int64_t items = order_work(pl, aa, aa.seq_idx);
+    return launch_status(hs, "quantised attention launch", [&] { return launch_attn_q8(aa, pl.d, items, hs); });
+}
+
+h3attn_status h3attn_fwd_proj_q8(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                                 const void *w_qkv, const float *norm_w, const float *rope_tables,
+                                 const int32_t *cu_seqlens_host, void *out, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    return h3attn_fwd_proj_q8_stages(p, model_dim, x, x_stride, w_qkv, norm_w, rope_tables, cu_seqlens_host, out,
+                                     workspace, workspace_bytes, stream, 3);
+}
+
+// Exports the quantised state in natural layouts (shared by the two
+// quantised prologue diagnostics): codes and per-tile scales by the export
+// kernel, the K means and V scales by device copies.
+static h3attn_status q8_export(const Plan &pl, const Q8Args &qa, int8_t *q8, int8_t *k8, float *q_scale,
+                               float *k_scale, float *k_mean, uint8_t *v8, float *v_scale, hipStream_t hs)
+{
     Q8ExportArgs ea;
     std::memset(&ea, 0, sizeof ea);
     ea.q8 = qa.q8;
@@ -887,6 +1003,7 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
     ea.ntiles = qa.ntiles;
     for (int s = 0; s < pl.S; ++s) ea.nblocks += (pl.cu[s + 1] - pl.cu[s] + kTile - 1) / kTile;
     ea.seq = qa.seq;
+    h3attn_status st;
     if ((st = launch_status(hs, "quantised export launch",
             [&] { return launch_q8_export(ea, hs); })) != H3ATTN_OK) return st;
     const size_t sb = (size_t)pl.S * pl.H * pl.d * sizeof(float);
@@ -895,6 +1012,31 @@ h3attn_status h3attn_q8_prologue(const h3attn_params *p, const void *q, const vo
         return st;
     return launch_status(hs, "v_scale copy",
             [&] { return hipMemcpyAsync(v_scale, qa.vscale, sb, hipMemcpyDeviceToDevice, hs); });
+}
+
+h3attn_status h3attn_proj_q8_prologue(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                                      const void *w_qkv, const float *norm_w, const float *rope_tables,
+                                      const int32_t *cu_seqlens_host, void *workspace, size_t workspace_bytes,
+                                      int8_t *q8, int8_t *k8, float *q_scale, float *k_scale, float *k_mean,
+                                      uint8_t *v8, float *v_scale, void *stream)
+{
+    Plan pl;
+    ProjArgs pa;
+    Q8Args qa;
+    h3attn_status st = proj_plan(p, model_dim, x_stride, cu_seqlens_host, pl);
+    if (st != H3ATTN_OK || pl.N == 0) return st == H3ATTN_OK ? ok() : st;
+    const void *outs[7] = {q8, k8, q_scale, k_scale, k_mean, v8, v_scale};
+    const char *names[7] = {"q8", "k8", "q_scale", "k_scale", "k_mean", "v8", "v_scale"};
+    for (int i = 0; i < 7; ++i) {
+        if (!outs[i]) return fail(H3ATTN_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(outs[i], 8)) return fail(H3ATTN_ERR_INVALID_ARG, "%s is not 8-byte aligned", names[i]);
+    }
+    st = proj_q8_common(p, model_dim, x, x_stride, w_qkv, norm_w, rope_tables, cu_seqlens_host, x, workspace,
+                        workspace_bytes, pl, pa, qa);
+    if (st != H3ATTN_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = proj_q8_stage1(pl, pa, qa, hs)) != H3ATTN_OK) return st;
+    return q8_export(pl, qa, q8, k8, q_scale, k_scale, k_mean, v8, v_scale, hs);
 }
 
 static h3attn_status mx_common(const h3attn_params *p, const void *q, const void *k, const void *v,

@@ -41,17 +41,6 @@ constexpr int QD = 128;               // head dim of the quantised path
 constexpr float kPScale = 224.0f;     // 448 / 2^kQ8Lazy
 constexpr float kQ8Lazy = 1.0f;       // running max raised when a tile exceeds it by > 1 (log2 units)
 
-__device__ __forceinline__ int32_t i8code(float r)
-{
-    return (int32_t)fminf(fmaxf(__builtin_rintf(r), -127.f), 127.f);
-}
-
-__device__ __forceinline__ uint32_t pack_i8x4(int32_t a, int32_t b, int32_t c, int32_t d)
-{
-    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-           ((uint32_t)(d & 0xff) << 24);
-}
-
 // Four fp32 -> four OCP e4m3 bytes (round to nearest even), little-endian.  The
 // first conversion's pass-through operand is arbitrary (its half is overwritten
 // by the second); passing a dead input avoids materialising a zero.
@@ -91,6 +80,10 @@ __device__ __forceinline__ bool tile_head(int H, int ntiles, int &gt, int &h)
 }
 
 // ------------------------------------------------------------------ pass 1
+// WS (the projection's quantised path): khat and v come from a.k32 / a.v16,
+// and qhat was already coded by the projection, so only the K sums and the V
+// maxima are formed.
+template <bool WS>
 __global__ __launch_bounds__(256) void q8_pass1_kernel(Q8Args a)
 {
     constexpr int LPR = QD / 8, RPP = 256 / LPR;
@@ -102,53 +95,75 @@ __global__ __launch_bounds__(256) void q8_pass1_kernel(Q8Args a)
     int s, j, valid;
     tile_seq(a.seq.cu, a.seq.off, a.seq.S, gt, s, j, valid);
     const int t = threadIdx.x, c = t % LPR, rr = t / LPR;
-    float wq[8], wk[8];
-    load_w8(a.norm_w, h, QD, c, wq);
-    load_w8(a.norm_w, a.H + h, QD, c, wk);
-    float qv[kTile / RPP][8], ks[8], vm[8], qa = 0.f;
+    float ks[8], vm[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) ks[i] = vm[i] = 0.f;
+    if constexpr (WS) {
 #pragma unroll
-    for (int pass = 0; pass < kTile / RPP; ++pass) {
-        const int r = pass * RPP + rr;
-        const bool ok = r < valid;
-        const int64_t tok = (int64_t)a.seq.cu[s] + kTile * j + r;
-        float cs[8] = {1.f, 0.f, 1.f, 0.f, 1.f, 0.f, 1.f, 0.f};
-        if (ok) load_cs8(a.rope, tok, QD, c, cs);
-        u32x4_t rq = {0u, 0u, 0u, 0u}, rk = rq, rv = rq;
-        if (ok) {
-            rq = *reinterpret_cast<const u32x4_t *>(a.q + tok * a.q_stride + h * QD + 8 * c);
-            rk = *reinterpret_cast<const u32x4_t *>(a.k + tok * a.k_stride + h * QD + 8 * c);
-            rv = *reinterpret_cast<const u32x4_t *>(a.v + tok * a.v_stride + h * QD + 8 * c);
+        for (int pass = 0; pass < kTile / RPP; ++pass) {
+            const int r = pass * RPP + rr;
+            if (r < valid) {
+                const int64_t row = ((int64_t)h * a.Npad + a.seq.off[s] + kTile * j + r) * QD + 8 * c;
+                const f32x4_t k0 = *reinterpret_cast<const f32x4_t *>(a.k32 + row);
+                const f32x4_t k1 = *reinterpret_cast<const f32x4_t *>(a.k32 + row + 4);
+                float x[8];
+                unpack8(*reinterpret_cast<const u32x4_t *>(a.v16 + row), x);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ks[i] += k0[i];
+                    ks[4 + i] += k1[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vm[i] = fmaxf(vm[i], fabsf(x[i]));
+            }
         }
-        float x[8], y[8];
-        unpack8(rq, x);
-        norm_rope8<LPR>(x, wq, cs, 1.0f / QD, a.eps, y);
+    } else {
+        float wq[8], wk[8], qv[kTile / RPP][8], qa = 0.f;
+        load_w8(a.norm_w, h, QD, c, wq);
+        load_w8(a.norm_w, a.H + h, QD, c, wk);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            qv[pass][i] = ok ? y[i] : 0.f;
-            qa = fmaxf(qa, fabsf(qv[pass][i]));
+        for (int pass = 0; pass < kTile / RPP; ++pass) {
+            const int r = pass * RPP + rr;
+            const bool ok = r < valid;
+            const int64_t tok = (int64_t)a.seq.cu[s] + kTile * j + r;
+            float cs[8] = {1.f, 0.f, 1.f, 0.f, 1.f, 0.f, 1.f, 0.f};
+            if (ok) load_cs8(a.rope, tok, QD, c, cs);
+            u32x4_t rq = {0u, 0u, 0u, 0u}, rk = rq, rv = rq;
+            if (ok) {
+                rq = *reinterpret_cast<const u32x4_t *>(a.q + tok * a.q_stride + h * QD + 8 * c);
+                rk = *reinterpret_cast<const u32x4_t *>(a.k + tok * a.k_stride + h * QD + 8 * c);
+                rv = *reinterpret_cast<const u32x4_t *>(a.v + tok * a.v_stride + h * QD + 8 * c);
+            }
+            float x[8], y[8];
+            unpack8(rq, x);
+            norm_rope8<LPR>(x, wq, cs, 1.0f / QD, a.eps, y);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qv[pass][i] = ok ? y[i] : 0.f;
+                qa = fmaxf(qa, fabsf(qv[pass][i]));
+            }
+            unpack8(rk, x);
+            norm_rope8<LPR>(x, wk, cs, 1.0f / QD, a.eps, y);
+            if (ok) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ks[i] += y[i];
+            }
+            unpack8(rv, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vm[i] = fmaxf(vm[i], fabsf(x[i]));
         }
-        unpack8(rk, x);
-        norm_rope8<LPR>(x, wk, cs, 1.0f / QD, a.eps, y);
-        if (ok) {
+        const float amax = block_max256(qa, red);
+        const float sq = amax > 0.f ? amax / 127.0f : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ks[i] += y[i];
+        for (int pass = 0; pass < kTile / RPP; ++pass) {
+            const int r = pass * RPP + rr;
+            int32_t q[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = i8code(qv[pass][i] / sq);
+            const u32x2_t w2 = {pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])};
+            *reinterpret_cast<u32x2_t *>(a.q8 + ((int64_t)h * a.Npad + a.seq.off[s] + kTile * j + r) * QD + 8 * c) = w2;
         }
-        unpack8(rv, x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vm[i] = fmaxf(vm[i], fabsf(x[i]));
-    }
-    const float amax = block_max256(qa, red);
-    const float sq = amax > 0.f ? amax / 127.0f : 1.0f;
-#pragma unroll
-    for (int pass = 0; pass < kTile / RPP; ++pass) {
-        const int r = pass * RPP + rr;
-        int32_t q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = i8code(qv[pass][i] / sq);
-        const u32x2_t w2 = {pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])};
-        *reinterpret_cast<u32x2_t *>(a.q8 + ((int64_t)h * a.Npad + a.seq.off[s] + kTile * j + r) * QD + 8 * c) = w2;
+        if (t == 0) a.qscale[(int64_t)h * a.ntiles + gt] = sq;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -166,7 +181,6 @@ __global__ __launch_bounds__(256) void q8_pass1_kernel(Q8Args a)
         a.ksum[o] = sum;
         a.vmax[o] = mx;
     }
-    if (t == 0) a.qscale[(int64_t)h * a.ntiles + gt] = sq;
 }
 
 // ------------------------------------------------------------------ reduce
@@ -203,6 +217,8 @@ __global__ __launch_bounds__(kReduceGroups * QD) void q8_reduce_kernel(Q8Args a)
 }
 
 // ------------------------------------------------------------------ pass 3
+// WS: khat and v read from a.k32 / a.v16 (the projection's quantised path).
+template <bool WS>
 __global__ __launch_bounds__(256) void q8_pass3_kernel(Q8Args a)
 {
     constexpr int LPR = QD / 8, RPP = 256 / LPR;
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(256) void q8_pass3_kernel(Q8Args a)
     tile_seq(a.seq.cu, a.seq.off, a.seq.S, gt, s, j, valid);
     const int t = threadIdx.x, c = t % LPR, rr = t / LPR;
     float wk[8], km[8], vsc[8];
-    load_w8(a.norm_w, a.H + h, QD, c, wk);
+    if constexpr (!WS) load_w8(a.norm_w, a.H + h, QD, c, wk);
     load_w8(a.kmean, (int64_t)s * a.H + h, QD, c, km);
     load_w8(a.vscale, (int64_t)s * a.H + h, QD, c, vsc);
     float kv[kTile / RPP][8], ka = 0.f;
@@ -223,16 +239,33 @@ __global__ __launch_bounds__(256) void q8_pass3_kernel(Q8Args a)
         const int r = pass * RPP + rr;
         const bool ok = r < valid;
         const int64_t tok = (int64_t)a.seq.cu[s] + kTile * j + r;
-        float cs[8] = {1.f, 0.f, 1.f, 0.f, 1.f, 0.f, 1.f, 0.f};
-        if (ok) load_cs8(a.rope, tok, QD, c, cs);
-        u32x4_t rk = {0u, 0u, 0u, 0u}, rv = rk;
-        if (ok) {
-            rk = *reinterpret_cast<const u32x4_t *>(a.k + tok * a.k_stride + h * QD + 8 * c);
-            rv = *reinterpret_cast<const u32x4_t *>(a.v + tok * a.v_stride + h * QD + 8 * c);
-        }
         float x[8], y[8];
-        unpack8(rk, x);
-        norm_rope8<LPR>(x, wk, cs, 1.0f / QD, a.eps, y);
+        u32x4_t rv = {0u, 0u, 0u, 0u};
+        if constexpr (WS) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = 0.f;
+            if (ok) {
+                const int64_t row = ((int64_t)h * a.Npad + a.seq.off[s] + kTile * j + r) * QD + 8 * c;
+                const f32x4_t k0 = *reinterpret_cast<const f32x4_t *>(a.k32 + row);
+                const f32x4_t k1 = *reinterpret_cast<const f32x4_t *>(a.k32 + row + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    y[i] = k0[i];
+                    y[4 + i] = k1[i];
+                }
+                rv = *reinterpret_cast<const u32x4_t *>(a.v16 + row);
+            }
+        } else {
+            float cs[8] = {1.f, 0.f, 1.f, 0.f, 1.f, 0.f, 1.f, 0.f};
+            if (ok) load_cs8(a.rope, tok, QD, c, cs);
+            u32x4_t rk = {0u, 0u, 0u, 0u};
+            if (ok) {
+                rk = *reinterpret_cast<const u32x4_t *>(a.k + tok * a.k_stride + h * QD + 8 * c);
+                rv = *reinterpret_cast<const u32x4_t *>(a.v + tok * a.v_stride + h * QD + 8 * c);
+            }
+            unpack8(rk, x);
+            norm_rope8<LPR>(x, wk, cs, 1.0f / QD, a.eps, y);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             kv[pass][i] = ok ? y[i] - km[i] : 0.f;
@@ -598,18 +631,32 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     }
 }
 
+// Explicit instantiations: the host pass does not emit the launch stub of an
+// instantiation that is only named inside the launcher's branches.
+template __global__ void q8_pass1_kernel<false>(Q8Args);
+template __global__ void q8_pass1_kernel<true>(Q8Args);
+template __global__ void q8_pass3_kernel<false>(Q8Args);
+template __global__ void q8_pass3_kernel<true>(Q8Args);
+
 // ------------------------------------------------------------------ launch
 hipError_t launch_q8_prep(const Q8Args &a, int d, hipStream_t st)
 {
     if (d != QD) return hipErrorInvalidValue;
     const int64_t groups = (a.ntiles + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * a.H));
-    hipLaunchKernelGGL(q8_pass1_kernel, grid, dim3(256), 0, st, a);
+    const bool ws = a.k32 != nullptr;
+    if (ws)
+        hipLaunchKernelGGL(q8_pass1_kernel<true>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(q8_pass1_kernel<false>, grid, dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(q8_reduce_kernel, dim3((unsigned)(a.seq.S * a.H)), dim3(kReduceGroups * QD), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(q8_pass3_kernel, grid, dim3(256), 0, st, a);
+    if (ws)
+        hipLaunchKernelGGL(q8_pass3_kernel<true>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(q8_pass3_kernel<false>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -49,9 +49,100 @@ __device__ __forceinline__ int vt_key_pos(int r)
     return (r & ~0xC) | ((r >> 1) & 4) | ((r << 1) & 8);
 }
 
-// D: head dim.  Workgroup tile: 256 padded tokens of one sequence x the
-// feature blocks 2 F2 and 2 F2 + 1 (F = which * H + head).
+// Quantised epilogue of one wave (d = 128): its 64-token tile of q, k or v in
+// acc[token block][feature block].  q: RMSNorm + RoPE in fp32 (no softmax
+// scale), then INT8 codes with one scale per tile, amax / 127 over the tile's
+// tokens (1 when that is 0), exactly as the quantised prologue codes qhat.
+// k: the fp32 khat for the K-mean and coding passes.  v: rounded to bf16 once.
+// All three in [H][Npad][d]; padding rows are written as zeros.
 template <int D>
+__device__ __forceinline__ void q8_epilogue(const ProjArgs &a, f32x16 (&acc)[2][D / 32], int which, int head,
+                                            int s, int n_s, int jt, int gt, int m, int hh, int lane)
+{
+    constexpr int FB = D / 32;
+    const int valid = min(max(n_s - 64 * jt, 0), 64);
+    const int64_t row0 = (int64_t)head * a.Npad + a.seq.off[s] + 64 * jt;
+    if (which < 2) {
+        const float *wn = a.norm_w + (int64_t)(which * a.H + head) * D;
+        float amax = 0.f;
+#pragma unroll
+        for (int tb2 = 0; tb2 < 2; ++tb2) {
+            f32x16 *ac = acc[tb2];
+            const int t = 32 * tb2 + m;
+            const bool ok = t < valid;
+            const int64_t tok = (int64_t)a.seq.cu[s] + 64 * jt + t;
+            float ss = 0.f;
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) ss = fmaf(ac[fb][e], ac[fb][e], ss);
+            ss = row_sum2(ss);
+            const float rs = rsqrtf(fmaf(ss, 1.0f / (float)D, a.eps));
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int f0 = 32 * fb + 8 * g + 4 * hh;
+                    const f32x4_t w4 = *reinterpret_cast<const f32x4_t *>(wn + f0);
+                    f32x4_t cs = {1.f, 0.f, 1.f, 0.f};
+                    if (ok) cs = *reinterpret_cast<const f32x4_t *>(a.rope + tok * D + f0);
+                    const float x0 = ac[fb][4 * g] * rs * w4[0], x1 = ac[fb][4 * g + 1] * rs * w4[1];
+                    const float x2 = ac[fb][4 * g + 2] * rs * w4[2], x3 = ac[fb][4 * g + 3] * rs * w4[3];
+                    f32x4_t y = {x0 * cs[0] - x1 * cs[1], x0 * cs[1] + x1 * cs[0], x2 * cs[2] - x3 * cs[3],
+                                 x2 * cs[3] + x3 * cs[2]};
+                    if (!ok) y = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ac[fb][4 * g + e] = y[e];
+                        amax = fmaxf(amax, fabsf(y[e]));
+                    }
+                    if (which == 1) *reinterpret_cast<f32x4_t *>(a.k32 + (row0 + t) * D + f0) = y;
+                }
+            }
+        }
+        if (which == 0) {
+#pragma unroll
+            for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, __shfl_xor(amax, msk));
+            const float sq = amax > 0.f ? amax / 127.0f : 1.0f;
+#pragma unroll
+            for (int tb2 = 0; tb2 < 2; ++tb2) {
+                const int t = 32 * tb2 + m;
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16 &ac = acc[tb2][fb];
+                        const uint32_t w = pack_i8x4(i8code(ac[4 * g] / sq), i8code(ac[4 * g + 1] / sq),
+                                                     i8code(ac[4 * g + 2] / sq), i8code(ac[4 * g + 3] / sq));
+                        *reinterpret_cast<uint32_t *>(a.q8 + (row0 + t) * D + 32 * fb + 8 * g + 4 * hh) = w;
+                    }
+                }
+            }
+            if (lane == 0) a.qscale[(int64_t)head * a.ntiles + gt] = sq;
+        }
+    } else {
+#pragma unroll
+        for (int tb2 = 0; tb2 < 2; ++tb2) {
+            const int t = 32 * tb2 + m;
+            const bool ok = t < valid;
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16 &ac = acc[tb2][fb];
+                    u32x2 o = {pack2(ac[4 * g], ac[4 * g + 1]), pack2(ac[4 * g + 2], ac[4 * g + 3])};
+                    if (!ok) o = (u32x2){0u, 0u};
+                    *reinterpret_cast<u32x2 *>(a.v16 + (row0 + t) * D + 32 * fb + 8 * g + 4 * hh) = o;
+                }
+            }
+        }
+    }
+}
+
+// D: head dim.  Workgroup tile: 256 padded tokens of one sequence x the
+// feature blocks 2 F2 and 2 F2 + 1 (F = which * H + head).  Q8: the quantised
+// epilogue above instead of the bf16 one.
+template <int D, bool Q8>
 __global__ __launch_bounds__(64 * kGemmWaves, 1) void qkv_proj_kernel(ProjArgs a)
 {
     constexpr int FB = D / 32;
@@ -91,6 +182,10 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void qkv_proj_kernel(ProjArgs a
     f32x16 acc[2][FB];
     gemm_mainloop<D>(acc, stages, xrs, xrow, wrs, wrow, a.model_dim / kGemmBK, wave, lane);
     if (F >= nfb) return;                            // the missing half of the last pair
+    if constexpr (Q8) {
+        q8_epilogue<D>(a, acc, which, head, s, n_s, j0 + tw, 4 * b + tw, m, hh, lane);
+        return;
+    }
 
     // ---- epilogue: this wave's 64-token tile, two 32-token blocks
     const float inv_d = 1.0f / (float)D;
@@ -177,16 +272,24 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void qkv_proj_kernel(ProjArgs a
 
 // Explicit instantiations: the host pass does not emit the launch stub of an
 // instantiation that is only named inside the launcher's branches.
-template __global__ void qkv_proj_kernel<64>(ProjArgs);
-template __global__ void qkv_proj_kernel<128>(ProjArgs);
+template __global__ void qkv_proj_kernel<64, false>(ProjArgs);
+template __global__ void qkv_proj_kernel<128, false>(ProjArgs);
+template __global__ void qkv_proj_kernel<128, true>(ProjArgs);
 
 hipError_t launch_qkv_proj(const ProjArgs &a, int d, hipStream_t st)
 {
     const dim3 grid(gemm_grid(a.nblk, (3 * (int64_t)a.H + 1) / 2));
     if (d == 128)
-        hipLaunchKernelGGL(qkv_proj_kernel<128>, grid, dim3(64 * kGemmWaves), 0, st, a);
+        hipLaunchKernelGGL((qkv_proj_kernel<128, false>), grid, dim3(64 * kGemmWaves), 0, st, a);
     else
-        hipLaunchKernelGGL(qkv_proj_kernel<64>, grid, dim3(64 * kGemmWaves), 0, st, a);
+        hipLaunchKernelGGL((qkv_proj_kernel<64, false>), grid, dim3(64 * kGemmWaves), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_proj_q8(const ProjArgs &a, hipStream_t st)
+{
+    const dim3 grid(gemm_grid(a.nblk, (3 * (int64_t)a.H + 1) / 2));
+    hipLaunchKernelGGL((qkv_proj_kernel<128, true>), grid, dim3(64 * kGemmWaves), 0, st, a);
     return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ SPARSE_BLOCK_ROWS = 256            # query rows per block-sparse tile list
 
 EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_fwd_q8",
             "h3attn_fwd_q8_stages", "h3attn_prologue", "h3attn_fwd_proj", "h3attn_fwd_proj_stages",
-            "h3attn_proj_prologue", "h3attn_out_proj", "h3attn_fwd_sparse", "h3attn_fwd_sparse_stages",
+            "h3attn_proj_prologue", "h3attn_fwd_proj_q8", "h3attn_fwd_proj_q8_stages", "h3attn_proj_q8_prologue",
+            "h3attn_out_proj", "h3attn_fwd_sparse", "h3attn_fwd_sparse_stages",
             "h3attn_q8_prologue", "h3attn_fwd_mx", "h3attn_fwd_mx_stages", "h3attn_mx_prologue",
             "h3attn_fwd_static", "h3attn_mfma_ceiling", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
             "h3attn_status_string", "h3attn_last_error", "h3attn_version")
@@ -77,10 +78,15 @@ def lib():
         L.h3attn_fwd_static.argtypes = [P(h3attn_params), vp, vp, vp, vp, vp, P(C.c_int32), vp, vp]
         proj_args = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp, P(C.c_int32), vp, vp,
                      C.c_size_t, vp]
-        L.h3attn_fwd_proj.restype = C.c_int
-        L.h3attn_fwd_proj.argtypes = proj_args
-        L.h3attn_fwd_proj_stages.restype = C.c_int
-        L.h3attn_fwd_proj_stages.argtypes = proj_args + [C.c_int]
+        for name in ("h3attn_fwd_proj", "h3attn_fwd_proj_q8"):
+            getattr(L, name).restype = C.c_int
+            getattr(L, name).argtypes = proj_args
+        for name in ("h3attn_fwd_proj_stages", "h3attn_fwd_proj_q8_stages"):
+            getattr(L, name).restype = C.c_int
+            getattr(L, name).argtypes = proj_args + [C.c_int]
+        L.h3attn_proj_q8_prologue.restype = C.c_int
+        L.h3attn_proj_q8_prologue.argtypes = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp,
+                                              P(C.c_int32), vp, C.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
         L.h3attn_proj_prologue.restype = C.c_int
         L.h3attn_proj_prologue.argtypes = [P(h3attn_params), C.c_int32, vp, C.c_int64, vp, vp, vp,
                                            P(C.c_int32), vp, vp, vp, vp]
@@ -153,17 +159,18 @@ def _cu_ptr(cu: np.ndarray):
 
 
 def _mode(quantized) -> int:
-    """False/0: bf16; True/1: INT8/FP8; 2: bf16 plus the sparse selection; "mx"/3: MXFP4."""
+    """False/0: bf16; True/1: INT8/FP8; 2: bf16 plus the sparse selection; "mx"/3: MXFP4;
+    4: the projection's INT8/FP8 path (h3attn_fwd_proj_q8)."""
     if isinstance(quantized, str):
         if quantized != "mx":
-            raise ValueError("quantized must be a bool, 0..3 or 'mx' (got %r)" % quantized)
+            raise ValueError("quantized must be a bool, 0..4 or 'mx' (got %r)" % quantized)
         return 3
     return int(quantized)
 
 
 def h3attn_workspace_size(params: h3attn_params, cu_seqlens, quantized=False) -> int:
     """Workspace bytes: quantized False/0 bf16, True/1 INT8/FP8, 2 bf16 plus the
-    sparse selection, "mx"/3 MXFP4."""
+    sparse selection, "mx"/3 MXFP4, 4 the projection's INT8/FP8 path."""
     cu = _cu_array(cu_seqlens)
     n = int(lib().h3attn_workspace_size(C.byref(params), _cu_ptr(cu), _mode(quantized)))
     if n == 0:
@@ -302,15 +309,17 @@ def h3attn_prologue(q, k, norm_w, rope_tables, cu_seqlens, q_hat=None, k_hat=Non
 
 
 def proj_raw(params, model_dim: int, x, x_stride: int, w_qkv, norm_w, rope_tables, cu_seqlens, out,
-             workspace, workspace_bytes, stream, stages: int = 3) -> int:
-    """Direct call of h3attn_fwd_proj (_stages when ``stages`` is not 3) with
-    integer device pointers; returns the status code."""
+             workspace, workspace_bytes, stream, stages: int = 3, quantized: bool = False) -> int:
+    """Direct call of h3attn_fwd_proj (h3attn_fwd_proj_q8 when ``quantized``;
+    _stages when ``stages`` is not 3) with integer device pointers; returns
+    the status code."""
     cu = _cu_array(cu_seqlens)
     args = (C.byref(params), int(model_dim), x, int(x_stride), w_qkv, norm_w, rope_tables, _cu_ptr(cu),
             out, workspace, workspace_bytes, stream)
+    name = "h3attn_fwd_proj_q8" if quantized else "h3attn_fwd_proj"
     if stages != 3:
-        return int(lib().h3attn_fwd_proj_stages(*args, int(stages)))
-    return int(lib().h3attn_fwd_proj(*args))
+        return int(getattr(lib(), name + "_stages")(*args, int(stages)))
+    return int(getattr(lib(), name)(*args))
 
 
 def _proj_params(x, w_qkv, num_heads: int, head_dim: int, num_seqs: int, o_stride: int, eps, softmax_scale):
@@ -324,10 +333,11 @@ def _proj_params(x, w_qkv, num_heads: int, head_dim: int, num_seqs: int, o_strid
 
 def h3attn_fwd_proj(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: int, head_dim: int, out=None,
                     workspace=None, eps: float = 1e-6, softmax_scale: float = 0.0, stream=None,
-                    stages: int = 3):
+                    stages: int = 3, quantized: bool = False):
     """out[N, H, d] (bf16) = attention of the fused QKV projection of hidden
     states x [N, D] (bf16) by w_qkv [3*H*d, D] (bf16), with the RMSNorm + RoPE
-    prologue (include/h3attn.h, h3attn_fwd_proj)."""
+    prologue (include/h3attn.h, h3attn_fwd_proj); with ``quantized`` the
+    INT8/FP8 path with its prologue in the projection (h3attn_fwd_proj_q8)."""
     import torch
     N, D = x.shape
     if out is None:
@@ -335,10 +345,11 @@ def h3attn_fwd_proj(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: int, h
     cu = _cu_array(cu_seqlens)
     params = _proj_params(x, w_qkv, num_heads, head_dim, len(cu) - 1, out.stride(0), eps, softmax_scale)
     if workspace is None:
-        workspace = _empty(stream, (h3attn_workspace_size(params, cu),), torch.uint8, x.device)
+        workspace = _empty(stream, (h3attn_workspace_size(params, cu, 4 if quantized else 0),), torch.uint8,
+                           x.device)
     _check(proj_raw(params, D, _dev_ptr(x), x.stride(0), _dev_ptr(w_qkv), _dev_ptr(norm_w),
                     _dev_ptr(rope_tables), cu, _dev_ptr(out), _dev_ptr(workspace),
-                    workspace.numel() * workspace.element_size(), _stream_ptr(stream), stages))
+                    workspace.numel() * workspace.element_size(), _stream_ptr(stream), stages, quantized))
     return out
 
 
@@ -354,6 +365,28 @@ def h3attn_proj_prologue(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: i
                                       _dev_ptr(norm_w), _dev_ptr(rope_tables), _cu_ptr(cu),
                                       *[_dev_ptr(t) for t in res], _stream_ptr(stream)))
     return tuple(res)
+
+
+def h3attn_proj_q8_prologue(x, w_qkv, norm_w, rope_tables, cu_seqlens, num_heads: int, head_dim: int,
+                            workspace=None, eps: float = 1e-6, stream=None):
+    """Stage 1 of h3attn_fwd_proj_q8 exported like h3attn_q8_prologue (see include/h3attn.h)."""
+    import torch
+    N, D = x.shape
+    cu = _cu_array(cu_seqlens)
+    S = len(cu) - 1
+    H, d = num_heads, head_dim
+    nblocks = int(sum((int(cu[s + 1] - cu[s]) + 63) // 64 for s in range(S)))
+    params = _proj_params(x, w_qkv, H, d, S, H * d, eps, 0.0)
+    if workspace is None:
+        workspace = _empty(stream, (h3attn_workspace_size(params, cu, 4),), torch.uint8, x.device)
+    dev = x.device
+    res = _q8_outputs(stream, N, H, d, S, nblocks, dev)
+    _check(lib().h3attn_proj_q8_prologue(
+        C.byref(params), D, _dev_ptr(x), x.stride(0), _dev_ptr(w_qkv), _dev_ptr(norm_w), _dev_ptr(rope_tables),
+        _cu_ptr(cu), _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
+        *[_dev_ptr(res[n]) for n in ("q8", "k8", "q_scale", "k_scale", "k_mean", "v8", "v_scale")],
+        _stream_ptr(stream)))
+    return res
 
 
 def sparse_items(cu_seqlens, num_heads: int) -> int:
@@ -432,6 +465,19 @@ def h3attn_out_proj(attn, w_o, cu_seqlens, gate=None, resid=None, out=None, stre
     return out
 
 
+def _q8_outputs(stream, N: int, H: int, d: int, S: int, nblocks: int, dev):
+    import torch
+    return {
+        "q8": _empty(stream, (N, H, d), torch.int8, dev),
+        "k8": _empty(stream, (N, H, d), torch.int8, dev),
+        "q_scale": _empty(stream, (H, nblocks), torch.float32, dev),
+        "k_scale": _empty(stream, (H, nblocks), torch.float32, dev),
+        "k_mean": _empty(stream, (S, H, d), torch.float32, dev),
+        "v8": _empty(stream, (N, H, d), torch.uint8, dev),
+        "v_scale": _empty(stream, (S, H, d), torch.float32, dev),
+    }
+
+
 def h3attn_q8_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,
                        eps: float = 1e-6, stream=None):
     """Quantised prologue exported in natural layouts (see include/h3attn.h)."""
@@ -443,16 +489,7 @@ def h3attn_q8_prologue(q, k, v, norm_w, rope_tables, cu_seqlens, workspace=None,
     params = params_for(q, k, v, q, S, eps)
     if workspace is None:
         workspace = _empty(stream, (h3attn_workspace_size(params, cu, True),), torch.uint8, q.device)
-    dev = q.device
-    res = {
-        "q8": _empty(stream, (N, H, d), torch.int8, dev),
-        "k8": _empty(stream, (N, H, d), torch.int8, dev),
-        "q_scale": _empty(stream, (H, nblocks), torch.float32, dev),
-        "k_scale": _empty(stream, (H, nblocks), torch.float32, dev),
-        "k_mean": _empty(stream, (S, H, d), torch.float32, dev),
-        "v8": _empty(stream, (N, H, d), torch.uint8, dev),
-        "v_scale": _empty(stream, (S, H, d), torch.float32, dev),
-    }
+    res = _q8_outputs(stream, N, H, d, S, nblocks, q.device)
     _check(lib().h3attn_q8_prologue(
         C.byref(params), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(norm_w),
         _dev_ptr(rope_tables), _cu_ptr(cu), _dev_ptr(workspace),

@@ -81,8 +81,9 @@ typedef struct h3attn_params {
 
 /*
  * Bytes of device workspace h3attn_fwd (quantized = 0), h3attn_fwd_q8
- * (quantized = 1), h3attn_fwd_sparse with its tile selection (quantized = 2)
- * or h3attn_fwd_mx (quantized = 3) needs for this shape.  cu_seqlens_host: HOST int32 [S+1],
+ * (quantized = 1), h3attn_fwd_sparse with its tile selection (quantized = 2),
+ * h3attn_fwd_mx (quantized = 3) or h3attn_fwd_proj_q8 (quantized = 4) needs
+ * for this shape.  cu_seqlens_host: HOST int32 [S+1],
  * cu[0] = 0, non-decreasing; N = cu[S] is the packed token count.  Returns 0
  * and sets the last error when the arguments are invalid.
  */
@@ -291,6 +292,49 @@ h3attn_status h3attn_proj_prologue(const h3attn_params *p, int32_t model_dim, co
                                    int64_t x_stride, const void *w_qkv, const float *norm_w,
                                    const float *rope_tables, const int32_t *cu_seqlens_host,
                                    void *q_hat, void *k_hat, void *v_out, void *stream);
+
+/*
+ * The QKV projection with the quantised prologue of h3attn_fwd_q8 in its
+ * epilogue, then the quantised attention.  The page "Buyer Questions: Current
+ * Evidence Status" (question 4) counts the block's GEMMs and its scale/pack
+ * work beside attention; the pages give no formula, so this is h3attn_fwd_q8
+ * applied to the projection of h3attn_fwd_proj, with that entry point's
+ * precision: q and k are normalised and rotated in fp32 from the fp32
+ * accumulators (never rounded to bf16), v is rounded to bf16 once.  The
+ * projection's epilogue codes qhat to INT8 (one scale per 64-token block of a
+ * head, amax / 127, as h3attn_fwd_q8), writes khat in fp32 and v in bf16 to
+ * the workspace; the K means, V scales and the K / V codes are then formed as
+ * in h3attn_fwd_q8, and the attention is that entry point's.
+ *   head_dim 128 only (else H3ATTN_ERR_UNSUPPORTED);
+ *   workspace >= h3attn_workspace_size(p, cu, 4) bytes;
+ *   all other arguments and conventions as h3attn_fwd_proj.
+ */
+h3attn_status h3attn_fwd_proj_q8(const h3attn_params *p, int32_t model_dim, const void *x, int64_t x_stride,
+                                 const void *w_qkv, const float *norm_w, const float *rope_tables,
+                                 const int32_t *cu_seqlens_host, void *out, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* The two stages of h3attn_fwd_proj_q8 (1: projection + quantised prologue
+ * into the workspace, 2: attention, 3: both); same contract as
+ * h3attn_fwd_stages. */
+h3attn_status h3attn_fwd_proj_q8_stages(const h3attn_params *p, int32_t model_dim, const void *x,
+                                        int64_t x_stride, const void *w_qkv, const float *norm_w,
+                                        const float *rope_tables, const int32_t *cu_seqlens_host,
+                                        void *out, void *workspace, size_t workspace_bytes,
+                                        void *stream, int stages);
+
+/*
+ * Diagnostic: stage 1 of h3attn_fwd_proj_q8 exported in natural layouts, with
+ * the outputs and layouts of h3attn_q8_prologue (q8, k8, q_scale, k_scale,
+ * k_mean, v8, v_scale).  Runs the same kernels into `workspace` (>=
+ * h3attn_workspace_size(p, cu, 4) bytes), then copies out.
+ */
+h3attn_status h3attn_proj_q8_prologue(const h3attn_params *p, int32_t model_dim, const void *x,
+                                      int64_t x_stride, const void *w_qkv, const float *norm_w,
+                                      const float *rope_tables, const int32_t *cu_seqlens_host,
+                                      void *workspace, size_t workspace_bytes, int8_t *q8, int8_t *k8,
+                                      float *q_scale, float *k_scale, float *k_mean, uint8_t *v8,
+                                      float *v_scale, void *stream);
 
 /*
  * Output projection of the attention output with the gated residual of a

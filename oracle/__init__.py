@@ -183,15 +183,20 @@ class Problem:
                    inputs["norm_w"], theta=w.theta, eps=w.eps, **kw)
 
     @classmethod
-    def from_projection(cls, w, inputs, proj=None, **kw):
+    def from_projection(cls, w, inputs, proj=None, round_v: bool = False, **kw):
         """The problem whose q, k, v are the fp64 QKV projection of the
         hidden states inputs["x"] by inputs["w_qkv"] (``project``); ``proj``
-        may pass that projection in when it is already computed."""
+        may pass that projection in when it is already computed.  With
+        ``round_v`` v is that projection rounded to bf16 (to nearest, ties to
+        even): the quantised projection path stores v in bf16 before coding it
+        in FP8, and its FP8 coding takes bf16 v like the quantised path's."""
         if proj is None:
             proj = project(inputs["x"], inputs["w_qkv"])
         hd = w.H * w.d
         assert proj.shape == (w.N, 3 * hd)
         q, k, v = (proj[:, i * hd:(i + 1) * hd].reshape(w.N, w.H, w.d) for i in range(3))
+        if round_v:
+            v = _bf16_bits_rne(v)
         return cls(w.H, w.d, w.seqs, w.split, q, k, v, inputs["norm_w"], theta=w.theta, eps=w.eps, **kw)
 
     # -- queries -----------------------------------------------------------
@@ -498,11 +503,15 @@ def out_proj(attn, w_o, cu_seqlens, gate=None, resid=None, rows=None, chunk: int
     return out
 
 
+def _bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """bf16 bits of fp64 values rounded to nearest, ties to even (via fp32)."""
+    f = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((f + np.uint32(0x7FFF) + ((f >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
 def _round_bf16(x: np.ndarray) -> np.ndarray:
     """fp64 values rounded to bf16 (to nearest, ties to even) and back, via fp32."""
-    f = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = ((f + np.uint32(0x7FFF) + ((f >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)) << np.uint32(16)
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return _bf16_bits_to_f64(_bf16_bits_rne(x))
 
 
 def _bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:

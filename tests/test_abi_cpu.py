@@ -273,12 +273,12 @@ def test_fp4_prologue_export_errors():
 
 
 def _proj_call(params=None, model_dim=3072, x_stride=3072, cu=(0, 1000), ws_bytes=1 << 40, ptrs=None,
-               stages=3):
+               stages=3, quantized=False):
     params = params if params is not None else _params()
     p = dict(x=FAKE, w=FAKE, norm_w=FAKE, rope=FAKE, out=FAKE, ws=FAKE * 256)
     p.update(ptrs or {})
     return h.proj_raw(params, model_dim, p["x"], x_stride, p["w"], p["norm_w"], p["rope"], np.array(cu, np.int32),
-                      p["out"], p["ws"], ws_bytes, None, stages)
+                      p["out"], p["ws"], ws_bytes, None, stages, quantized)
 
 
 @pytest.mark.parametrize("kw,msg,code", [
@@ -295,21 +295,55 @@ def _proj_call(params=None, model_dim=3072, x_stride=3072, cu=(0, 1000), ws_byte
     (dict(ws_bytes=4096), "needs", h.H3ATTN_ERR_WORKSPACE),
     (dict(params=_params(num_heads=0)), "num_heads", h.H3ATTN_ERR_INVALID_ARG),
 ])
-def test_projection_argument_errors(kw, msg, code):
-    assert _proj_call(**kw) == code
+@pytest.mark.parametrize("quantized", [False, True])
+def test_projection_argument_errors(kw, msg, code, quantized):
+    assert _proj_call(quantized=quantized, **kw) == code
     assert msg in h.last_error()
 
 
-def test_projection_ignores_qkv_strides_and_accepts_empty_input():
+@pytest.mark.parametrize("quantized", [False, True])
+def test_projection_ignores_qkv_strides_and_accepts_empty_input(quantized):
     # the q/k/v strides of the params are not read by the projection entry points
     p = _params(q_stride=8, k_stride=8, v_stride=8)
-    assert _proj_call(p, cu=(0, 0)) == h.H3ATTN_OK
-    assert _proj_call(p, cu=(0, 0), ptrs={"x": 0, "w": 0}) == h.H3ATTN_OK    # N = 0 reads nothing
+    assert _proj_call(p, cu=(0, 0), quantized=quantized) == h.H3ATTN_OK
+    assert _proj_call(p, cu=(0, 0), ptrs={"x": 0, "w": 0}, quantized=quantized) == h.H3ATTN_OK
 
 
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device error path; a GPU is present")
-def test_projection_valid_call_without_gpu_reports_device_error():
-    assert _proj_call() == h.H3ATTN_ERR_DEVICE
+@pytest.mark.parametrize("quantized", [False, True])
+def test_projection_valid_call_without_gpu_reports_device_error(quantized):
+    assert _proj_call(quantized=quantized) == h.H3ATTN_ERR_DEVICE
+
+
+def test_quantised_projection_workspace_and_head_dim():
+    """h3attn_fwd_proj_q8 takes workspace mode 4: the INT8/FP8 regions plus
+    fp32 khat and bf16 v of every padded token; head_dim 128 only."""
+    p = _params()
+    q8 = h.h3attn_workspace_size(p, [0, 1000], True)
+    q8p = h.h3attn_workspace_size(p, [0, 1000], 4)
+    assert q8p - q8 >= 24 * 1024 * 128 * (4 + 2)
+    assert _proj_call(ws_bytes=q8, quantized=True) == h.H3ATTN_ERR_WORKSPACE and "needs" in h.last_error()
+    p64 = _params(head_dim=64, q_stride=1536, k_stride=1536, v_stride=1536, o_stride=1536)
+    assert _proj_call(p64, quantized=True) == h.H3ATTN_ERR_UNSUPPORTED and "head_dim 128" in h.last_error()
+    with pytest.raises(h.H3AttnError):
+        h.h3attn_workspace_size(p64, [0, 1000], 4)
+    with pytest.raises(h.H3AttnError):
+        h.h3attn_workspace_size(p, [0, 1000], 5)
+
+
+def test_quantised_projection_prologue_export_errors():
+    import ctypes as C
+    L = h.lib()
+    cu = np.array([0, 1000], np.int32)
+    outs = [FAKE] * 7
+    args = lambda o: (C.byref(_params()), 3072, FAKE, 3072, FAKE, FAKE, FAKE, cu.ctypes.data_as(C.POINTER(C.c_int32)),
+                      FAKE * 256, 1 << 40, *o, None)
+    names = ("q8", "k8", "q_scale", "k_scale", "k_mean", "v8", "v_scale")
+    for i in range(7):      # every output is checked before any device call
+        o = list(outs)
+        o[i] = 0
+        assert L.h3attn_proj_q8_prologue(*args(o)) == h.H3ATTN_ERR_INVALID_ARG
+        assert names[i] in h.last_error() and "NULL" in h.last_error()
 
 
 def _out_call(H=24, d=128, D=3072, cu=(0, 1000), attn_stride=3072, resid_stride=3072, out_stride=3072,
@@ -385,7 +419,7 @@ def test_sparse_workspace_sizes():
     assert h.sparse_items([0, 1000, 1000, 1129], 24) == 24 * 4 + 24 * 1     # 256-row blocks
     assert h.SPARSE_BLOCK_ROWS == oracle.SPARSE_BLOCK
     with pytest.raises(h.H3AttnError):
-        h.h3attn_workspace_size(p, [0, 1000], 4)
+        h.h3attn_workspace_size(p, [0, 1000], 5)
 
 
 def test_injected_launch_failure_reports_hip_error(monkeypatch):
@@ -401,6 +435,8 @@ def test_injected_launch_failure_reports_hip_error(monkeypatch):
         (lambda: _call(quantized="mx"), "FP4 prologue launch"),
         (lambda: _call(quantized="mx", stages=2), "FP4 attention launch"),
         (lambda: _proj_call(), "projection launch"),
+        (lambda: _proj_call(quantized=True), "projection launch"),
+        (lambda: _proj_call(quantized=True, stages=2), "quantised attention launch"),
         (lambda: _out_call(), "output projection launch"),
         (lambda: _sparse_call(), "prologue launch"),
         (lambda: _sparse_call(stages=4), "sparse attention launch"),

@@ -1,0 +1,195 @@
+"""GPU parity of the projection's quantised path (h3attn_fwd_proj_q8,
+h3attn_proj_q8_prologue) against the oracle: the fp64 QKV projection
+(``oracle.project``) with v rounded to bf16 (``round_v``), then the quantised
+path's quantisers and its step-by-step emulation.
+
+Stage parity, as for h3attn_q8_prologue: INT8 codes of qhat and of khat - mean
+equal away from rounding boundaries (the GPU forms the values being rounded in
+fp32 from its fp32 product, the oracle in fp64), scales and K means to fp32
+rounding.  v is rounded to bf16 by the GPU from its fp32 product and by the
+oracle from its fp64 one; where the product lies within the fp32 error of a
+bf16 rounding midpoint the two take neighbouring bf16 values, so an FP8 code
+of v may differ by one step at such a value (at most 1e-4 of the codes) and a
+V scale by one bf16 step of its maximum.
+
+End to end: every output row of the small cases against the exact fp64
+attention of the projection (the quantised tolerance) and against the
+oracle's emulation of the quantised path (its tighter gate).  Small cases
+cover ragged and empty sequences, audio tokens, model dims of 1, 3 and 5
+pipeline slabs, an odd number of d-feature blocks (3 heads) and hidden states
+read through a token stride wider than the model dim.  The 125,242-token joint
+layer (D = 3072, 24 heads) on sampled rows of two heads.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from audio_diffusion_transformer_amd import h3attn as h
+from audio_diffusion_transformer_amd import synth
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+Seq = synth.Seq
+
+SMALL = {
+    "pq8_ragged_D160": synth.Workload(
+        "pq8_ragged_D160", H=2, d=128, seqs=(Seq(2, 8, 9, 37), Seq(0, 1, 1), Seq(1, 3, 3), Seq(0, 1, 1, 5)),
+        split=(32, 48, 48), seed=61, model_dim=160),
+    "pq8_long_D96": synth.Workload(
+        "pq8_long_D96", H=2, d=128, seqs=(Seq(4, 15, 18, 20),), split=(32, 48, 48), seed=62, model_dim=96),
+    "pq8_three_heads_D32": synth.Workload(
+        "pq8_three_heads_D32", H=3, d=128, seqs=(Seq(3, 7, 9), Seq(1, 2, 5, 9)), split=(32, 48, 48), seed=63,
+        model_dim=32),
+}
+X_PAD = {"pq8_ragged_D160": 24}     # extra elements per x row
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+def _upload(w, inp, torch):
+    t = G.to_device(inp, w)
+    pad = X_PAD.get(w.name, 0)
+    x = t["x"]
+    if pad:
+        wide = torch.zeros((w.N, w.model_dim + pad), dtype=torch.bfloat16, device=x.device)
+        wide[:, :w.model_dim] = x
+        x = wide[:, :w.model_dim]
+        assert x.stride(0) == w.model_dim + pad
+    return t, x
+
+
+def _run(torch, w, t, x, label):
+    G.announce("%s workload=%s seed=%d N=%d H=%d d=%d D=%d x_stride=%d entry=h3attn_fwd_proj_q8" % (
+        label, w.name, w.seed, w.N, w.H, w.d, w.model_dim, x.stride(0)))
+    o = h.h3attn_fwd_proj(x, t["w_qkv"], t["norm_w"], t["rope"], t["cu"], w.H, w.d, eps=w.eps, quantized=True)
+    torch.cuda.synchronize()
+    return G.bits(o)
+
+
+def _int8_codes_match(got, codes, ratio, label):
+    diff = got.astype(np.int32) - codes.astype(np.int32)
+    frac = np.abs(ratio - np.floor(ratio) - 0.5)          # distance of the ratio to a tie
+    boundary = frac < 2e-3
+    bad = (diff != 0) & ~(boundary & (np.abs(diff) == 1))
+    assert not bad.any(), "%s: %d INT8 codes differ away from a rounding boundary" % (label, int(bad.sum()))
+    assert boundary.mean() < 1e-2, label
+    return int((diff != 0).sum())
+
+
+def _sub_problems(w, inp, heads):
+    """The oracle's projection problems restricted to `heads` (heads are
+    independent): v rounded to bf16 (the quantised path's) and exact."""
+    hd = w.H * w.d
+    sel = np.concatenate([part * hd + hh * w.d + np.arange(w.d) for part in range(3) for hh in heads])
+    ws = w.replace(H=len(heads))
+    sub = {"x": inp["x"], "w_qkv": np.ascontiguousarray(inp["w_qkv"][sel]),
+           "norm_w": np.ascontiguousarray(inp["norm_w"][:, heads])}
+    proj = oracle.project(sub["x"], sub["w_qkv"])
+    return (oracle.Problem.from_projection(ws, sub, proj=proj, round_v=True),
+            oracle.Problem.from_projection(ws, sub, proj=proj))
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_quantised_projection_stage(torch_dev, name):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t, x = _upload(w, inp, torch_dev)
+    G.announce("proj q8 prologue %s x_stride=%d" % (name, x.stride(0)))
+    res = h.h3attn_proj_q8_prologue(x, t["w_qkv"], t["norm_w"], t["rope"], t["cu"], w.H, w.d, eps=w.eps)
+    torch_dev.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in res.items()}
+    p = oracle.Problem.from_projection(w, inp, round_v=True)
+    km = p.q8_kmean()
+    np.testing.assert_allclose(g["k_mean"], km, rtol=0, atol=2e-5)
+    cu = inp["cu_seqlens"]
+    nblk = [(int(cu[s + 1] - cu[s]) + 63) // 64 for s in range(w.S)]
+    bpre = np.concatenate([[0], np.cumsum(nblk)])
+    changed, v_off, v_total = 0, 0, 0
+    dec = np.vectorize(oracle.e4m3_decode)
+    for s in range(w.S):
+        for hd in range(w.H):
+            for b in range(nblk[s]):
+                toks = np.arange(cu[s] + 64 * b, min(cu[s] + 64 * b + 64, cu[s + 1]))
+                for which, key in ((0, "q"), (1, "k")):
+                    scale, ratio, codes = p.q8_block_quant(which, s, hd, b, kmean=km)
+                    gs = g[key + "_scale"][hd, bpre[s] + b]
+                    assert gs == pytest.approx(scale, rel=2e-5), (name, key, s, hd, b)
+                    changed += _int8_codes_match(g[key + "8"][toks, hd], codes, ratio,
+                                                 "%s %s s%d h%d b%d" % (name, key, s, hd, b))
+            if cu[s + 1] > cu[s]:
+                vs, vr, vc = p.q8_v_quant(s, hd)
+                np.testing.assert_allclose(g["v_scale"][s, hd], vs, rtol=2.0 ** -7)
+                gc = g["v8"][cu[s]:cu[s + 1], hd]
+                gv, ov = dec(gc), dec(vc)
+                tie = np.abs(vr - 0.5 * (gv + ov)) <= 1e-5 * np.abs(vr) + 1e-12
+                off = (gc != vc) & ~tie
+                # a neighbouring bf16 v moves a code by at most one e4m3 step
+                assert np.all(np.abs(gv[off] - ov[off]) <= 2.0 ** -3 * np.abs(ov[off]) + 2.0 ** -9), name
+                v_off += int(off.sum())
+                v_total += gc.size
+    assert v_off <= max(1, int(1e-4 * v_total)), "%s: %d of %d FP8 codes of v differ" % (name, v_off, v_total)
+    G.announce("%s: %d INT8 codes at rounding boundaries, %d FP8 codes of v off by a bf16 step" % (
+        name, changed, v_off))
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_quantised_projection_attention_all_rows(torch_dev, name):
+    w = SMALL[name]
+    inp = synth.generate(w)
+    t, x = _upload(w, inp, torch_dev)
+    out = _run(torch_dev, w, t, x, name)
+    rows = np.arange(w.N * w.H, dtype=np.int64)
+    got = G.gpu_rows(out, rows, w.H)
+    exact = oracle.Problem.from_projection(w, inp).attention_rows(rows, nthreads=G.oracle_threads())
+    G.check(G.metrics(got, exact), G.Q8_GATE, name)
+    emu = oracle.Problem.from_projection(w, inp, round_v=True).q8_attention_rows(rows, nthreads=G.oracle_threads())
+    G.check(G.metrics(got, emu), G.Q8_EMULATION_GATE, name + " vs emulation")
+
+
+def test_quantised_projection_stages_equal_single_call(torch_dev):
+    """Stage 1 (projection + quantised prologue) then stage 2 (attention) on
+    one workspace equal the single call bit for bit, and a repeat call is
+    bit-identical (no state carried over)."""
+    w = SMALL["pq8_long_D96"]
+    inp = synth.generate(w)
+    t, x = _upload(w, inp, torch_dev)
+    one = _run(torch_dev, w, t, x, "pq8 single call")
+    again = _run(torch_dev, w, t, x, "pq8 repeat call")
+    np.testing.assert_array_equal(one, again)
+    ws = torch_dev.empty((h.h3attn_workspace_size(
+        h.make_params(w.H, w.d, w.S, w.H * w.d, w.H * w.d, w.H * w.d, w.H * w.d, w.eps, 0.0),
+        inp["cu_seqlens"], 4),), dtype=torch_dev.uint8, device="cuda:0")
+    out = torch_dev.empty((w.N, w.H, w.d), dtype=torch_dev.bfloat16, device="cuda:0")
+    for st in (1, 2):
+        G.announce("pq8 stage %d" % st)
+        h.h3attn_fwd_proj(x, t["w_qkv"], t["norm_w"], t["rope"], t["cu"], w.H, w.d, out=out, workspace=ws,
+                          eps=w.eps, stages=st, quantized=True)
+    torch_dev.cuda.synchronize()
+    np.testing.assert_array_equal(G.bits(out), one)
+
+
+def test_quantised_projection_full_layer_sampled(torch_dev):
+    # the whole 24-head layer on the GPU (the bench shape); the oracle takes
+    # two heads: 192 sampled tokens of each, against exact attention and the
+    # emulation
+    w = synth.WORKLOADS["proj_joint"].replace(name="proj_joint_q8")
+    heads = [4, 19]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = _run(torch_dev, w, t, t["x"], w.name)
+    del t
+    p, pe = _sub_problems(w, inp, heads)
+    rng = np.random.default_rng(8)
+    toks = np.sort(rng.choice(w.N, 192, replace=False))
+    toks[0], toks[-1] = 0, w.N - 1
+    rows_sub = (toks[:, None] * len(heads) + np.arange(len(heads))[None, :]).reshape(-1)
+    got = G.decode(out[toks][:, heads]).reshape(-1, w.d)
+    emu = p.q8_attention_rows(rows_sub, nthreads=G.oracle_threads())
+    G.check(G.metrics(got, emu), G.Q8_EMULATION_GATE, w.name + " vs emulation")
+    exact = pe.attention_rows(rows_sub, nthreads=G.oracle_threads())
+    G.check(G.metrics(got, exact), G.Q8_GATE, w.name)

@@ -521,6 +521,33 @@ def test_projection_with_permutation_weights_equals_direct_inputs():
     np.testing.assert_array_equal(pp.attention_rows(rows), pd.attention_rows(rows))
 
 
+def test_quantised_projection_problem_equals_direct_inputs():
+    # round_v: permutation weights make the projection exact bf16 values, so v
+    # rounded to bf16 is the direct v bit for bit, and every quantiser of the
+    # quantised path (fed fp64 q, k from the projection) agrees with the bf16
+    # path on the same values
+    w, inp, direct = _permutation_projection()
+    pp = oracle.Problem.from_projection(w, inp, round_v=True, library=L())
+    pd = oracle.Problem(w.H, w.d, w.seqs, w.split, *direct, inp["norm_w"], library=L())
+    assert pp.v.dtype == np.uint16 and np.array_equal(pp.v, direct[2])
+    km = pp.q8_kmean()
+    np.testing.assert_array_equal(km, pd.q8_kmean())
+    for s in range(w.S):
+        n = int(pp.cu[s + 1] - pp.cu[s])
+        for hh in range(w.H):
+            for b in range((n + 63) // 64):
+                for which in (0, 1):
+                    a = pp.q8_block_quant(which, s, hh, b, kmean=km)
+                    c = pd.q8_block_quant(which, s, hh, b, kmean=km)
+                    for x, y in zip(a, c):
+                        np.testing.assert_array_equal(x, y)
+            if n:
+                for x, y in zip(pp.q8_v_quant(s, hh), pd.q8_v_quant(s, hh)):
+                    np.testing.assert_array_equal(x, y)
+    rows = np.arange(w.N * w.H)
+    np.testing.assert_array_equal(pp.q8_attention_rows(rows, kmean=km), pd.q8_attention_rows(rows, kmean=km))
+
+
 def test_projection_scale_leaves_qk_and_scales_output():
     # W -> 2W (exact in bf16): RMSNorm removes the factor from q and k, v doubles,
     # so the attention output doubles
