@@ -138,6 +138,11 @@ WORKLOADS: Dict[str, Workload] = {
         "proj_joint", H=24, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128, seed=1013,
         model_dim=3072,
         description="QKV projection (D=3072) + attention on the joint 125,242-token sequence, H=24"),
+    "proj_q8_joint": Workload(
+        "proj_q8_joint", H=24, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128, seed=1013,
+        model_dim=3072, quantized=True,
+        description="the proj_joint inputs on the quantised path: QKV projection (D=3072) with the INT8/FP8 "
+                    "prologue in its epilogue + INT8/FP8 attention, H=24"),
     "proj_joint_h3": Workload(
         "proj_joint_h3", H=3, d=128, seqs=(Seq(31, 48, 84, 250),), split=_SPLIT128, seed=1016,
         model_dim=3072,

@@ -15,9 +15,13 @@ the CPU oracle's throughput on a bounded sample of the same workload.
 
 With a projection workload (``--workload proj_joint``) a step starts from the
 hidden states: the fused QKV projection + prologue kernel, then the attention
-kernel (h3attn_fwd_proj_stages 1 and 2); the step's FLOP count adds the
-projection's 2 * N * D * 3*H*d, and the line also reports the projection
-kernel beside the vendor-library GEMM plus the separate prologue.
+kernel (h3attn_fwd_proj_stages 1 and 2), then the output projection with its
+gated residual; the step's FLOP count adds the projections' 2 * N * D * 3*H*d
+and 2 * N * H*d * D, and the line also reports the projection kernel beside
+the vendor-library GEMM plus the separate prologue.  ``--workload
+proj_q8_joint`` runs the same layer on the quantised path
+(h3attn_fwd_proj_q8_stages: the projection with the INT8/FP8 prologue, then
+the INT8/FP8 attention).
 """
 from __future__ import annotations
 
@@ -280,7 +284,8 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
 def library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream, reps: int = 5):
     """The unfused alternative, timed after the timed region: the QKV product on
     the vendor library (torch.mm, hipBLASLt) into a bf16 [N, 3*H*d] buffer,
-    then this library's prologue reading q, k and v as strided views of it."""
+    then this library's prologue (the quantised one for a quantised workload)
+    reading q, k and v as strided views of it."""
     hd = w.H * w.d
     y = torch.empty((w.N, 3 * hd), dtype=torch.bfloat16, device=x.device)
     wt = wq.t()
@@ -288,9 +293,11 @@ def library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_byte
     out = torch.empty((w.N, w.H, w.d), dtype=torch.bfloat16, device=x.device)
     params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
     ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
+    assert ws_bytes >= h.h3attn_workspace_size(params, cu, w.quantized)
 
     def prologue():
-        st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, int(stream.cuda_stream), False, 1)
+        st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, int(stream.cuda_stream),
+                       w.quantized, 1)
         if st != 0:
             raise RuntimeError(h.last_error())
 
@@ -429,7 +436,7 @@ def main():
         params = h.params_for(q, k, v, out, len(cu) - 1, w.eps)
         ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), norm_w.data_ptr(), rope.data_ptr()]
     mode = "mx" if w.fp4 else w.quantized
-    ws_bytes = h.h3attn_workspace_size(params, cu, 2 if sparse else mode)
+    ws_bytes = h.h3attn_workspace_size(params, cu, 2 if sparse else 4 if (proj and w.quantized) else mode)
     if sparse:
         tiles = torch.empty((h.sparse_items(cu, w.H), w.keep_tiles), dtype=torch.int32, device=dev)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -459,7 +466,7 @@ def main():
                                 gate.data_ptr(), resid.data_ptr(), resid.stride(0), y.data_ptr(), y.stride(0), sp)
         elif proj:
             st = h.proj_raw(params, w.model_dim, x.data_ptr(), x.stride(0), wq.data_ptr(), norm_w.data_ptr(),
-                            rope.data_ptr(), cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp, sid)
+                            rope.data_ptr(), cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp, sid, w.quantized)
         else:
             st = h.fwd_raw(params, *ptrs, cu, out.data_ptr(), ws.data_ptr(), ws_bytes, sp, mode, sid)
         if st != 0:
@@ -528,6 +535,14 @@ def main():
         pro_bytes = 4 * N * H * d * 2 + 2 * N * (d // 2) * 8 + 3 * N * H * d // 2 + 3 * N * H * d // 32
         metric = ("attention TFLOP/s (MXFP4 QK and PV) and %% of fp4 MFMA peak at N=%d packed tokens, "
                   "H=%d, d=%d" % (N, H, d))
+    elif w.quantized and proj:
+        # the projection reads x, W and the table and writes q8, fp32 khat and bf16 v;
+        # pass 1 and pass 3 each read khat and v, pass 3 writes k8 and v8
+        pro_bytes = (N * w.model_dim * 2 + 3 * H * d * w.model_dim * 2 + N * (d // 2) * 8
+                     + N * H * d * (1 + 4 + 2) + 2 * N * H * d * (4 + 2) + 2 * N * H * d)
+        metric = ("attention layer on the quantised path (QKV projection with the INT8/FP8 prologue, INT8/FP8 "
+                  "attention, output projection with gated residual; D=%d) TFLOP/s at N=%d packed tokens, "
+                  "H=%d, d=%d" % (w.model_dim, N, H, d))
     elif w.quantized:
         # pass 1 reads q, k, v and the table and writes q8; pass 3 re-reads k, v and the
         # table and writes k8 and v8 (per-tile scales and sums are negligible)
