@@ -71,7 +71,10 @@ def test_attention_entry_points_replay(torch_dev, path):
     _replays(torch, fn, out, "graph " + path)
 
 
-def test_layer_entry_points_replay(torch_dev):
+@pytest.mark.parametrize("quantized", [False, True])
+def test_layer_entry_points_replay(torch_dev, quantized):
+    """The projection (bf16, or with the quantised prologue), the attention and
+    the output projection captured as one graph."""
     torch = torch_dev
     w = synth.Workload("graph_layer", H=2, d=128, seqs=(Seq(2, 8, 9, 37), Seq(1, 3, 3)), split=(32, 48, 48),
                        seed=62, model_dim=256)
@@ -82,15 +85,17 @@ def test_layer_entry_points_replay(torch_dev):
     o = torch.empty((w.N, w.H, w.d), dtype=torch.bfloat16, device="cuda:0")
     y = torch.empty((w.N, w.model_dim), dtype=torch.bfloat16, device="cuda:0")
     params = h._proj_params(t["x"], t["w_qkv"], w.H, w.d, w.S, o.stride(0), w.eps, 0.0)
-    ws = torch.empty(h.h3attn_workspace_size(params, inp["cu_seqlens"]), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(h.h3attn_workspace_size(params, inp["cu_seqlens"], 4 if quantized else 0), dtype=torch.uint8,
+                     device="cuda:0")
 
     def fn():
         s = torch.cuda.current_stream()
         h.h3attn_fwd_proj(t["x"], t["w_qkv"], t["norm_w"], t["rope"], t["cu"], w.H, w.d, out=o, workspace=ws,
-                          eps=w.eps, stream=s)
+                          eps=w.eps, stream=s, quantized=quantized)
         h.h3attn_out_proj(o, w_o, t["cu"], gate=gate, resid=resid, out=y, stream=s)
 
-    G.announce("graph layer eager")
+    label = "graph layer%s" % (" q8" if quantized else "")
+    G.announce(label + " eager")
     fn()
     torch.cuda.synchronize()
-    _replays(torch, fn, y, "graph layer")
+    _replays(torch, fn, y, label)
