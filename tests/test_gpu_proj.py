@@ -9,7 +9,10 @@ unit roundoff of its 8-bit significand; the fp32 matrix product and the fp32
 norm and rotation add a few 1e-6 absolute).  End to end: the attention output at the bf16
 gates.  Small cases cover every token and row: ragged and empty sequences,
 audio tokens, both head dims, model dims of 1, 2, 3 and 5 pipeline slabs and
-hidden states read through a token stride wider than the model dim.  The
+hidden states read through a token stride wider than the model dim, and at
+head dim 128 model dims of 2 and 6 slabs (64, 192), the latter with three
+heads (an odd number of feature blocks, so the last workgroup's second block
+is absent).  The
 125,242-token joint shape is checked on sampled rows (all three heads of one
 GPU's share, and four of the 24 heads of the whole layer).
 """
@@ -34,11 +37,17 @@ SMALL = {
     "proj_two_slabs_D64_long": synth.Workload(
         "proj_two_slabs_D64_long", H=2, d=128, seqs=(Seq(4, 15, 18, 20),), split=(32, 48, 48), seed=33,
         model_dim=64),
+    "proj_ragged_d128_D192_h3": synth.Workload(
+        "proj_ragged_d128_D192_h3", H=3, d=128, seqs=(Seq(2, 8, 9, 37), Seq(0, 1, 1), Seq(1, 5, 7, 3)),
+        split=(32, 48, 48), seed=35, model_dim=192),
+    "proj_one_slab_D64": synth.Workload(
+        "proj_one_slab_D64", H=2, d=128, seqs=(Seq(3, 9, 11),), split=(32, 48, 48), seed=36, model_dim=64),
     "proj_three_slabs_D96_d64": synth.Workload(
         "proj_three_slabs_D96_d64", H=3, d=64, seqs=(Seq(2, 6, 10, 3), Seq(1, 5, 5)), split=(16, 24, 24),
         seed=34, model_dim=96),
 }
-X_PAD = {"proj_three_slabs_D96_d64": 64, "proj_ragged_d128_D160": 8}   # extra elements per x row
+X_PAD = {"proj_three_slabs_D96_d64": 64, "proj_ragged_d128_D160": 8,   # extra elements per x row
+         "proj_ragged_d128_D192_h3": 40}
 
 
 @pytest.fixture(scope="module")

@@ -15,9 +15,9 @@ V scale by one bf16 step of its maximum.
 End to end: every output row of the small cases against the exact fp64
 attention of the projection (the quantised tolerance) and against the
 oracle's emulation of the quantised path (its tighter gate).  Small cases
-cover ragged and empty sequences, audio tokens, model dims of 1, 3 and 5
-pipeline slabs, an odd number of d-feature blocks (3 heads) and hidden states
-read through a token stride wider than the model dim.  The 125,242-token joint
+cover ragged and empty sequences, audio tokens, model dims of 1, 2, 3, 5 and 6
+pipeline slabs (32 to 192), an odd number of d-feature blocks (3 heads) and
+hidden states read through a token stride wider than the model dim.  The 125,242-token joint
 layer (D = 3072, 24 heads) on sampled rows of two heads.
 """
 import numpy as np
@@ -40,8 +40,13 @@ SMALL = {
     "pq8_three_heads_D32": synth.Workload(
         "pq8_three_heads_D32", H=3, d=128, seqs=(Seq(3, 7, 9), Seq(1, 2, 5, 9)), split=(32, 48, 48), seed=63,
         model_dim=32),
+    "pq8_ragged_D192_h3": synth.Workload(
+        "pq8_ragged_D192_h3", H=3, d=128, seqs=(Seq(2, 8, 9, 37), Seq(0, 1, 1), Seq(1, 5, 7, 3)),
+        split=(32, 48, 48), seed=64, model_dim=192),
+    "pq8_one_slab_D64": synth.Workload(
+        "pq8_one_slab_D64", H=2, d=128, seqs=(Seq(3, 9, 11),), split=(32, 48, 48), seed=65, model_dim=64),
 }
-X_PAD = {"pq8_ragged_D160": 24}     # extra elements per x row
+X_PAD = {"pq8_ragged_D160": 24, "pq8_ragged_D192_h3": 40}     # extra elements per x row
 
 
 @pytest.fixture(scope="module")
