@@ -66,6 +66,71 @@ def measured_traffic(kernel_file: str, summary: str):
     return float(t.group(1))
 
 
+def _sha256_file(path: str) -> str:
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        for blk in iter(lambda: f.read(1 << 20), b""):
+            h.update(blk)
+    return h.hexdigest()
+
+
+def _input_digest(arrays) -> str:
+    """xxh3-64 (blake2b when xxhash is absent) over the input arrays' bytes, in order."""
+    try:
+        import xxhash
+        h, kind = xxhash.xxh3_64(), "xxh3_64"
+    except ImportError:
+        h, kind = hashlib.blake2b(digest_size=8), "blake2b-64"
+    for a in arrays:
+        h.update(memoryview(np.ascontiguousarray(a)).cast("B"))
+    return "%s:%s" % (kind, h.hexdigest())
+
+
+def provenance(torch, h, w, inputs) -> dict:
+    """What the line was measured on and with: device, ROCm/HIP and torch
+    versions, the library file and ABI, the sources it was built from, the
+    command line, the workload seed and a digest of the generated inputs."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    csrc = os.path.join(ROOT, "audio_diffusion_transformer_amd", "csrc")
+    src = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        src.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            src.update(f.read())
+    keys = [k for k in ("q", "k", "v", "x", "w_qkv", "norm_w", "cu_seqlens") if k in inputs]
+    return {
+        "gpu": torch.cuda.get_device_name(0),
+        "arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "rocm": rocm,
+        "hip_runtime": torch.version.hip,
+        "torch": torch.__version__,
+        "library": {"file": os.path.relpath(h.LIB_PATH, ROOT), "sha256": _sha256_file(h.LIB_PATH),
+                    "abi_version": h.version()},
+        "sources_sha256": src.hexdigest(),
+        "argv": sys.argv[1:],
+        "workload_seed": w.seed,
+        "inputs": keys,
+        "inputs_digest": _input_digest([inputs[k] for k in keys]),
+    }
+
+
+def parity_metrics(got: np.ndarray, ref: np.ndarray, against: str) -> dict:
+    """The run's own output rows against the oracle's rows for the same queries."""
+    d = got - ref
+    nr = float(np.linalg.norm(ref))
+    return {"rows": int(got.shape[0]), "against": against,
+            "max_abs": float(np.abs(d).max()), "mean_abs": float(np.abs(d).mean()),
+            "rel_l2": float(np.linalg.norm(d) / max(nr, 1e-300)),
+            "cosine": float(np.sum(got * ref) / max(np.linalg.norm(got) * nr, 1e-300))}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -168,9 +233,11 @@ def one_head_problem(w, inputs, head: int):
     return w1, oracle.Problem.from_projection(w1, sub)
 
 
-def cpu_baseline_sparse(w, inputs, seconds: float, threads: int):
+def cpu_baseline_sparse(w, inputs, seconds: float, threads: int, gpu_rows=None, gpu_lists=None):
     """Time the fp64 CPU oracle of the block-sparse path on one head: its own
-    tile selection for that head, then sampled query rows over their kept keys."""
+    tile selection for that head, then sampled query rows over their kept keys.
+    With gpu_rows / gpu_lists (the GPU's output rows and tile lists of that
+    head) the timed rows of blocks whose lists agree are also compared."""
     import oracle
     rng = np.random.default_rng(w.seed + 99)
     head = int(rng.integers(w.H))
@@ -193,17 +260,17 @@ def cpu_baseline_sparse(w, inputs, seconds: float, threads: int):
         blocks = np.sort(rng.choice(nqb, size=nblocks, replace=False))
         toks = np.concatenate([np.arange(B * qb, min(B * qb + B, n)) for qb in blocks]).astype(np.int64)
         t1 = time.perf_counter()
-        p.sparse_attention_rows(toks, tiles, w.keep_tiles, nthreads=threads)
-        return time.perf_counter() - t1, toks
+        vals = p.sparse_attention_rows(toks, tiles, w.keep_tiles, nthreads=threads)
+        return time.perf_counter() - t1, toks, vals
 
-    t_probe, _ = run(1)
+    t_probe, _, _ = run(1)
     nb = int(max(1, min(nqb, seconds / max(t_probe, 1e-6))))
-    t, toks = run(nb)
+    t, toks, vals = run(nb)
     nrows = len(toks)
     flops = sum(4.0 * w.d * keys_per_block[int(tk) // B] for tk in toks)
     t += sel_s * nrows / n                 # the head's selection, spread over its rows
     value = flops / t / 1e12
-    return {
+    res = {
         "value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "cpu_model": cpu_model(),
         "extrapolated_full_s": round(sparse_total_flops_estimate(w, keys_per_block) / (value * 1e12), 1),
         "kind": "oracle",
@@ -211,6 +278,14 @@ def cpu_baseline_sparse(w, inputs, seconds: float, threads: int):
                   "the %d tiles the oracle keeps for its block; fp64; the head's pooled-score selection (%.1f s) "
                   "spread over its rows; %.1f s" % (nrows, nb, B, head, w.N, w.H, w.keep_tiles, sel_s, t),
     }
+    if gpu_rows is not None and gpu_lists is not None:
+        same = np.all(gpu_lists(head) == tiles, axis=1)           # blocks whose kept tiles agree
+        keep = same[toks // B]
+        if keep.any():
+            res["parity"] = parity_metrics(gpu_rows(toks[keep], head), vals[keep],
+                                           "fp64 oracle over the same kept tiles (blocks whose lists agree: "
+                                           "%d of %d)" % (int(same.sum()), len(same)))
+    return res
 
 
 def sparse_total_flops_estimate(w, keys_per_block) -> float:
@@ -218,11 +293,13 @@ def sparse_total_flops_estimate(w, keys_per_block) -> float:
     return float(sum(4.0 * w.d * min(B, n - B * qb) * k for qb, k in enumerate(keys_per_block))) * w.H
 
 
-def cpu_baseline(w, inputs, seconds: float, threads: int):
-    """Time the fp64 CPU oracle on sampled query rows of one head (full key set)."""
+def cpu_baseline(w, inputs, seconds: float, threads: int, gpu_rows=None, gpu_lists=None):
+    """Time the fp64 CPU oracle on sampled query rows of one head (full key
+    set).  With gpu_rows (token indices, head -> the GPU output rows) the
+    oracle rows of the timed run are also compared with this run's output."""
     import oracle
     if w.keep_tiles > 0:
-        return cpu_baseline_sparse(w, inputs, seconds, threads)
+        return cpu_baseline_sparse(w, inputs, seconds, threads, gpu_rows, gpu_lists)
     rng = np.random.default_rng(w.seed + 99)
     head = int(rng.integers(w.H))
     n = w.seqs[0].n
@@ -241,11 +318,14 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
 
     rows_fn = p.mx_attention_rows if w.fp4 else p.attention_rows
 
+    last = {}
+
     def run(nrows):
         toks = np.sort(rng.choice(n, size=nrows, replace=False)).astype(np.int64)
         rows = toks * H_rows + head_row
         t0 = time.perf_counter()
-        rows_fn(rows, nthreads=threads)
+        last["vals"] = rows_fn(rows, nthreads=threads)
+        last["toks"] = toks
         return time.perf_counter() - t0
 
     # fixed cost (the keys' prologue, and for the FP4 emulation their
@@ -270,7 +350,7 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
     if w.model_dim > 0:
         sample += ("; plus the head's fp64 QKV projection of all tokens (%.1f s, %.0f%% of it "
                    "charged to the sampled rows)" % (proj_s, 100.0 * nrows / n))
-    return {
+    res = {
         "value": round(value, 6),
         "unit": "TFLOP/s",
         "cores": threads,
@@ -279,6 +359,10 @@ def cpu_baseline(w, inputs, seconds: float, threads: int):
         "kind": "oracle",
         "sample": sample,
     }
+    if gpu_rows is not None:
+        res["parity"] = parity_metrics(gpu_rows(last["toks"], head), last["vals"],
+                                       "fp64 MXFP4 emulation" if w.fp4 else "exact fp64 attention")
+    return res
 
 
 def library_gemm_then_prologue(torch, h, w, x, wq, norm_w, rope, cu, ws, ws_bytes, stream, reps: int = 5):
@@ -505,6 +589,9 @@ def main():
     outp_avg = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])) if proj else 0.0
     sel_avg = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])) if sparse else 0.0
     step_ms = [ev[i][0].elapsed_time(ev[i][nst]) for i in range(K)]
+    # the output of the last timed step, kept for the parity figures (the dense
+    # attention run after the block-sparse one writes `out`)
+    out_final = out.clone() if sparse else out
     copy_gbps = device_copy_rate(torch, dev)        # after the timed region
     ceiling = mfma_ceiling(torch, h, dev, stream, path="mx" if w.fp4 else "q8" if w.quantized else "bf16")
     print("[bench] %d steps: %.3f ms/step (attention %.3f, %s %.3f), wall %.3f s" % (
@@ -624,10 +711,22 @@ def main():
                      "out_proj_frac": round(of / MI355X_BF16_DENSE_TFLOPS, 4)})
         kern.update(unfused)
         res["config"]["model_dim"] = w.model_dim
+    res["provenance"] = provenance(torch, h, w, inp)
     if not args.no_cpu_baseline:
         threads, host = oracle_threads()
         print("[bench] timing the CPU oracle on %d threads (%s)" % (threads, host), file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, threads)
+        out_rows = out_final.view(torch.int16)
+
+        def gpu_rows(toks, head):
+            b = out_rows[torch.from_numpy(np.asarray(toks, dtype=np.int64)).to(dev), head].cpu().numpy()
+            return (b.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+        def gpu_lists(head):
+            nqb = (w.seqs[0].n + SPARSE_BLOCK_ROWS - 1) // SPARSE_BLOCK_ROWS
+            return tiles[head * nqb:(head + 1) * nqb].cpu().numpy()
+
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, threads, gpu_rows,
+                                           gpu_lists if sparse else None)
         res["cpu_baseline"].update(host)
     print(json.dumps(res), flush=True)
     return 0
