@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libh3attn.so")
+# The same sources with the attention kernels' invariant checks and timing
+# jitter compiled in (H3ATTN_CHECKED); loaded only through H3ATTN_LIB.
+LIB_CHECKED = os.path.join(HERE, "libh3attn_checked.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -50,5 +53,10 @@ def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
     return out
 
 
+def build_all(verbose: bool = False):
+    """The product library and its checked build."""
+    return build(verbose), build(verbose, out=LIB_CHECKED, extra=("-DH3ATTN_CHECKED",))
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

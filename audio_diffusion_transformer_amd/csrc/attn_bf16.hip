@@ -59,6 +59,40 @@
 
 namespace h3 {
 
+#ifdef H3ATTN_CHECKED
+// Checked build only (libh3attn_checked.so; the product library compiles none
+// of this).  The kernels record violated invariants in h3_check_flags (one word
+// per kind, any nonzero value marks it; read back by h3attn_checked), and with
+// a nonzero h3_jitter_seed every wave sleeps a pseudo-random 0..3 x 128 cycles
+// before each fill and each phase.  The delays change the relative timing of
+// the waves and of their direct-to-LDS fills without changing any
+// synchronisation, so a fill that could race with a fragment read (a missing
+// wait or barrier) shows up as different output bits between seeds.
+__device__ uint32_t h3_check_flags[kCheckKinds];
+__device__ uint32_t h3_jitter_seed;
+__device__ __forceinline__ void check_invariant(bool ok, int kind)
+{
+    if (!ok) atomicOr(&h3_check_flags[kind], 1u);
+}
+__device__ __forceinline__ void jitter(int wave, int j, int where)
+{
+    const uint32_t seed = h3_jitter_seed;
+    if (seed == 0) return;
+    uint32_t x = seed ^ ((uint32_t)blockIdx.x * 0x9E3779B1u) ^ ((uint32_t)wave * 0x85EBCA77u) ^
+                 ((uint32_t)j * 0xC2B2AE3Du) ^ ((uint32_t)where * 0x27D4EB2Fu);
+    x ^= x >> 15;
+    x *= 0x2C1B3C6Du;
+    x ^= x >> 12;
+    const int nap = __builtin_amdgcn_readfirstlane((int)(x >> 30));
+    for (int i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(2);
+}
+#define H3_CHECK(ok, kind) check_invariant((ok), (kind))
+#define H3_JITTER(wave, j, where) jitter((wave), (j), (where))
+#else
+#define H3_CHECK(ok, kind) ((void)0)
+#define H3_JITTER(wave, j, where) ((void)0)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -144,6 +178,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, hh = lane >> 5;
     const int q0 = qb * kBlockM + wave * 32;
+    H3_CHECK(si < a.nseq && head < a.H && qb < nqb, kCheckItem);
+    H3_CHECK(off + q0 + 32 <= a.Npad, kCheckRows);
 
     // ---- Q^T fragments: lane holds query q0+m, channels 16s + 8hh .. +7
     bf16x8 qf[KSTEPS];
@@ -164,7 +200,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
         nt = min(a.tpb, ntk);
         const int32_t *lst =
             a.tiles + ((int64_t)a.seq_item_base[si] + (int64_t)head * ((nqb + R - 1) / R) + qb / R) * a.tpb;
-        for (int i = threadIdx.x; i < nt; i += 256) ltiles[i] = min(max(lst[i], 0), ntk - 1);
+        for (int i = threadIdx.x; i < nt; i += 256) {
+            H3_CHECK(lst[i] >= 0 && lst[i] < ntk, kCheckListEntry);
+            ltiles[i] = min(max(lst[i], 0), ntk - 1);
+        }
         __syncthreads();
     }
     auto tix = [&](int j) -> int {
@@ -185,8 +224,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
         const_cast<uint16_t *>(kbase), 0, ntk * tbytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(vbase), 0, ntk * tbytes, kBufferFlags);
-    auto load_k = [&](int j, uint16_t *dst) { kfill.load(krs, (uint32_t)(tix(j) * tbytes), dst, wave); };
-    auto load_v = [&](int j, uint16_t *dst) { vfill.load(vrs, (uint32_t)(tix(j) * tbytes), dst, wave); };
+    auto load_k = [&](int j, uint16_t *dst) {
+        H3_CHECK(j < nt && tix(j) >= 0 && tix(j) < ntk, kCheckFillTile);
+        H3_JITTER(wave, j, 0);
+        kfill.load(krs, (uint32_t)(tix(j) * tbytes), dst, wave);
+    };
+    auto load_v = [&](int j, uint16_t *dst) {
+        H3_CHECK(j < nt && tix(j) >= 0 && tix(j) < ntk, kCheckFillTile);
+        H3_JITTER(wave, j, 1);
+        vfill.load(vrs, (uint32_t)(tix(j) * tbytes), dst, wave);
+    };
 
     f32x16 o[DB];
 #pragma unroll
@@ -367,12 +414,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
         load_k(j + 2, lk0);
         load_v(j + 1, lv1);
         row_max_update(j, sa0, sa1, false);
+        H3_JITTER(wave, j, 2);
         body(lk1, lv0, sa0, sa1, sb0, sb1);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         load_k(j + 3, lk1);
         load_v(j + 2, lv0);
         row_max_update(j + 1, sb0, sb1, false);
+        H3_JITTER(wave, j + 1, 2);
         body(lk0, lv1, sb0, sb1, sa0, sa1);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
@@ -381,6 +430,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a)
         if (j + 2 < nt) load_k(j + 2, kbuf(j & 1));
         load_v(j + 1, vbuf((j + 1) & 1));
         row_max_update(j, sa0, sa1, false);
+        H3_JITTER(wave, j, 3);
         scores(kbuf((j + 1) & 1), sb0, sb1);
         exp_pv(vbuf(j & 1), sa0, sa1);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -478,6 +528,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     const int grp = wave >> 2, gw = wave & 3;
     const int m = lane & 31, hh = lane >> 5;
     const int q0 = qb * kBlockM2 + wave * 32;
+    H3_CHECK(si < a.nseq && head < a.H && qb < nqb, kCheckItem);
+    H3_CHECK(off + q0 + 32 <= a.Npad, kCheckRows);
 
     bf16x8 qf[KSTEPS];
     {
@@ -495,7 +547,10 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
         // reads its entry back as a wave-uniform scalar
         nt = min(a.tpb, ntk);
         const int32_t *lst = a.tiles + ((int64_t)a.seq_item_base[si] + (int64_t)head * nqb + qb) * a.tpb;
-        for (int i = tid; i < nt; i += 512) ltiles[i] = min(max(lst[i], 0), ntk - 1);
+        for (int i = tid; i < nt; i += 512) {
+            H3_CHECK(lst[i] >= 0 && lst[i] < ntk, kCheckListEntry);
+            ltiles[i] = min(max(lst[i], 0), ntk - 1);
+        }
         __syncthreads();
     }
     // Sequence tile of visit j (j < nt).
@@ -524,6 +579,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     const __amdgpu_buffer_rsrc_t frs = grp ? vrs : krs;
     // sequence tile t into dst
     auto fill = [&](__amdgpu_buffer_rsrc_t rs, int t, uint16_t *dst) {
+        H3_CHECK(t >= 0 && t < ntk, kCheckFillTile);
         const uint32_t toff = (uint32_t)(t * tbytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -700,10 +756,13 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
     // kf = lk[j%3] and vf = lv[(j+2)%3] (this tile's fills).
     auto tile = [&](int j, const uint16_t *kn, const uint16_t *vc, const uint16_t *kn2, uint16_t *kf, uint16_t *vf,
                     f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1) {
+        H3_JITTER(wave, j, 0);
         if (j + 3 - grp < nt) fill(frs, tix(j + 3 - grp), grp ? vf : kf);
         row_max_update(tix(j), c0, c1);
+        H3_JITTER(wave, j, 1);
         phase_s(kn, vc, c0, n0, n1, pre);
         end_s();
+        H3_JITTER(wave, j, 2);
         phase_p(vc, kn2, c1, pre);
         end_p();
     };
@@ -742,6 +801,23 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnArgs a)
 
 template __global__ void attn_bf16_pp_kernel<128, false>(AttnArgs);
 template __global__ void attn_bf16_pp_kernel<128, true>(AttnArgs);
+
+#ifdef H3ATTN_CHECKED
+// Checked build: copy out (and optionally clear) the attention kernels' flag
+// words, and set the jitter seed of later launches (0: no delays).
+hipError_t attn_checked(uint32_t *flags_out, bool clear, uint32_t jitter_seed)
+{
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess && flags_out)
+        e = hipMemcpyFromSymbol(flags_out, HIP_SYMBOL(h3_check_flags), sizeof(uint32_t) * kCheckKinds);
+    if (e == hipSuccess && clear) {
+        const uint32_t zeros[kCheckKinds] = {};
+        e = hipMemcpyToSymbol(HIP_SYMBOL(h3_check_flags), zeros, sizeof zeros);
+    }
+    if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(h3_jitter_seed), &jitter_seed, sizeof jitter_seed);
+    return e;
+}
+#endif
 
 // Head_dim 128 runs attn_bf16_pp_kernel over 256-row query blocks, dense or
 // block-sparse (a.tiles); head_dim 64 runs attn_bf16_kernel over 128-row

@@ -270,6 +270,19 @@ struct OutProjArgs {
     int32_t cu[kMaxSeqs + 1];
 };
 
+// Invariants the checked build (H3ATTN_CHECKED) records in the attention
+// kernels, one flag word each.
+enum CheckKind {
+    kCheckItem = 0,        // work item decoded outside its sequence / head / query block
+    kCheckRows = 1,        // a workgroup's query rows outside the padded layout
+    kCheckFillTile = 2,    // a K/V tile fill outside the sequence's tiles
+    kCheckListEntry = 3,   // a block-sparse list entry outside [0, tiles of the sequence) (clamped)
+    kCheckKinds = 4
+};
+#ifdef H3ATTN_CHECKED
+hipError_t attn_checked(uint32_t *flags_out, bool clear, uint32_t jitter_seed);
+#endif
+
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_prologue(const PrologueArgs &a, int d, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs &a, int d, int64_t nitems, hipStream_t st);

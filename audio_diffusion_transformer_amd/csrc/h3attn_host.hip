@@ -429,6 +429,23 @@ h3attn_status h3attn_fwd_static(const h3attn_params *p, const void *q, const voi
                              H3ATTN_STATIC_WORKSPACE_BYTES, stream, 3);
 }
 
+h3attn_status h3attn_checked(uint32_t *flags_out, int clear, uint32_t jitter_seed)
+{
+#ifdef H3ATTN_CHECKED
+    h3attn_status st = check_device();
+    if (st != H3ATTN_OK) return st;
+    const hipError_t e = attn_checked(flags_out, clear != 0, jitter_seed);
+    if (e != hipSuccess) return fail(H3ATTN_ERR_HIP, "checked-build state: %s", hipGetErrorString(e));
+    return ok();
+#else
+    (void)flags_out;
+    (void)clear;
+    (void)jitter_seed;
+    return fail(H3ATTN_ERR_UNSUPPORTED, "this library is built without checks (the checked build is "
+                "libh3attn_checked.so)");
+#endif
+}
+
 h3attn_status h3attn_mfma_ceiling(int mix, int workgroups, int iters, float *out, void *stream)
 {
     if (mix < 0 || mix > 5) return fail(H3ATTN_ERR_INVALID_ARG, "mix must be in 0..5 (got %d)", mix);

@@ -35,7 +35,7 @@ EXPORTED = ("h3attn_workspace_size", "h3attn_fwd", "h3attn_fwd_stages", "h3attn_
             "h3attn_out_proj", "h3attn_fwd_sparse", "h3attn_fwd_sparse_stages",
             "h3attn_q8_prologue", "h3attn_fwd_mx", "h3attn_fwd_mx_stages", "h3attn_mx_prologue",
             "h3attn_fwd_static", "h3attn_mfma_ceiling", "h3attn_rope_fill_video", "h3attn_rope_fill_audio",
-            "h3attn_status_string", "h3attn_last_error", "h3attn_version")
+            "h3attn_checked", "h3attn_status_string", "h3attn_last_error", "h3attn_version")
 
 
 class H3AttnError(RuntimeError):
@@ -72,6 +72,8 @@ def lib():
         for name in ("h3attn_fwd_stages", "h3attn_fwd_q8_stages", "h3attn_fwd_mx_stages"):
             getattr(L, name).restype = C.c_int
             getattr(L, name).argtypes = fwd_args + [C.c_int]
+        L.h3attn_checked.restype = C.c_int
+        L.h3attn_checked.argtypes = [vp, C.c_int, C.c_uint32]
         L.h3attn_mfma_ceiling.restype = C.c_int
         L.h3attn_mfma_ceiling.argtypes = [C.c_int, C.c_int, C.c_int, vp, vp]
         L.h3attn_fwd_static.restype = C.c_int
@@ -259,6 +261,19 @@ def h3attn_fwd(q, k, v, norm_w, rope_tables, cu_seqlens, out=None, workspace=Non
                    workspace.numel() * workspace.element_size(), _stream_ptr(stream), quantized,
                    stages))
     return out
+
+
+H3ATTN_CHECK_KINDS = 4
+
+
+def checked(clear: bool = True, jitter_seed: int = 0) -> np.ndarray:
+    """Checked build only (H3ATTN_LIB=.../libh3attn_checked.so): the attention
+    kernels' invariant flag words (cleared after reading when ``clear``), and
+    the timing-jitter seed for later launches (0: none).  Raises on the
+    product library."""
+    flags = np.zeros(H3ATTN_CHECK_KINDS, dtype=np.uint32)
+    _check(lib().h3attn_checked(flags.ctypes.data, 1 if clear else 0, int(jitter_seed)))
+    return flags
 
 
 def mfma_ceiling_raw(mix: int, workgroups: int, iters: int, out, stream) -> int:

@@ -425,6 +425,28 @@ h3attn_status h3attn_rope_fill_audio(int32_t n, int32_t pos0, int32_t dim, doubl
 const char *h3attn_status_string(h3attn_status s);
 /* Detail of the calling thread's last non-OK status ("" if none). */
 const char *h3attn_last_error(void);
+/*
+ * Diagnostic for the checked build of this library (libh3attn_checked.so, the
+ * same sources compiled with H3ATTN_CHECKED; the product library returns
+ * H3ATTN_ERR_UNSUPPORTED).  Its attention kernels record violated invariants
+ * in H3ATTN_CHECK_KINDS device flag words:
+ *   0  a work item decoded outside its sequence, head or query block;
+ *   1  a workgroup's query rows outside the padded workspace layout;
+ *   2  a K/V tile fill outside the sequence's tiles;
+ *   3  a block-sparse tile-list entry outside the sequence's tiles (the
+ *      kernels clamp it; it breaks the caller contract of h3attn_fwd_sparse).
+ * With a nonzero jitter seed every wave of those kernels sleeps a
+ * pseudo-random 0..3 x 128 cycles before each tile fill and each phase:
+ * synchronisation is unchanged, so outputs must stay bit-identical to the
+ * product library for every seed; a difference means a race between the LDS
+ * fills and the reads.  The call waits for the device, then
+ *   flags_out  HOST uint32 [H3ATTN_CHECK_KINDS] or NULL: the flag words
+ *   clear      nonzero: reset the flags to 0 after reading them
+ *   jitter_seed  seed for later launches (0: no delays)
+ */
+#define H3ATTN_CHECK_KINDS 4
+h3attn_status h3attn_checked(uint32_t *flags_out, int clear, uint32_t jitter_seed);
+
 /* H3ATTN_VERSION of the built library. */
 int h3attn_version(void);
 

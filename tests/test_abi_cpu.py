@@ -519,3 +519,24 @@ def test_binding_refuses_another_abi_version(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
                        env=dict(os.environ, H3ATTN_LIB=str(so)))
     assert "REFUSED" in r.stdout and "ABI version 1" in r.stdout, r.stdout + r.stderr
+
+
+def test_checked_entry_point_and_checked_build():
+    """h3attn_checked is a diagnostic of the checked build: the product library
+    refuses it before touching a device; the checked library (same sources with
+    H3ATTN_CHECKED) exports exactly the same symbols and the same ABI version."""
+    import ctypes as C
+    from audio_diffusion_transformer_amd import build as B
+    with pytest.raises(h.H3AttnError) as e:
+        h.checked()
+    assert e.value.status == h.H3ATTN_ERR_UNSUPPORTED and "without checks" in str(e.value)
+    assert os.path.exists(B.LIB_CHECKED), "libh3attn_checked.so is not built"
+    L = C.CDLL(B.LIB_CHECKED)
+    for n in h.EXPORTED:
+        assert hasattr(L, n), n
+    L.h3attn_version.restype = C.c_int
+    assert L.h3attn_version() == h.H3ATTN_VERSION
+    if not _gpu_present():
+        L.h3attn_checked.restype = C.c_int
+        L.h3attn_checked.argtypes = [C.c_void_p, C.c_int, C.c_uint32]
+        assert L.h3attn_checked(None, 0, 0) == h.H3ATTN_ERR_DEVICE     # past the build check, no device here
