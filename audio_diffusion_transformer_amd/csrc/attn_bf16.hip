@@ -56,42 +56,10 @@
 // row sum l adds exactly those rounded values.
 #include "h3_internal.h"
 #include "attn_common.h"
+#include "h3_checked.h"
 
 namespace h3 {
 
-#ifdef H3ATTN_CHECKED
-// Checked build only (libh3attn_checked.so; the product library compiles none
-// of this).  The kernels record violated invariants in h3_check_flags (one word
-// per kind, any nonzero value marks it; read back by h3attn_checked), and with
-// a nonzero h3_jitter_seed every wave sleeps a pseudo-random 0..3 x 128 cycles
-// before each fill and each phase.  The delays change the relative timing of
-// the waves and of their direct-to-LDS fills without changing any
-// synchronisation, so a fill that could race with a fragment read (a missing
-// wait or barrier) shows up as different output bits between seeds.
-__device__ uint32_t h3_check_flags[kCheckKinds];
-__device__ uint32_t h3_jitter_seed;
-__device__ __forceinline__ void check_invariant(bool ok, int kind)
-{
-    if (!ok) atomicOr(&h3_check_flags[kind], 1u);
-}
-__device__ __forceinline__ void jitter(int wave, int j, int where)
-{
-    const uint32_t seed = h3_jitter_seed;
-    if (seed == 0) return;
-    uint32_t x = seed ^ ((uint32_t)blockIdx.x * 0x9E3779B1u) ^ ((uint32_t)wave * 0x85EBCA77u) ^
-                 ((uint32_t)j * 0xC2B2AE3Du) ^ ((uint32_t)where * 0x27D4EB2Fu);
-    x ^= x >> 15;
-    x *= 0x2C1B3C6Du;
-    x ^= x >> 12;
-    const int nap = __builtin_amdgcn_readfirstlane((int)(x >> 30));
-    for (int i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(2);
-}
-#define H3_CHECK(ok, kind) check_invariant((ok), (kind))
-#define H3_JITTER(wave, j, where) jitter((wave), (j), (where))
-#else
-#define H3_CHECK(ok, kind) ((void)0)
-#define H3_JITTER(wave, j, where) ((void)0)
-#endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -803,19 +771,9 @@ template __global__ void attn_bf16_pp_kernel<128, false>(AttnArgs);
 template __global__ void attn_bf16_pp_kernel<128, true>(AttnArgs);
 
 #ifdef H3ATTN_CHECKED
-// Checked build: copy out (and optionally clear) the attention kernels' flag
-// words, and set the jitter seed of later launches (0: no delays).
-hipError_t attn_checked(uint32_t *flags_out, bool clear, uint32_t jitter_seed)
+hipError_t attn_checked(uint32_t *or_into, bool clear, uint32_t jitter_seed)
 {
-    hipError_t e = hipDeviceSynchronize();
-    if (e == hipSuccess && flags_out)
-        e = hipMemcpyFromSymbol(flags_out, HIP_SYMBOL(h3_check_flags), sizeof(uint32_t) * kCheckKinds);
-    if (e == hipSuccess && clear) {
-        const uint32_t zeros[kCheckKinds] = {};
-        e = hipMemcpyToSymbol(HIP_SYMBOL(h3_check_flags), zeros, sizeof zeros);
-    }
-    if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(h3_jitter_seed), &jitter_seed, sizeof jitter_seed);
-    return e;
+    return checked_state_here(or_into, clear, jitter_seed);
 }
 #endif
 

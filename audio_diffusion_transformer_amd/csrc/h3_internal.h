@@ -280,7 +280,12 @@ enum CheckKind {
     kCheckKinds = 4
 };
 #ifdef H3ATTN_CHECKED
-hipError_t attn_checked(uint32_t *flags_out, bool clear, uint32_t jitter_seed);
+// Per translation unit (bf16, quantised, MXFP4 attention): OR the unit's flag
+// words into or_into, clear them if asked, set its jitter seed.  The caller
+// synchronises the device first.
+hipError_t attn_checked(uint32_t *or_into, bool clear, uint32_t jitter_seed);
+hipError_t q8_checked(uint32_t *or_into, bool clear, uint32_t jitter_seed);
+hipError_t mx_checked(uint32_t *or_into, bool clear, uint32_t jitter_seed);
 #endif
 
 // Launchers: return the hipError_t of the launch.

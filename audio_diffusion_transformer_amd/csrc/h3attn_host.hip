@@ -434,8 +434,13 @@ h3attn_status h3attn_checked(uint32_t *flags_out, int clear, uint32_t jitter_see
 #ifdef H3ATTN_CHECKED
     h3attn_status st = check_device();
     if (st != H3ATTN_OK) return st;
-    const hipError_t e = attn_checked(flags_out, clear != 0, jitter_seed);
+    uint32_t f[kCheckKinds] = {};
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = attn_checked(f, clear != 0, jitter_seed);
+    if (e == hipSuccess) e = q8_checked(f, clear != 0, jitter_seed);
+    if (e == hipSuccess) e = mx_checked(f, clear != 0, jitter_seed);
     if (e != hipSuccess) return fail(H3ATTN_ERR_HIP, "checked-build state: %s", hipGetErrorString(e));
+    if (flags_out) std::memcpy(flags_out, f, sizeof f);
     return ok();
 #else
     (void)flags_out;

@@ -40,6 +40,7 @@
 #include "h3_internal.h"
 #include "norm_rope.h"
 #include "attn_common.h"
+#include "h3_checked.h"
 
 namespace h3 {
 
@@ -332,6 +333,8 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     int m = lane & 31, hh = lane >> 5;    // re-derived before the tail loop
     const int q0 = qb * kBlockM + wave * 32;
+    H3_CHECK(si < a.nseq && head < a.H && qb < nqb, kCheckItem);
+    H3_CHECK(off + q0 + 32 <= a.Npad, kCheckRows);
 
     // Q row q0 + m: channels 64 st + 32 hh .. +31 of step st (16 bytes each);
     // the scale word shifted so that bytes 0 and 2 are blocks hh and 2 + hh.
@@ -355,6 +358,8 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>((vside ? a.vxs : a.kxs) + t0 * kScaleBytes), 0, nt * kScaleBytes, kBufferFlags);
     auto fill = [&](int jj, void *kd, void *vd, uint32_t *ksd, uint32_t *vsd) {
+        H3_CHECK(jj >= 0 && jj < nt, kCheckFillTile);
+        H3_JITTER(wave, jj, 0);
         kfill.load(krs, (uint32_t)(jj * kTileBytes), kd, wave);
         vfill.load(vrs, (uint32_t)(jj * kTileBytes), vd, wave);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (__attribute__((address_space(3))) void *)(vside ? vsd : ksd),
@@ -395,6 +400,7 @@ __global__ __launch_bounds__(256, 3) void attn_mx_kernel(MxAttnArgs a)
     // jfill (when `more`), scores, the running max, P in FP4, P.V and the row sum.
     auto step = [&](int jj, const uint8_t *kl, const uint8_t *vl, const uint32_t *ksl, const uint32_t *vsl,
                     bool more, void *kn, void *vn, uint32_t *ksn, uint32_t *vsn, bool mask, int jfill) {
+        H3_JITTER(wave, jj, 1);
         const i32x4 k00 = kfrag(kl, 0, 0), k10 = kfrag(kl, 1, 0), k01 = kfrag(kl, 0, 1), k11 = kfrag(kl, 1, 1);
         const uint32_t ksw = ksl[lane];
 
@@ -559,6 +565,13 @@ hipError_t launch_mx_prep(const MxArgs &a, int d, hipStream_t st)
     hipLaunchKernelGGL(mx_pass3_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
+
+#ifdef H3ATTN_CHECKED
+hipError_t mx_checked(uint32_t *or_into, bool clear, uint32_t jitter_seed)
+{
+    return checked_state_here(or_into, clear, jitter_seed);
+}
+#endif
 
 hipError_t launch_attn_mx(const MxAttnArgs &a, int d, int64_t nitems, hipStream_t st)
 {

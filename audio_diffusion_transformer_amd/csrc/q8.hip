@@ -29,6 +29,7 @@
 #include "h3_internal.h"
 #include "norm_rope.h"
 #include "attn_common.h"
+#include "h3_checked.h"
 
 namespace h3 {
 
@@ -363,6 +364,8 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, hh = lane >> 5;
     const int q0 = qb * kBlockM + wave * 32;
+    H3_CHECK(si < a.nseq && head < a.H && qb < nqb, kCheckItem);
+    H3_CHECK(off + q0 + 32 <= a.Npad, kCheckRows);
 
     i32x4 qf[4];
     {
@@ -384,8 +387,16 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(a.v8t + ((int64_t)head * ntiles + off / kTile) * (QD * kTile)), 0, nt * tbytes,
         kBufferFlags);
-    auto load_k = [&](int j, void *dst) { kfill.load(krs, (uint32_t)(j * tbytes), dst, wave); };
-    auto load_v = [&](int j, void *dst) { vfill.load(vrs, (uint32_t)(j * tbytes), dst, wave); };
+    auto load_k = [&](int j, void *dst) {
+        H3_CHECK(j >= 0 && j < nt, kCheckFillTile);
+        H3_JITTER(wave, j, 0);
+        kfill.load(krs, (uint32_t)(j * tbytes), dst, wave);
+    };
+    auto load_v = [&](int j, void *dst) {
+        H3_CHECK(j >= 0 && j < nt, kCheckFillTile);
+        H3_JITTER(wave, j, 1);
+        vfill.load(vrs, (uint32_t)(j * tbytes), dst, wave);
+    };
 
     f32x16 o[4];                    // O^T per 32-channel block
     for (int i = 0; i < 4; ++i) o[i] = (f32x16){};
@@ -509,6 +520,8 @@ __global__ __launch_bounds__(256, 2) void attn_q8_kernel(Q8AttnArgs a)
     static_assert(KP + VP <= 8, "fill pieces must fit in the step's chunks");
     auto body = [&](const int8_t *kl, const uint8_t *vprev, const i32x16 &c0s, const i32x16 &c1s, float cs,
                     float c0, i32x16 &n0, i32x16 &n1, int kj, void *kdst, int vj, void *vdst) {
+        H3_CHECK(kj < nt && vj < nt, kCheckFillTile);
+        H3_JITTER(wave, kj, 2);
         i32x4 kf[8];
         i32x8 vf[4];
         i32x8 pn;
@@ -659,6 +672,13 @@ hipError_t launch_q8_prep(const Q8Args &a, int d, hipStream_t st)
         hipLaunchKernelGGL(q8_pass3_kernel<false>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
+
+#ifdef H3ATTN_CHECKED
+hipError_t q8_checked(uint32_t *or_into, bool clear, uint32_t jitter_seed)
+{
+    return checked_state_here(or_into, clear, jitter_seed);
+}
+#endif
 
 hipError_t launch_attn_q8(const Q8AttnArgs &a, int d, int64_t nitems, hipStream_t st)
 {

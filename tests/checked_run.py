@@ -26,6 +26,7 @@ CASES = {
                                split=(16, 24, 24), seed=74),
 }
 SPARSE = {"long_d128": 7, "long_d64": 5}      # cases also run block-sparse, with this many tiles per list
+QUANT = {"long_d128": (True, "mx"), "ragged_d128": (True, "mx")}   # cases also run on the INT8/FP8 and MXFP4 paths
 
 
 def random_lists(w, tpb, seed, bad=False):
@@ -54,6 +55,10 @@ def run_all(torch):
         inp = synth.generate(w)
         t = G.to_device(inp, w)
         res[name] = G.bits(G.run(w, t, label="checked-comparison " + name))
+        for mode in QUANT.get(name, ()):
+            tag = "q8" if mode is True else mode
+            res["%s_%s" % (name, tag)] = G.bits(G.run(w, t, quantized=mode, label="checked-comparison %s %s" % (
+                name, tag)))
         if name in SPARSE:
             tpb = SPARSE[name]
             bt = torch.from_numpy(random_lists(w, tpb, seed=tpb)).to("cuda:0")

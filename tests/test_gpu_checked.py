@@ -4,7 +4,8 @@ product library.
 
 For every case of tests/checked_run.py (the eight-wave kernel dense on a ragged
 batch, a long sequence and sharp inputs, and block-sparse on caller lists; the
-four-wave kernel dense and block-sparse), run in a child process on the checked
+four-wave kernel dense and block-sparse; the INT8/FP8 and MXFP4 kernels on the
+ragged batch and the long sequence), run in a child process on the checked
 build with jitter seeds 0, 1, 2 and 3:
 - every output is bit-identical to the product library's: the kernels are
   deterministic, and the jitter (per-wave delays before every fill and phase)
