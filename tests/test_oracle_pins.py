@@ -521,6 +521,29 @@ def test_projection_with_permutation_weights_equals_direct_inputs():
     np.testing.assert_array_equal(pp.attention_rows(rows), pd.attention_rows(rows))
 
 
+def test_bf16_rounding_is_round_to_nearest_even():
+    # the oracle's fp64 -> bf16 rounding (used for v of the quantised projection
+    # path and for the stored q/k of the selection scores): ties to even at exact
+    # midpoints, otherwise to nearest; against closed forms and against torch's
+    # own float32 -> bfloat16 cast on random values
+    one, ulp = 1.0, 2.0 ** -7                      # bf16 spacing in [1, 2)
+    cases = {one + ulp / 2: one,                   # midpoint, 1.0 has the even mantissa
+             one + 3 * ulp / 2: one + 2 * ulp,     # midpoint, rounds up to the even one
+             one + ulp / 2 + 2.0 ** -20: one + ulp,
+             one + ulp / 2 - 2.0 ** -20: one,
+             -(one + 3 * ulp / 2): -(one + 2 * ulp),
+             0.0: 0.0}
+    x = np.array(list(cases), dtype=np.float64)
+    want = np.array(list(cases.values()), dtype=np.float64)
+    np.testing.assert_array_equal(oracle._round_bf16(x), want)
+    bits = oracle._bf16_bits_rne(x)
+    assert bits.dtype == np.uint16
+    np.testing.assert_array_equal((bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64), want)
+    r = np.random.default_rng(9).standard_normal(1 << 16) * np.exp(np.random.default_rng(10).uniform(-20, 20, 1 << 16))
+    ref = torch.from_numpy(r.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle._bf16_bits_rne(r), ref)
+
+
 def test_quantised_projection_problem_equals_direct_inputs():
     # round_v: permutation weights make the projection exact bf16 values, so v
     # rounded to bf16 is the direct v bit for bit, and every quantiser of the
