@@ -83,16 +83,20 @@ def main(argv):
     w = CASES["long_d128"]
     inp = synth.generate(w)
     t = G.to_device(inp, w)
+    # (the best of three batches of 20 calls each, so a stray slow batch cannot decide it)
     for seed in (0, 1):
         h.checked(clear=False, jitter_seed=seed)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], eps=w.eps)
-        e0.record()
-        for _ in range(10):
-            h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], eps=w.eps)
-        e1.record()
-        torch.cuda.synchronize()
-        saved["ms@%d" % seed] = np.array([e0.elapsed_time(e1) / 10])
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                h.h3attn_fwd(t["q"], t["k"], t["v"], t["norm_w"], t["rope"], t["cu"], eps=w.eps)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 20)
+        saved["ms@%d" % seed] = np.array([best])
     h.checked(clear=True, jitter_seed=0)
     # a list entry out of range: clamped by the kernel, recorded in flag word 3
     bt = torch.from_numpy(random_lists(w, 7, seed=7, bad=True)).to("cuda:0")
