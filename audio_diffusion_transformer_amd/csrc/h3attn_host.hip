@@ -1195,19 +1195,36 @@ h3attn_status h3attn_rope_fill_video(int32_t T, int32_t Hg, int32_t Wg, int32_t 
     if (!(theta > 1.0) || !std::isfinite(theta)) return fail(H3ATTN_ERR_INVALID_ARG, "theta must be > 1");
     if (!out && (int64_t)T * Hg * Wg > 0) return fail(H3ATTN_ERR_INVALID_ARG, "out is NULL");
     const int half = (dt + dh + dw) / 2;
-    const int32_t secs[3] = {dt, dh, dw};
-    for (int64_t nidx = 0; nidx < (int64_t)T * Hg * Wg; ++nidx) {
-        const int64_t pos[3] = {nidx / ((int64_t)Hg * Wg), (nidx / Wg) % Hg, nidx % Wg};
-        float *row = out + nidx * half * 2;
-        int pair = 0;
-        for (int ax = 0; ax < 3; ++ax) {
-            for (int j = 0; j < secs[ax] / 2; ++j, ++pair) {
-                const double phi = (double)pos[ax] * std::pow(theta, -2.0 * j / secs[ax]);
-                row[2 * pair] = (float)std::cos(phi);
-                row[2 * pair + 1] = (float)std::sin(phi);
-            }
+    const int64_t HW = (int64_t)Hg * Wg;
+    // section `sec` (first pair `p0`) of a row, for position pos
+    auto section = [&](float *row, int p0, int sec, int64_t pos) {
+        for (int j = 0; j < sec / 2; ++j) {
+            const double phi = (double)pos * std::pow(theta, -2.0 * j / sec);
+            row[2 * (p0 + j)] = (float)std::cos(phi);
+            row[2 * (p0 + j) + 1] = (float)std::sin(phi);
         }
-    }
+    };
+    // Each section depends on one coordinate only, so it is computed on the
+    // first row with that coordinate (t: row (t,0,0); y: row (0,y,0); x: row
+    // (0,0,x)) and copied from there into every other row: the same values,
+    // with T*dt/2 + Hg*dh/2 + Wg*dw/2 angle evaluations in all.
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t y = 0; y < Hg; ++y)
+            for (int64_t x = 0; x < Wg; ++x) {
+                float *row = out + (t * HW + y * Wg + x) * half * 2;
+                if (y == 0 && x == 0)
+                    section(row, 0, dt, t);
+                else
+                    std::memcpy(row, out + (t * HW) * half * 2, sizeof(float) * dt);
+                if (t == 0 && x == 0)
+                    section(row, dt / 2, dh, y);
+                else
+                    std::memcpy(row + dt, out + (y * Wg) * half * 2 + dt, sizeof(float) * dh);
+                if (t == 0 && y == 0)
+                    section(row, (dt + dh) / 2, dw, x);
+                else
+                    std::memcpy(row + dt + dh, out + x * half * 2 + dt + dh, sizeof(float) * dw);
+            }
     return ok();
 }
 

@@ -184,6 +184,8 @@ def _oracle_angles(seqs, split, d):
 @pytest.mark.parametrize("seqs,split,d", [
     ([(4, 8, 8, 0)], (16, 24, 24), 64),
     ([(3, 7, 9, 250), (2, 5, 5, 0), (0, 1, 1, 4)], (32, 48, 48), 128),
+    # unit grid extents (each section is filled once per coordinate and copied)
+    ([(2, 1, 5, 0), (3, 4, 1, 2), (1, 1, 1, 0), (5, 1, 1, 3)], (32, 48, 48), 128),
 ])
 def test_rope_tables_match_oracle_angles(seqs, split, d):
     tab = h.rope_table(seqs, split, d)

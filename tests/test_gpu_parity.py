@@ -94,6 +94,36 @@ def test_attention_full_size_sampled_rows(torch_dev, name):
     G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.BF16_GATE, name)
 
 
+@pytest.mark.timeout(400)
+def test_longest_accepted_sequence_sampled(torch_dev):
+    """One sequence of the longest length the dense kernels accept at head_dim
+    128: 8,388,544 tokens, whose per-(sequence, head) K/V slice of 131,071
+    64-key tiles is one tile short of the 2 GiB that the kernels' 32-bit buffer
+    ranges and tile offsets cover (one token more is rejected,
+    tests/test_abi_cpu.py).  H = 1.  The q, k, v rows repeat one seeded
+    65,536-token draw (RoPE still rotates by each token's own grid position);
+    sampled rows, the first and last token among them, are compared with the
+    oracle over all 8.4M keys."""
+    base = synth.Workload("longest_base", H=1, d=128, seqs=(Seq(1, 256, 256),), split=(32, 48, 48),
+                          k_offset_std=0.5, seed=21)
+    w = base.replace(name="longest_seq_d128", seqs=(Seq(127, 256, 258, 448),))
+    assert w.N == (2 ** 31 // (2 * w.d)) // 64 * 64 - 64
+    small = synth.generate(base)
+    inp = dict(small)
+    reps = -(-w.N // base.N)
+    for key in ("q", "k", "v"):
+        inp[key] = np.tile(small[key], (reps, 1, 1))[:w.N]
+    inp["cu_seqlens"] = w.cu_seqlens()
+    G.announce("longest sequence: inputs on the device (%d tokens)" % w.N)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, label="longest sequence"))
+    del t
+    rows = synth.sample_rows(w, 24)
+    G.announce("longest sequence: oracle, %d rows over %d keys" % (len(rows), w.N))
+    ref = G.oracle_rows(w, inp, rows)
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.BF16_GATE, w.name)
+
+
 def test_sharp_full_video_shape_sampled(torch_dev):
     """Peaky softmax (score std ~4) at the 58,320-token video shape: outputs are
     O(0.3-1), so absolute tolerances are meaningful here."""
