@@ -44,6 +44,8 @@ MI355X_BF16_DENSE_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense
 MI355X_FP8_DENSE_TFLOPS = 5033.2
 MI355X_FP4_DENSE_TFLOPS = 10066.4     # FP4 (and FP6) dense MFMA
 MI355X_HBM_GBPS = 8000.0
+# performance gate of the attention kernel: this fraction of its datasheet peak
+PERF_GATE_FRAC = 0.60
 METRIC = "attention TFLOP/s and % of bf16 MFMA peak at N=125k packed tokens, H=24, d=128"
 
 
@@ -671,6 +673,11 @@ def main():
                      "kernel": {"mx": "attn_mx_kernel", "q8": "attn_q8_kernel",
                                 "bf16": "attn_bf16_pp_kernel<128, false>"}[kname],
                      "avg_ms": round(att_avg, 4)},
+        # the attention kernel against 60% of its datasheet peak: the result is reported on every
+        # run, met or not, with the kernel time that would meet it
+        "perf_gate": {"target_frac": PERF_GATE_FRAC, "frac": round(achieved / peak, 4),
+                      "met": bool(achieved >= PERF_GATE_FRAC * peak),
+                      "attention_ms_at_target": round(attn_flops / (PERF_GATE_FRAC * peak * 1e12) * 1e3, 3)},
         # the same box's sustained matrix-core rate for this path's MFMA type, alone and with the
         # path's vector work beside it (h3attn_mfma_ceiling), beside the datasheet peak
         "measured_mfma_ceiling": None,
