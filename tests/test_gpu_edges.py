@@ -4,7 +4,8 @@
   empty through single tokens, audio-only sequences and lengths on 64- and
   256-token boundaries, through both the bf16 and the quantised path;
 - single-token sequences only (every tile has one valid key);
-- a non-default softmax scale and RMSNorm epsilon.
+- a non-default softmax scale and RMSNorm epsilon;
+- the most heads the ABI takes (4,096), on both paths.
 
 All rows are compared (the cases are small).
 """
@@ -57,6 +58,21 @@ def test_largest_batch_of_sequences(torch_dev, quantized):
     out = G.bits(G.run(w, t, quantized=quantized, label="max_batch_64"))
     _all_rows(w, inp, out, G.Q8_GATE if quantized else G.BF16_GATE,
               "max_batch_64" + ("_q8" if quantized else ""))
+
+
+@pytest.mark.parametrize("d,quantized", [(128, False), (64, False), (128, True)])
+def test_most_heads(torch_dev, d, quantized):
+    """The most heads the ABI takes (4,096) on two short sequences (a partial
+    tile and a 3-token tail): the work-item decode, the per-(sequence, head)
+    slices and the quantised path's per-head scales at their largest head index."""
+    split = (32, 48, 48) if d == 128 else (16, 24, 24)
+    w = synth.Workload("most_heads_d%d" % d, H=4096, d=d, seqs=(Seq(1, 7, 10), Seq(1, 1, 3)), split=split,
+                       k_offset_std=0.5, seed=23)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    label = w.name + ("_q8" if quantized else "")
+    out = G.bits(G.run(w, t, quantized=quantized, label=label))
+    _all_rows(w, inp, out, G.Q8_GATE if quantized else G.BF16_GATE, label)
 
 
 def test_single_token_sequences(torch_dev):
