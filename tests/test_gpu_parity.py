@@ -95,6 +95,31 @@ def test_attention_full_size_sampled_rows(torch_dev, name):
 
 
 @pytest.mark.timeout(400)
+def test_ragged_every_row_of_two_sequences(torch_dev):
+    """Full-tensor evidence at a full-size workload: the three-sequence ragged
+    batch (18,144 / 45,250 / 7,200 tokens, H = 24) runs whole; every row of one
+    seeded head of its first and last sequence (25,344 rows), and every row of
+    every head of its last sequence (172,800 rows), each over all keys of its
+    sequence, is compared with the oracle."""
+    w = synth.WORKLOADS["ragged"]
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, label="ragged, every row of two sequences"))
+    del t
+    head = int(np.random.default_rng(w.seed + 31).integers(w.H))
+    cu = w.cu_seqlens().astype(np.int64)
+    toks = np.concatenate([np.arange(cu[0], cu[1]), np.arange(cu[2], cu[3])])
+    rows = toks * w.H + head
+    G.announce("ragged: oracle, %d rows of head %d" % (len(rows), head))
+    ref = G.oracle_rows(w, inp, rows)
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.BF16_GATE, "ragged_every_row_head%d" % head)
+    rows = (np.arange(cu[2], cu[3])[:, None] * w.H + np.arange(w.H)[None, :]).reshape(-1)
+    G.announce("ragged: oracle, every row of every head of the last sequence (%d rows)" % len(rows))
+    ref = G.oracle_rows(w, inp, rows)
+    G.check(G.metrics(G.gpu_rows(out, rows, w.H), ref), G.BF16_GATE, "ragged_last_sequence_every_row")
+
+
+@pytest.mark.timeout(400)
 def test_longest_accepted_sequence_sampled(torch_dev):
     """One sequence of the longest length the dense kernels accept at head_dim
     128: 8,388,544 tokens, whose per-(sequence, head) K/V slice of 131,071
