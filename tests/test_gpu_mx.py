@@ -176,6 +176,48 @@ def test_mx_attention_matches_stepwise_emulation(torch_dev, name):
     G.check(m, G.MX_EMULATION_GATE, name + " vs emulation")
 
 
+@pytest.mark.timeout(400)
+def test_mx_ragged_last_sequence_every_row(torch_dev):
+    """Full-tensor evidence on the FP4 path at a full-size workload: the
+    three-sequence ragged batch runs whole, and every row of every head of its
+    7,200-token sequence (172,800 rows) is compared with the step-by-step FP4
+    emulation, and guarded against exact attention.
+
+    Over this many rows a few (measured: 49, 0.03%) sit on an FP4 rounding
+    boundary that fp32 and fp64 decide differently (a code or a block scale one
+    step apart; an e2m1 step is 25-50% of a value), so their outputs differ by
+    up to ~20% of the row.  Both are valid FP4 results: the aggregate gate
+    applies to all rows, and each row past the per-row bound must be a rare
+    boundary case (at most 0.1% of rows) whose GPU output is no further from
+    exact attention than the emulation's (measured ratio 0.99-1.08; bound 1.25)."""
+    w = synth.WORKLOADS["ragged"].replace(name="ragged_mx", fp4=True)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized="mx", label="ragged_mx, every row of the last sequence"))
+    del t
+    cu = w.cu_seqlens().astype(np.int64)
+    rows = (np.arange(cu[2], cu[3])[:, None] * w.H + np.arange(w.H)[None, :]).reshape(-1)
+    got = G.gpu_rows(out, rows, w.H)
+    p = oracle.Problem.from_workload(w, inp)
+    G.announce("ragged_mx: emulation and exact oracle, %d rows" % len(rows))
+    emu = p.mx_attention_rows(rows, nthreads=G.oracle_threads())
+    m = _emulation_metrics(got, emu)
+    print("ragged_mx last sequence vs emulation", m)
+    bound = G.MX_EMULATION_GATE["max_rel_row"]
+    G.check(m, {k: v for k, v in G.MX_EMULATION_GATE.items() if k != "max_rel_row"},
+            "ragged_mx last sequence vs emulation")
+    exact = p.attention_rows(rows, nthreads=G.oracle_threads())
+    G.check(G.metrics(got, exact), G.MX_GATE, "ragged_mx last sequence vs exact")
+    rel = np.linalg.norm(got - emu, axis=1) / np.maximum(np.linalg.norm(emu, axis=1), 1e-30)
+    off = np.nonzero(rel > bound)[0]
+    assert len(off) <= 1e-3 * len(rows), "%d of %d rows past the per-row bound" % (len(off), len(rows))
+    d_got = np.linalg.norm(got[off] - exact[off], axis=1)
+    d_emu = np.linalg.norm(emu[off] - exact[off], axis=1)
+    G.announce("ragged_mx: %d rows past the per-row bound; distance to exact, GPU / emulation: max %.3f" % (
+        len(off), float((d_got / d_emu).max()) if len(off) else 0.0))
+    assert np.all(d_got <= 1.25 * d_emu), "a row past the per-row bound is further from exact attention"
+
+
 @pytest.mark.parametrize("name", ["mx", "joint_mx", "ragged_mx"])
 def test_mx_attention_full_size_sampled(torch_dev, name):
     w = {"mx": lambda: synth.WORKLOADS["mx"],

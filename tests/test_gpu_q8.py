@@ -136,6 +136,29 @@ def _emulation_metrics(got, ref):
     return m
 
 
+@pytest.mark.timeout(400)
+def test_quantised_ragged_last_sequence_every_row(torch_dev):
+    """Full-tensor evidence on the quantised path at a full-size workload: the
+    three-sequence ragged batch runs whole, and every row of every head of its
+    7,200-token sequence (172,800 rows) is compared with the step-by-step
+    emulation and with exact attention."""
+    w = synth.WORKLOADS["ragged"].replace(name="ragged_q8", quantized=True)
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    out = G.bits(G.run(w, t, quantized=True, label="ragged_q8, every row of the last sequence"))
+    del t
+    cu = w.cu_seqlens().astype(np.int64)
+    rows = (np.arange(cu[2], cu[3])[:, None] * w.H + np.arange(w.H)[None, :]).reshape(-1)
+    got = G.gpu_rows(out, rows, w.H)
+    p = oracle.Problem.from_workload(w, inp)
+    G.announce("ragged_q8: emulation and exact oracle, %d rows" % len(rows))
+    m = _emulation_metrics(got, p.q8_attention_rows(rows, nthreads=G.oracle_threads()))
+    print("ragged_q8 last sequence vs emulation", m)
+    G.check(m, G.Q8_EMULATION_GATE, "ragged_q8 last sequence vs emulation")
+    G.check(G.metrics(got, p.attention_rows(rows, nthreads=G.oracle_threads())), G.Q8_GATE,
+            "ragged_q8 last sequence vs exact")
+
+
 @pytest.mark.parametrize("name", sorted(SMALL) + ["q8"])
 def test_quantised_attention_matches_stepwise_emulation(torch_dev, name):
     """Against the oracle's step-by-step emulation of the quantised path (the
