@@ -207,6 +207,27 @@ def test_full_size_ragged_two_heads(torch_dev):
     G.check(G.metrics(gotr, ref), G.BF16_GATE, w.name + " sampled")
 
 
+@pytest.mark.timeout(400)
+def test_caller_lists_ragged_last_sequence_every_row(torch_dev):
+    """Full-tensor evidence on the block-sparse path at a full-size workload:
+    the three-sequence ragged batch runs whole with 40 seeded caller-given
+    tiles per 256-row block, and every row of every head of its 7,200-token
+    sequence (172,800 rows) is compared with the oracle's softmax over the
+    listed keys."""
+    w = synth.WORKLOADS["ragged"].replace(name="sparse_ragged_lists")
+    tpb = 40
+    inp = synth.generate(w)
+    t = G.to_device(inp, w)
+    tiles = _random_lists(w, tpb, seed=41)
+    got, _ = _run_sparse(torch_dev, w, t, tpb, tiles=tiles, select=False, label=w.name)
+    del t
+    cu = w.cu_seqlens().astype(np.int64)
+    rows = (np.arange(cu[2], cu[3])[:, None] * w.H + np.arange(w.H)[None, :]).reshape(-1)
+    G.announce("%s: oracle, %d rows" % (w.name, len(rows)))
+    ref = oracle.Problem.from_workload(w, inp).sparse_attention_rows(rows, tiles, tpb, nthreads=G.oracle_threads())
+    G.check(G.metrics(G.gpu_rows(got, rows, w.H), ref), G.BF16_GATE, w.name + " last sequence")
+
+
 def test_longest_sequence_every_tile_selected(torch_dev):
     """The largest sequence the block-sparse path accepts: 131,072 tokens
     (32 x 64 x 64 video grid), i.e. 2,048 tiles, with 2,048 tiles per block,
